@@ -1,0 +1,170 @@
+/*
+ * w4a16.h -- C ABI of the MI355X (gfx950) W4A16 weight-only-quantized linear
+ * layer library (libw4a16.so).
+ *
+ * The operation (vLLM PR #37352 write-up, "Code analysis" item 1: the reference
+ * dequantize-then-matmul formula and the kernel call taking group_size, qzeros
+ * and zp_bias):
+ *
+ *     out[m][n] = sum_k a[m][k] * (q[k][n] - z[k/G][n]) * s[k/G][n]
+ *
+ * with q the unsigned 4-bit weight, z the zero point of the (K-group, column)
+ * and s its fp16 scale; out is rounded to fp16.  Accumulation is fp32.
+ *
+ * Conventions for every entry point:
+ *   - fp16 values travel as their 16-bit patterns (uint16_t).
+ *   - Packed int4: 8 nibbles per 32-bit word, nibble j (bits 4j..4j+3) is the
+ *     j-th lowest index of the 8 elements the word packs; nibbles are unsigned
+ *     0..15 and words are used as raw bit patterns (negative int32 is normal).
+ *   - All tensors are dense row-major; pointers marked "device" must be device
+ *     memory of the current HIP device; the caller owns every buffer it passes.
+ *   - Work is enqueued on `stream` (NULL = the default stream).  A return of
+ *     W4A16_OK means "validated and enqueued"; faults inside a kernel surface at
+ *     the caller's next synchronisation.
+ *   - Every argument is validated on the host before any HIP call; a rejected
+ *     call touches nothing and enqueues nothing.
+ *   - No function throws or aborts; each returns a w4a16_status code and, on
+ *     failure, records a message readable with w4a16_last_error() on the same
+ *     host thread.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W4A16_OK = 0,
+    W4A16_ERR_INVALID_ARG = 1, /* NULL pointer, bad size, bad divisibility, overlap */
+    W4A16_ERR_UNSUPPORTED = 2, /* legal shape the kernels do not cover (see each call) */
+    W4A16_ERR_HIP = 3,         /* a HIP runtime call or kernel launch failed */
+    W4A16_ERR_WORKSPACE = 4    /* library-owned scratch could not be allocated */
+} w4a16_status;
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *w4a16_status_string(int status);
+
+/* Message describing the last failing call on this host thread ("" if none).
+ * The pointer stays valid until the next library call on the same thread. */
+const char *w4a16_last_error(void);
+
+/*
+ * Repack checkpoint-layout weights into the kernel layout.
+ * Defined by: vLLM PR #37352 write-up, "Code analysis" item 2 -- the loaded
+ * compressed-tensors weight [N, K/8] becomes [K, N/8] before the kernel runs.
+ *
+ *   src_nk8  device, int32 [N, K/8]: word (n, k/8) holds element (k, n) at
+ *            nibble k%8.
+ *   dst_kn8  device, int32 [K, N/8]: word (k, n/8) receives element (k, n) at
+ *            nibble n%8.  Must not overlap src (no in-place repack).
+ *   K, N     > 0, both multiples of 8.
+ * Bit-exact.  Errors: INVALID_ARG for NULL pointers, K or N <= 0 or not a
+ * multiple of 8, or overlapping buffers; HIP if the launch fails.
+ */
+int w4a16_repack(const int32_t *src_nk8, int32_t *dst_kn8, int64_t K, int64_t N,
+                 hipStream_t stream);
+
+/*
+ * out = a . ((q - z) * s).
+ * Defined by: vLLM PR #37352 write-up, "Code analysis" item 1 (formula and call
+ * signature) and "Why it is good" item 3 (contiguous inputs, N % 8 == 0).
+ *
+ *   a        device, fp16 [M, K] activations.
+ *   b_packed device, int32 [K, N/8] weights (kernel layout, see w4a16_repack).
+ *   scales   device, fp16 [K/G, N]: scale of (group k/G, column n).
+ *   qzeros   device, int32 [K/G, N/8] packed zero points (nibble n%8 of word
+ *            (g, n/8)), or NULL for the symmetric case z = zp_bias.  When given,
+ *            zp_bias is ignored.
+ *   M        >= 0 rows (M == 0 is a no-op returning W4A16_OK; a and out may
+ *            then be NULL).
+ *   K        > 0, a multiple of G.
+ *   N        > 0, a multiple of 8.
+ *   G        group size along K; must be a multiple of 32 (UNSUPPORTED else).
+ *   zp_bias  symmetric zero point in [0, 15] (8 for signed int4), used only when
+ *            qzeros is NULL.
+ *   out      device, fp16 [M, N], caller-allocated; must not overlap any input.
+ *
+ * Paths: M <= 8 runs a split-K GEMV on the vector ALUs; M >= 9 runs an MFMA
+ * kernel (fp16 inputs, fp32 accumulation).  Split-K partial sums live in a
+ * scratch buffer that the library allocates lazily per (device, stream) on the
+ * first call that needs it and keeps until w4a16_release(); concurrent calls
+ * on the same stream from several host threads are not supported.  The result
+ * is deterministic (fixed reduction order) for a given shape.
+ *
+ * Errors: INVALID_ARG for NULL b_packed/scales (or a/out with M > 0), M < 0, K/N/G <= 0,
+ * N % 8 != 0, K % G != 0, zp_bias outside [0, 15] without qzeros, or `out`
+ * overlapping an input; UNSUPPORTED for G % 32 != 0 or a pointer that is not
+ * 16-byte aligned; WORKSPACE if scratch allocation fails; HIP on launch failure.
+ */
+int w4a16_gemm(const uint16_t *a, const int32_t *b_packed, const uint16_t *scales,
+               const int32_t *qzeros, int64_t M, int64_t K, int64_t N, int64_t G,
+               int32_t zp_bias, uint16_t *out, hipStream_t stream);
+
+/* One W4A16 linear of a decode stack (host struct; pointers are device). */
+typedef struct {
+    const int32_t *b_packed;  /* [K, N/8] */
+    const uint16_t *scales;   /* [K/G, N] fp16 */
+    const int32_t *qzeros;    /* [K/G, N/8] or NULL */
+    int64_t K, N, G;
+    int32_t zp_bias;
+} w4a16_linear;
+
+/*
+ * Scratch bytes w4a16_decode_step needs for M rows and this stack (0 if the
+ * stack is malformed).  Host-only, no HIP calls.
+ */
+size_t w4a16_decode_workspace_bytes(int64_t M, const w4a16_linear *lin, int64_t n_layers);
+
+/*
+ * One decode step through n_layers transformer layers' linears.
+ * Follows: the decode phase of the from-scratch C++/CUDA inference-engine
+ * article (pt.news.hada.io topic 18295, section 1.1: one pass through the
+ * stack of blocks per generated token) with every linear a W4A16 GEMM.  The
+ * pages give no glue between the linears; this step uses, per layer with
+ * hidden H and MLP width I (both read from the stack):
+ *     q  = lin[4l+0](x)                  [M, Nq], Nq >= H
+ *     h1 = rn(q[:, :H])                  (stands in for attention)
+ *     h2 = rn(lin[4l+1](h1))             [M, H]
+ *     gu = lin[4l+2](h2)                 [M, 2I]
+ *     h3 = rn(silu(gu[:, :I]) * gu[:, I:])
+ *     x  = rn(lin[4l+3](h3))             [M, H]
+ * rn(v) = v / sqrt(mean(v^2) + 1e-6) per row, computed in fp32; silu(x) =
+ * x / (1 + exp(-x)).  Intermediates are stored as fp16.
+ *
+ *   lin        host array of 4*n_layers linears: qkv, o, gate_up, down per layer
+ *              (shapes must chain as above, else INVALID_ARG).
+ *   x_in       device fp16 [M, H]; x_out device fp16 [M, H] (may equal x_in).
+ *   M          1..8192 rows.
+ *   workspace  device scratch of at least w4a16_decode_workspace_bytes(...)
+ *              bytes, caller-owned, not shared with a concurrent call.
+ * Errors: INVALID_ARG for a malformed stack, NULL pointers, M out of range or
+ * a workspace smaller than required; otherwise as w4a16_gemm.
+ */
+int w4a16_decode_step(const w4a16_linear *lin, int64_t n_layers, const uint16_t *x_in,
+                      uint16_t *x_out, int64_t M, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/*
+ * Describe the plan w4a16_gemm would run for a shape (host-only, no HIP calls):
+ * path 1 = GEMV (vector ALUs), 2 = MFMA; splits = K-splits across workgroups;
+ * grid = workgroups launched.  Returns the status w4a16_gemm would return from
+ * validation of the sizes alone (pointers are not examined).
+ */
+int w4a16_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t G, int32_t *path,
+                    int32_t *splits, int64_t *grid);
+
+/* Free library-owned scratch on every device after synchronising the streams
+ * that used it.  Safe to call at any time no w4a16 call is in flight. */
+int w4a16_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

@@ -1,0 +1,169 @@
+"""C-ABI boundary tests that need no GPU.
+
+Every call here is rejected by host-side validation before any HIP call, so it
+is safe with or without a device: fake pointers are never dereferenced.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import w4a16_weight_only_amd as w4
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+
+# Distinct, 16-byte-aligned fake device addresses (never dereferenced).
+A, B, S, Z, O = (ctypes.c_void_p(0x10_0000_0000 + i * 0x1_0000_0000) for i in range(5))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(w4.LIB_PATH):
+        import w4a16_weight_only_amd.build as bld
+        bld.build()
+    return w4.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a16_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("w4a16_repack", "w4a16_gemm", "w4a16_decode_step"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", w4.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (w4a16_\w+)", out))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    for n in declared_functions():
+        assert hasattr(lib, n)
+
+
+def test_status_strings(lib):
+    for code, name in w4.STATUS.items():
+        assert lib.w4a16_status_string(code).decode() == name
+    assert lib.w4a16_status_string(99).decode() == "W4A16_ERR_UNKNOWN"
+
+
+def gemm(lib, a=A, b=B, s=S, z=None, M=1, K=256, N=256, G=64, zp=8, o=O):
+    return lib.w4a16_gemm(a, b, s, z, M, K, N, G, zp, o, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(a=None), INVALID), (dict(b=None), INVALID), (dict(s=None), INVALID), (dict(o=None), INVALID),
+    (dict(M=-1), INVALID), (dict(K=0), INVALID), (dict(N=0), INVALID), (dict(G=0), INVALID),
+    (dict(N=260), INVALID),                      # N % 8 != 0
+    (dict(K=250, G=64), INVALID),                # K % G != 0
+    (dict(G=48, K=240), UNSUPPORTED),            # G % 32 != 0
+    (dict(zp=16), INVALID), (dict(zp=-1), INVALID),
+    (dict(a=ctypes.c_void_p(A.value + 8)), UNSUPPORTED),   # misaligned
+    (dict(z=ctypes.c_void_p(Z.value + 4)), UNSUPPORTED),
+    (dict(o=ctypes.c_void_p(A.value + 64)), INVALID),      # out overlaps a
+    (dict(o=ctypes.c_void_p(B.value)), INVALID),           # out overlaps b_packed
+    (dict(o=ctypes.c_void_p(S.value + 16)), INVALID),      # out overlaps scales
+    (dict(z=Z, o=ctypes.c_void_p(Z.value)), INVALID),      # out overlaps qzeros
+    (dict(M=1 << 21), UNSUPPORTED),
+])
+def test_gemm_rejects(lib, kw, status):
+    assert gemm(lib, **kw) == status
+    assert lib.w4a16_last_error().decode() != ""
+
+
+def test_gemm_m0_is_a_noop(lib):
+    # M == 0 returns before any HIP call; a and out may then be NULL.
+    assert gemm(lib, M=0) == OK
+    assert gemm(lib, M=0, a=None, o=None) == OK
+    assert gemm(lib, M=0, b=None) == INVALID
+
+
+def test_gemm_zp_ignored_with_qzeros(lib):
+    # zp_bias out of range is only an error in the symmetric case; with qzeros
+    # the call gets past that check (and is then rejected for overlap here).
+    assert gemm(lib, z=Z, zp=99, o=ctypes.c_void_p(A.value)) == INVALID
+    assert "overlap" in lib.w4a16_last_error().decode()
+
+
+@pytest.mark.parametrize("K,N,status", [(0, 8, INVALID), (8, 0, INVALID), (12, 8, INVALID),
+                                        (8, 12, INVALID), (-8, 8, INVALID)])
+def test_repack_rejects_sizes(lib, K, N, status):
+    assert lib.w4a16_repack(A, B, K, N, None) == status
+
+
+def test_repack_rejects_null_and_overlap(lib):
+    assert lib.w4a16_repack(None, B, 8, 8, None) == INVALID
+    assert lib.w4a16_repack(A, None, 8, 8, None) == INVALID
+    assert lib.w4a16_repack(A, ctypes.c_void_p(A.value + 4), 64, 64, None) == INVALID
+
+
+def test_gemm_plan_paths(lib):
+    # decode GEMV, batched and prefill shapes
+    assert w4.w4a16_gemm_plan(1, 4096, 12800, 128)[0] == 1
+    assert w4.w4a16_gemm_plan(8, 4096, 12800, 128)[0] == 1
+    assert w4.w4a16_gemm_plan(9, 4096, 12800, 128)[0] == 2
+    assert w4.w4a16_gemm_plan(32, 4096, 12800, 128)[0] == 2
+    assert w4.w4a16_gemm_plan(256, 12800, 4096, 128)[0] == 2
+    # N % 32 != 0 at small M goes to the MFMA kernel (word-granular loads)
+    assert w4.w4a16_gemm_plan(1, 256, 264, 64)[0] == 2
+    for shape in [(1, 4096, 12800, 128), (32, 4096, 12800, 128), (256, 12800, 4096, 128),
+                  (1, 256, 256, 64), (5, 12800, 4096, 128)]:
+        path, splits, grid = w4.w4a16_gemm_plan(*shape)
+        assert splits >= 1 and grid >= splits
+    with pytest.raises(w4.W4A16Error) as e:
+        w4.w4a16_gemm_plan(1, 100, 64, 30)
+    assert e.value.status == INVALID
+
+
+def _stack(K=64, NQ=96, I=128, G=32, layers=1, bad=False):
+    arr = (w4.Linear * (4 * layers))()
+    shapes = [(K, NQ), (K, K), (K, 2 * I), (I, K)]
+    for l in range(layers):
+        for j, (k, n) in enumerate(shapes):
+            if bad and j == 3:
+                k = I + 32
+            arr[4 * l + j] = w4.Linear(B.value + 0x100_0000 * (4 * l + j), S.value + 0x100_0000 * (4 * l + j),
+                                       None, k, n, G, 8)
+    return arr
+
+
+def test_decode_workspace_bytes(lib):
+    arr = _stack()
+    nb = lib.w4a16_decode_workspace_bytes(3, ctypes.cast(arr, ctypes.c_void_p), 1)
+    # T: 3 x max N (256) fp16, Hb: 3 x max(H, I) (128) fp16, each 256-aligned
+    assert nb == 1536 + 768
+    assert lib.w4a16_decode_workspace_bytes(3, ctypes.cast(_stack(bad=True), ctypes.c_void_p), 1) == 0
+    assert lib.w4a16_decode_workspace_bytes(0, ctypes.cast(arr, ctypes.c_void_p), 1) == 0
+
+
+def test_decode_step_rejects(lib):
+    arr = ctypes.cast(_stack(), ctypes.c_void_p)
+    W = ctypes.c_void_p(0x20_0000_0000)
+    call = lib.w4a16_decode_step
+    assert call(arr, 1, None, O, 3, W, 1 << 20, None) == INVALID
+    assert call(arr, 1, A, O, 0, W, 1 << 20, None) == INVALID           # M out of range
+    assert call(arr, 1, A, O, 3, W, 100, None) == INVALID               # workspace too small
+    assert call(ctypes.cast(_stack(bad=True), ctypes.c_void_p), 1, A, O, 3, W, 1 << 20, None) == INVALID
+    assert call(arr, 1, A, O, 3, ctypes.c_void_p(A.value), 1 << 20, None) == INVALID  # overlap
+
+
+def test_python_binding_rejects_host_tensors_and_bad_dtypes(lib):
+    a = torch.zeros(1, 256, dtype=torch.float16)
+    b = torch.zeros(256, 32, dtype=torch.int32)
+    s = torch.zeros(4, 256, dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU"):
+        w4.w4a16_gemm(a, b, s, None, 64)
+    with pytest.raises(TypeError):
+        w4.w4a16_gemm(a.float(), b, s, None, 64)
+    with pytest.raises(TypeError):
+        w4.w4a16_repack(b.to(torch.int64), 256)

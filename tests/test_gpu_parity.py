@@ -1,0 +1,242 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Acceptance for fp16 outputs: max |gpu - oracle| <= 1e-2 * max(1, |oracle|) per
+element (fp32 accumulation on the GPU, fp64 in the oracle).  Repack is checked
+bit for bit.  Inputs come from the seeded generators in
+w4a16_weight_only_amd.synth, identical bytes on both sides.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import w4a16_weight_only_amd as w4
+from tests._fixtures import pack_rows, unpack_rows
+from w4a16_weight_only_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+
+
+def note(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    w4.lib()  # raises if libw4a16.so is missing: no fallback
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(x):
+    if x is None:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+def check_close(got, want, what=""):
+    g = got.astype(np.float64)
+    r = want.astype(np.float64)
+    err = np.abs(g - r)
+    bound = TOL * np.maximum(1.0, np.abs(r))
+    worst = np.unravel_index(np.argmax(err / bound), err.shape) if err.size else None
+    ulp = np.abs(got.view(np.uint16).astype(np.int64) - want.view(np.uint16).astype(np.int64))
+    note("%s max|err|=%.3g max ulp=%d" % (what, err.max() if err.size else 0, ulp.max() if ulp.size else 0))
+    assert np.all(err <= bound), "%s: worst at %s got %r want %r" % (what, worst, g[worst], r[worst])
+
+
+def run_gemm(p, qzeros=True, b_key="b_packed"):
+    qz = p["qzeros"] if qzeros else None
+    out = w4.w4a16_gemm(dev(p["a"]), dev(p[b_key]), dev(p["scales"]), dev(qz), p["G"], p["zp_bias"])
+    torch.cuda.synchronize()
+    return host(out)
+
+
+# ----------------------------------------------------------------- repack ---
+
+@pytest.mark.parametrize("K,N", [(8, 8), (64, 32), (256, 1024), (1024, 136), (264, 520), (4096, 12800)])
+def test_repack_bit_exact(K, N):
+    note("repack K=%d N=%d" % (K, N))
+    src = synth.packed_words(synth.rng(K + 3 * N), N, K // 8)
+    want = oracle.repack(src, K)
+    s = dev(src)
+    outs = [host(w4.w4a16_repack(s, K)) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs:
+        assert np.array_equal(o, want)
+
+
+# ------------------------------------------------------ small full-output ---
+
+def small_cases():
+    cases = []
+    for M in range(1, 9):  # GEMV path: tiles of 256 columns, ragged last tile
+        cases.append((M, 512, 544, 128, M % 2 == 0))
+    cases += [(1, 256, 256, 64, False), (2, 1024, 256, 1024, True), (3, 4096, 1024, 128, False)]
+    for M in (9, 15, 16, 17, 32, 33, 64, 65, 100, 128, 200, 256):  # MFMA path, ragged words/rows
+        cases.append((M, 512, 520, 64, M % 2 == 1))
+    cases += [(1, 256, 264, 64, True), (7, 384, 8, 128, False),  # N % 32 != 0 at small M
+              (40, 2048, 1024, 2048, True), (256, 1280, 512, 128, True)]
+    return cases
+
+
+@pytest.mark.parametrize("M,K,N,G,asym", small_cases())
+def test_gemm_matches_oracle(M, K, N, G, asym):
+    path, splits, grid = w4.w4a16_gemm_plan(M, K, N, G)
+    note("gemm M=%d K=%d N=%d G=%d asym=%s path=%d splits=%d grid=%d" % (M, K, N, G, asym, path, splits, grid))
+    p = synth.problem(M, K, N, G, asym, seed=1000 + M * 7 + K + N)
+    got = run_gemm(p)
+    want = oracle.gemm(p["a"], p["b_packed"], p["scales"], p["qzeros"], G, 8)
+    check_close(got, want, "M=%d K=%d N=%d" % (M, K, N))
+
+
+@pytest.mark.parametrize("M", [1, 4, 8, 16, 32, 256])
+def test_gemm_deterministic(M):
+    p = synth.problem(M, 4096, 2048, 128, True, seed=77)
+    a, b, s, z = dev(p["a"]), dev(p["b_packed"]), dev(p["scales"]), dev(p["qzeros"])
+    o1 = host(w4.w4a16_gemm(a, b, s, z, 128))
+    o2 = host(w4.w4a16_gemm(a, b, s, z, 128))
+    assert np.array_equal(o1.view(np.uint16), o2.view(np.uint16))
+
+
+@pytest.mark.parametrize("M", [1, 5, 8, 12, 32, 256])
+def test_gemm_identities(M):
+    """All-8 nibbles with zero point 8 give exactly 0; qzeros all 8 equal the
+    symmetric call bit for bit; doubling every scale doubles the output exactly."""
+    K, N, G = 1024, 512, 128
+    p = synth.problem(M, K, N, G, False, seed=55 + M)
+    a, b, s = dev(p["a"]), dev(p["b_packed"]), dev(p["scales"])
+    eights = torch.full_like(b, np.uint32(0x88888888).view(np.int32).item())
+    zero = host(w4.w4a16_gemm(a, eights, s, None, G, 8))
+    assert np.all(zero == 0)
+    qz8 = torch.full((K // G, N // 8), np.uint32(0x88888888).view(np.int32).item(), dtype=torch.int32, device="cuda")
+    sym = host(w4.w4a16_gemm(a, b, s, None, G, 8))
+    asym = host(w4.w4a16_gemm(a, b, s, qz8, G, 3))
+    assert np.array_equal(sym.view(np.uint16), asym.view(np.uint16))
+    dbl = host(w4.w4a16_gemm(a, b, s * 2, None, G, 8))
+    assert np.array_equal(dbl.astype(np.float64), 2 * sym.astype(np.float64))
+
+
+def test_gemm_m0_and_into_out():
+    p = synth.problem(4, 256, 256, 64, False, seed=5)
+    a, b, s = dev(p["a"]), dev(p["b_packed"]), dev(p["scales"])
+    empty = w4.w4a16_gemm(a[:0], b, s, None, 64)
+    assert empty.shape == (0, 256)
+    out = torch.full((4, 256), 7.0, dtype=torch.float16, device="cuda")
+    w4.w4a16_gemm(a, b, s, None, 64, out=out)
+    want = oracle.gemm(p["a"], p["b_packed"], p["scales"], None, 64)
+    check_close(host(out), want, "into out")
+
+
+def test_gemm_after_repack_matches_checkpoint_layout():
+    p = synth.problem(32, 1024, 768, 128, True, seed=31, from_checkpoint=True)
+    bk = w4.w4a16_repack(dev(p["b_nk8"]), 1024)
+    out = host(w4.w4a16_gemm(dev(p["a"]), bk, dev(p["scales"]), dev(p["qzeros"]), 128))
+    want = oracle.gemm_nk8(p["a"], p["b_nk8"], p["scales"], p["qzeros"], 128)
+    check_close(out, want, "repack+gemm")
+
+
+# ------------------------------------------- full workload sizes, sampled ---
+
+def sample_idx(M, N, count, seed):
+    g = np.random.default_rng(seed)
+    mi = g.integers(0, M, count)
+    ni = g.integers(0, N, count)
+    # always include the corners and the last column (ragged tails)
+    mi = np.concatenate([mi, [0, M - 1, 0, M - 1]])
+    ni = np.concatenate([ni, [0, 0, N - 1, N - 1]])
+    return mi, ni
+
+
+@pytest.mark.parametrize("name", ["tiny", "gemv"])
+def test_workload_full_output(name):
+    p = synth.workload(name)
+    note("workload %s (full output)" % name)
+    got = run_gemm(p)
+    want = oracle.gemm(p["a"], p["b_packed"], p["scales"], p["qzeros"], p["G"], 8)
+    check_close(got, want, name)
+
+
+@pytest.mark.parametrize("name,count", [("batched", 3000), ("prefill", 1500)])
+def test_workload_sampled(name, count):
+    p = synth.workload(name)
+    note("workload %s (sampled %d)" % (name, count))
+    if "b_nk8" in p:
+        b = w4.w4a16_repack(dev(p["b_nk8"]), p["K"])
+        want_b = oracle.repack(p["b_nk8"], p["K"])
+        assert np.array_equal(host(b), want_b)
+        p["b_packed"] = want_b
+    else:
+        b = dev(p["b_packed"])
+    out = host(w4.w4a16_gemm(dev(p["a"]), b, dev(p["scales"]), dev(p["qzeros"]), p["G"], 8))
+    mi, ni = sample_idx(p["M"], p["N"], count, seed=9)
+    want, _ = oracle.gemm_sample(p["a"], p["b_packed"], p["scales"], p["qzeros"], p["G"], 8, mi, ni)
+    check_close(out[mi, ni], want, name)
+
+
+# ------------------------------------------------------------ decode step ---
+
+def dev_stack(layers):
+    return [dict(b_packed=dev(L["b_packed"]), scales=dev(L["scales"]), qzeros=None, G=L["G"], zp_bias=8)
+            for L in layers]
+
+
+@pytest.mark.parametrize("M", [1, 3, 20])
+def test_decode_step_small_stack(M):
+    """Teacher-forced per layer: the oracle's layer l is fed the GPU's own input
+    to layer l, so each comparison covers one layer (four chained linears) at
+    the per-element bound.  The multi-layer call must equal the chained
+    single-layer calls bit for bit, and the end-to-end drift against the
+    oracle's own chain (fp16 rounding differences compound) is reported and
+    bounded by relative L2 <= 1e-2."""
+    H, NQ, I, G, nl = 256, 384, 512, 64, 3
+    layers = []
+    for l in range(nl):
+        layers += synth.stack_layer(l, H=H, NQ=NQ, I=I, G=G, seed_base=900)
+    x = synth.stack_input(M, H, seed=M)
+    dstack = dev_stack(layers)
+    full = host(w4.w4a16_decode_step(dstack, dev(x)))
+    cur = dev(x)
+    for l in range(nl):
+        y = w4.w4a16_decode_step(dstack[4 * l: 4 * l + 4], cur)
+        want = oracle.decode_step(layers[4 * l: 4 * l + 4], host(cur), 1)
+        check_close(host(y), want, "decode small M=%d layer %d" % (M, l))
+        cur = y
+    assert np.array_equal(host(cur).view(np.uint16), full.view(np.uint16))
+    e2e = oracle.decode_step(layers, x, nl).astype(np.float64)
+    rel = np.linalg.norm(full.astype(np.float64) - e2e) / np.linalg.norm(e2e)
+    note("decode small M=%d end-to-end relative L2 drift %.3g" % (M, rel))
+    assert rel < 1e-2
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_decode_step_one_real_layer(M):
+    """One layer at the 8B-class shapes (QKV 4096->6144, O, gate+up
+    4096->25600, down 12800->4096), same launch plans as the full stack."""
+    layers = synth.stack_layer(0)
+    x = synth.stack_input(M)
+    note("decode real layer M=%d" % M)
+    got = host(w4.w4a16_decode_step(dev_stack(layers), dev(x)))
+    want = oracle.decode_step(layers, x, 1)
+    check_close(got, want, "decode real M=%d" % M)
+
+
+def test_decode_step_in_place_and_rms():
+    H, NQ, I, G = 256, 256, 384, 128
+    layers = synth.stack_layer(0, H=H, NQ=NQ, I=I, G=G) + synth.stack_layer(1, H=H, NQ=NQ, I=I, G=G)
+    x = dev(synth.stack_input(5, H))
+    ref = host(w4.w4a16_decode_step(dev_stack(layers), x))
+    w4.w4a16_decode_step(dev_stack(layers), x, out=x)  # x_out may equal x_in
+    got = host(x)
+    assert np.array_equal(got.view(np.uint16), ref.view(np.uint16))
+    rms = np.sqrt((got.astype(np.float64) ** 2).mean(1))
+    assert np.allclose(rms, 1.0, atol=5e-3)

@@ -1,0 +1,389 @@
+// api.cpp -- C ABI of libw4a16: host-side validation, planning, scratch
+// management and dispatch.  Every argument is checked before the first HIP
+// call, so invalid calls return a status without touching the device.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "../../include/w4a16.h"
+#include "kernels.h"
+
+namespace w4a16 {
+int gemv_words_for_m(int64_t M);
+}
+
+namespace {
+
+using namespace w4a16;
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string &msg) {
+    g_last_error = msg;
+    return status;
+}
+
+int ok() {
+    g_last_error.clear();
+    return W4A16_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void *p, size_t pn, const void *q, size_t qn) {
+    if (!p || !q || pn == 0 || qn == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), a1 = a0 + pn;
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(q), b1 = b0 + qn;
+    return a0 < b1 && b0 < a1;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------- tuning ---
+// Plan knobs, overridable for tuning sweeps via W4A16_TUNE="key=value,...".
+struct Tune {
+    int64_t gemv_target_wg = 512;   // aim for about this many GEMV workgroups
+    int64_t gemv_min_rows = 2;      // minimum split length in units of row-lane passes
+    int64_t gemv_split_len = 0;     // force the GEMV split length (16-row chunks)
+    int64_t mfma_target_wg = 512;
+    int64_t mfma_max_splits = 16;
+    int64_t mfma_splits = 0;        // force the MFMA split count
+    int64_t max_partial_bytes = 64ll << 20;
+};
+
+const Tune &tune() {
+    static Tune t = [] {
+        Tune v;
+        const char *env = std::getenv("W4A16_TUNE");
+        if (!env) return v;
+        std::string s(env);
+        size_t pos = 0;
+        while (pos < s.size()) {
+            size_t end = s.find(',', pos);
+            if (end == std::string::npos) end = s.size();
+            std::string kv = s.substr(pos, end - pos);
+            size_t eq = kv.find('=');
+            if (eq != std::string::npos) {
+                std::string k = kv.substr(0, eq);
+                int64_t val = std::atoll(kv.c_str() + eq + 1);
+                if (k == "gemv_target_wg") v.gemv_target_wg = val;
+                else if (k == "gemv_min_rows") v.gemv_min_rows = val;
+                else if (k == "gemv_split_len") v.gemv_split_len = val;
+                else if (k == "mfma_target_wg") v.mfma_target_wg = val;
+                else if (k == "mfma_max_splits") v.mfma_max_splits = val;
+                else if (k == "mfma_splits") v.mfma_splits = val;
+                else if (k == "max_partial_bytes") v.max_partial_bytes = val;
+            }
+            pos = end + 1;
+        }
+        return v;
+    }();
+    return t;
+}
+
+// ---------------------------------------------------------- validation ---
+int validate_sizes(int64_t M, int64_t K, int64_t N, int64_t G) {
+    if (M < 0) return fail(W4A16_ERR_INVALID_ARG, "M must be >= 0");
+    if (K <= 0 || N <= 0 || G <= 0) return fail(W4A16_ERR_INVALID_ARG, "K, N and G must be > 0");
+    if (N % 8 != 0) return fail(W4A16_ERR_INVALID_ARG, "N must be a multiple of 8");
+    if (K % G != 0) return fail(W4A16_ERR_INVALID_ARG, "K must be a multiple of G");
+    if (G % 32 != 0) return fail(W4A16_ERR_UNSUPPORTED, "G must be a multiple of 32");
+    if (M > (1ll << 20) || K > (1ll << 26) || N > (1ll << 26) || M * N > (1ll << 31) ||
+        M * K > (1ll << 31) || K * (N / 8) > (1ll << 31))
+        return fail(W4A16_ERR_UNSUPPORTED, "problem too large for 32-bit kernel indexing");
+    return W4A16_OK;
+}
+
+}  // namespace
+
+namespace w4a16 {
+
+GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G) {
+    (void)G;
+    const Tune &t = tune();
+    GemmPlan p;
+    const int64_t N8 = N / 8;
+    if (M <= 8 && N % 32 == 0) {
+        p.path = kPathGemv;
+        p.words = gemv_words_for_m(M);
+        p.waves = 4;
+        const int64_t CL = 32 / p.words, RL = 64 / CL;
+        p.tiles_n = cdiv(N8, 32);
+        const int64_t nchunks = K / 16;
+        int64_t len;
+        if (t.gemv_split_len > 0) {
+            len = t.gemv_split_len;
+        } else {
+            const int64_t splits_target = std::max<int64_t>(1, cdiv(t.gemv_target_wg, p.tiles_n));
+            len = cdiv(nchunks, splits_target);
+            len = std::max<int64_t>(len, t.gemv_min_rows * RL);
+            len = cdiv(len, RL) * RL;
+        }
+        len = std::min<int64_t>(std::max<int64_t>(len, 1), nchunks);
+        p.split_len = len;
+        p.splits = (int)cdiv(nchunks, len);
+        p.tiles_m = 1;
+    } else {
+        p.path = kPathMfma;
+        p.waves = 2;
+        p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : (M <= 64 ? 4 : 8));
+        p.tiles_n = cdiv(N8, 16 * p.waves);
+        p.tiles_m = cdiv(M, 16 * p.mt);
+        const int64_t nsteps = K / 32;
+        const int64_t tiles = p.tiles_n * p.tiles_m;
+        int64_t splits = t.mfma_splits > 0 ? t.mfma_splits
+                                           : std::max<int64_t>(1, cdiv(t.mfma_target_wg, tiles));
+        splits = std::min<int64_t>(splits, t.mfma_max_splits);
+        const int64_t cap = t.max_partial_bytes / std::max<int64_t>(1, M * N * 4);
+        splits = std::max<int64_t>(1, std::min<int64_t>(splits, cap));
+        splits = std::min<int64_t>(splits, nsteps);
+        p.split_len = cdiv(nsteps, splits);
+        p.splits = (int)cdiv(nsteps, p.split_len);
+    }
+    p.grid = p.tiles_n * p.tiles_m * p.splits;
+    p.partial_floats = p.splits > 1 ? (size_t)(p.splits * M * N) : 0;
+    p.counters = p.splits > 1 ? (size_t)(p.tiles_n * p.tiles_m) : 0;
+    return p;
+}
+
+}  // namespace w4a16
+
+namespace {
+
+// ------------------------------------------------- library-owned scratch ---
+// Split-K partials and arrival counters, one set per (device, stream).  The
+// counters are zeroed once at allocation; each split-K tile's last workgroup
+// resets its counter, so they are zero again whenever the stream is idle.
+struct Scratch {
+    float *partials = nullptr;
+    size_t partial_cap = 0;  // floats
+    uint32_t *counters = nullptr;
+    size_t counter_cap = 0;  // words
+};
+
+std::mutex g_mu;
+std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
+
+int get_scratch(hipStream_t stream, const GemmPlan &plan, float **partials, uint32_t **counters) {
+    *partials = nullptr;
+    *counters = nullptr;
+    if (plan.splits <= 1) return W4A16_OK;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(W4A16_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    std::lock_guard<std::mutex> lock(g_mu);
+    Scratch &s = g_scratch[{dev, stream}];
+    if (s.partial_cap < plan.partial_floats || s.counter_cap < plan.counters) {
+        // Growing: the old buffers may still be read by queued kernels.
+        if (s.partials || s.counters) {
+            e = hipStreamSynchronize(stream);
+            if (e != hipSuccess) return fail(W4A16_ERR_HIP, std::string("hipStreamSynchronize: ") + hipGetErrorString(e));
+            (void)hipFree(s.partials);
+            (void)hipFree(s.counters);
+            s = Scratch();
+        }
+        const size_t pcap = std::max<size_t>(plan.partial_floats, (size_t)1 << 20);
+        const size_t ccap = std::max<size_t>(plan.counters, (size_t)1 << 14);
+        e = hipMalloc((void **)&s.partials, pcap * sizeof(float));
+        if (e != hipSuccess) { s = Scratch(); return fail(W4A16_ERR_WORKSPACE, "hipMalloc of split-K partials failed"); }
+        e = hipMalloc((void **)&s.counters, ccap * sizeof(uint32_t));
+        if (e != hipSuccess) {
+            (void)hipFree(s.partials);
+            s = Scratch();
+            return fail(W4A16_ERR_WORKSPACE, "hipMalloc of split-K counters failed");
+        }
+        e = hipMemsetAsync(s.counters, 0, ccap * sizeof(uint32_t), stream);
+        if (e != hipSuccess) return fail(W4A16_ERR_HIP, std::string("hipMemsetAsync: ") + hipGetErrorString(e));
+        s.partial_cap = pcap;
+        s.counter_cap = ccap;
+    }
+    *partials = s.partials;
+    *counters = s.counters;
+    return W4A16_OK;
+}
+
+int validate_gemm(const uint16_t *a, const int32_t *b, const uint16_t *s, const int32_t *qz,
+                  int64_t M, int64_t K, int64_t N, int64_t G, int32_t zp, const uint16_t *out) {
+    if (!b || !s) return fail(W4A16_ERR_INVALID_ARG, "b_packed and scales must be non-NULL");
+    if (M != 0 && (!a || !out)) return fail(W4A16_ERR_INVALID_ARG, "a and out must be non-NULL when M > 0");
+    int rc = validate_sizes(M, K, N, G);
+    if (rc != W4A16_OK) return rc;
+    if (!qz && (zp < 0 || zp > 15)) return fail(W4A16_ERR_INVALID_ARG, "zp_bias must be in [0, 15]");
+    const size_t out_b = (size_t)M * N * 2;
+    if (overlaps(out, out_b, a, (size_t)M * K * 2) || overlaps(out, out_b, b, (size_t)K * (N / 8) * 4) ||
+        overlaps(out, out_b, s, (size_t)(K / G) * N * 2) ||
+        overlaps(out, out_b, qz, (size_t)(K / G) * (N / 8) * 4))
+        return fail(W4A16_ERR_INVALID_ARG, "out overlaps an input");
+    if (!aligned16(a) || !aligned16(b) || !aligned16(s) || !aligned16(out) || (qz && !aligned16(qz)))
+        return fail(W4A16_ERR_UNSUPPORTED, "a, b_packed, scales, qzeros and out must be 16-byte aligned");
+    return W4A16_OK;
+}
+
+int run_gemm(const uint16_t *a, const int32_t *b, const uint16_t *s, const int32_t *qz, int64_t M,
+             int64_t K, int64_t N, int64_t G, int32_t zp, uint16_t *out, hipStream_t stream) {
+    if (M == 0) return ok();
+    const GemmPlan plan = plan_gemm(M, K, N, G);
+    GemmArgs args{a, b, s, qz, M, K, N, G, zp, out, nullptr, nullptr};
+    int rc = get_scratch(stream, plan, &args.partials, &args.counters);
+    if (rc != W4A16_OK) return rc;
+    hipError_t e = plan.path == kPathGemv ? launch_gemv(args, plan, stream) : launch_mfma(args, plan, stream);
+    if (e != hipSuccess) return fail(W4A16_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+    return ok();
+}
+
+// Decode-step workspace layout: T (GEMM outputs, M x maxN fp16) then Hb
+// (re-normalised inputs, M x max(H, I) fp16), each 256-byte aligned.
+struct DecodeShape {
+    int64_t H = 0, NQ = 0, I = 0, maxN = 0, maxK = 0;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int check_stack(const w4a16_linear *lin, int64_t n_layers, DecodeShape *sh) {
+    if (!lin || n_layers <= 0) return fail(W4A16_ERR_INVALID_ARG, "empty stack");
+    const int64_t H = lin[0].K;
+    DecodeShape d;
+    d.H = H;
+    for (int64_t l = 0; l < n_layers; ++l) {
+        const w4a16_linear *L = lin + 4 * l;
+        const int64_t I = L[2].N / 2;
+        if (L[0].K != H || L[0].N < H || L[1].K != H || L[1].N != H || L[2].K != H || L[2].N % 2 != 0 ||
+            L[3].K != I || L[3].N != H)
+            return fail(W4A16_ERR_INVALID_ARG, "stack shapes do not chain (qkv, o, gate_up, down)");
+        for (int j = 0; j < 4; ++j) {
+            if (!L[j].b_packed || !L[j].scales)
+                return fail(W4A16_ERR_INVALID_ARG, "stack linear with NULL weights or scales");
+            int rc = validate_sizes(1, L[j].K, L[j].N, L[j].G);
+            if (rc != W4A16_OK) return rc;
+            if (!L[j].qzeros && (L[j].zp_bias < 0 || L[j].zp_bias > 15))
+                return fail(W4A16_ERR_INVALID_ARG, "zp_bias must be in [0, 15]");
+            if (!aligned16(L[j].b_packed) || !aligned16(L[j].scales) || (L[j].qzeros && !aligned16(L[j].qzeros)))
+                return fail(W4A16_ERR_UNSUPPORTED, "stack tensors must be 16-byte aligned");
+            d.maxN = std::max(d.maxN, L[j].N);
+        }
+        d.I = std::max(d.I, I);
+        d.NQ = std::max(d.NQ, L[0].N);
+    }
+    d.maxK = std::max(d.H, d.I);
+    *sh = d;
+    return W4A16_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *w4a16_status_string(int status) {
+    switch (status) {
+        case W4A16_OK: return "W4A16_OK";
+        case W4A16_ERR_INVALID_ARG: return "W4A16_ERR_INVALID_ARG";
+        case W4A16_ERR_UNSUPPORTED: return "W4A16_ERR_UNSUPPORTED";
+        case W4A16_ERR_HIP: return "W4A16_ERR_HIP";
+        case W4A16_ERR_WORKSPACE: return "W4A16_ERR_WORKSPACE";
+        default: return "W4A16_ERR_UNKNOWN";
+    }
+}
+
+const char *w4a16_last_error(void) { return g_last_error.c_str(); }
+
+int w4a16_repack(const int32_t *src_nk8, int32_t *dst_kn8, int64_t K, int64_t N, hipStream_t stream) {
+    if (!src_nk8 || !dst_kn8) return fail(W4A16_ERR_INVALID_ARG, "src and dst must be non-NULL");
+    if (K <= 0 || N <= 0 || K % 8 != 0 || N % 8 != 0)
+        return fail(W4A16_ERR_INVALID_ARG, "K and N must be positive multiples of 8");
+    if (K * (N / 8) > (1ll << 31)) return fail(W4A16_ERR_UNSUPPORTED, "repack too large for 32-bit indexing");
+    const size_t bytes = (size_t)K * (N / 8) * 4;
+    if (overlaps(src_nk8, bytes, dst_kn8, bytes)) return fail(W4A16_ERR_INVALID_ARG, "dst overlaps src");
+    hipError_t e = launch_repack(src_nk8, dst_kn8, K, N, stream);
+    if (e != hipSuccess) return fail(W4A16_ERR_HIP, std::string("repack launch: ") + hipGetErrorString(e));
+    return ok();
+}
+
+int w4a16_gemm(const uint16_t *a, const int32_t *b_packed, const uint16_t *scales, const int32_t *qzeros,
+               int64_t M, int64_t K, int64_t N, int64_t G, int32_t zp_bias, uint16_t *out,
+               hipStream_t stream) {
+    int rc = validate_gemm(a, b_packed, scales, qzeros, M, K, N, G, zp_bias, out);
+    if (rc != W4A16_OK) return rc;
+    return run_gemm(a, b_packed, scales, qzeros, M, K, N, G, zp_bias, out, stream);
+}
+
+int w4a16_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t G, int32_t *path, int32_t *splits,
+                    int64_t *grid) {
+    int rc = validate_sizes(M, K, N, G);
+    if (rc != W4A16_OK) return rc;
+    const GemmPlan p = plan_gemm(std::max<int64_t>(M, 1), K, N, G);
+    if (path) *path = p.path;
+    if (splits) *splits = p.splits;
+    if (grid) *grid = p.grid;
+    return ok();
+}
+
+size_t w4a16_decode_workspace_bytes(int64_t M, const w4a16_linear *lin, int64_t n_layers) {
+    DecodeShape d;
+    if (M <= 0 || check_stack(lin, n_layers, &d) != W4A16_OK) return 0;
+    return align256((size_t)M * d.maxN * 2) + align256((size_t)M * d.maxK * 2);
+}
+
+int w4a16_decode_step(const w4a16_linear *lin, int64_t n_layers, const uint16_t *x_in, uint16_t *x_out,
+                      int64_t M, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!x_in || !x_out || !workspace) return fail(W4A16_ERR_INVALID_ARG, "x_in, x_out and workspace must be non-NULL");
+    if (M < 1 || M > 8192) return fail(W4A16_ERR_INVALID_ARG, "M must be in [1, 8192]");
+    DecodeShape d;
+    int rc = check_stack(lin, n_layers, &d);
+    if (rc != W4A16_OK) return rc;
+    const size_t t_bytes = align256((size_t)M * d.maxN * 2);
+    const size_t need = t_bytes + align256((size_t)M * d.maxK * 2);
+    if (workspace_bytes < need) return fail(W4A16_ERR_INVALID_ARG, "workspace smaller than w4a16_decode_workspace_bytes()");
+    if (!aligned16(x_in) || !aligned16(x_out) || !aligned16(workspace))
+        return fail(W4A16_ERR_UNSUPPORTED, "x_in, x_out and workspace must be 16-byte aligned");
+    const size_t x_b = (size_t)M * d.H * 2;
+    if (overlaps(workspace, need, x_in, x_b) || overlaps(workspace, need, x_out, x_b))
+        return fail(W4A16_ERR_INVALID_ARG, "workspace overlaps x_in or x_out");
+    uint16_t *T = static_cast<uint16_t *>(workspace);
+    uint16_t *Hb = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + t_bytes);
+    const uint16_t *x = x_in;
+    auto glue = [](hipError_t e) {
+        return e == hipSuccess ? W4A16_OK
+                               : fail(W4A16_ERR_HIP, std::string("glue launch: ") + hipGetErrorString(e));
+    };
+    for (int64_t l = 0; l < n_layers; ++l) {
+        const w4a16_linear *L = lin + 4 * l;
+        const int64_t H = d.H, I = L[2].N / 2;
+        if ((rc = run_gemm(x, L[0].b_packed, L[0].scales, L[0].qzeros, M, H, L[0].N, L[0].G, L[0].zp_bias, T, stream)) ||
+            (rc = glue(launch_rownorm(T, M, L[0].N, H, Hb, stream))) ||
+            (rc = run_gemm(Hb, L[1].b_packed, L[1].scales, L[1].qzeros, M, H, H, L[1].G, L[1].zp_bias, T, stream)) ||
+            (rc = glue(launch_rownorm(T, M, H, H, Hb, stream))) ||
+            (rc = run_gemm(Hb, L[2].b_packed, L[2].scales, L[2].qzeros, M, H, 2 * I, L[2].G, L[2].zp_bias, T, stream)) ||
+            (rc = glue(launch_swiglu_rownorm(T, M, I, Hb, stream))) ||
+            (rc = run_gemm(Hb, L[3].b_packed, L[3].scales, L[3].qzeros, M, I, H, L[3].G, L[3].zp_bias, T, stream)) ||
+            (rc = glue(launch_rownorm(T, M, H, H, x_out, stream))))
+            return rc;
+        x = x_out;
+    }
+    return ok();
+}
+
+int w4a16_release(void) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    int rc = W4A16_OK;
+    for (auto &kv : g_scratch) {
+        int cur = 0;
+        (void)hipGetDevice(&cur);
+        if (hipSetDevice(kv.first.first) != hipSuccess) rc = W4A16_ERR_HIP;
+        if (hipStreamSynchronize(kv.first.second) != hipSuccess) rc = W4A16_ERR_HIP;
+        if (kv.second.partials) (void)hipFree(kv.second.partials);
+        if (kv.second.counters) (void)hipFree(kv.second.counters);
+        (void)hipSetDevice(cur);
+    }
+    g_scratch.clear();
+    if (rc != W4A16_OK) return fail(rc, "synchronising a stream during release failed");
+    return ok();
+}
+
+}  // extern "C"

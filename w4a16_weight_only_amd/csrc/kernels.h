@@ -1,0 +1,57 @@
+// kernels.h -- host-side plan and launch interface between the C ABI layer
+// (api.cpp) and the gfx950 kernels.  Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+enum GemmPath { kPathGemv = 1, kPathMfma = 2 };
+
+// Everything a GEMM launch needs besides the tensors; computed on the host
+// from (M, K, N, G) alone so that it can be inspected without a GPU.
+struct GemmPlan {
+    int path = 0;
+    // GEMV: `words` packed words (8 columns each) per lane, `waves` waves per
+    // workgroup.  MFMA: `mt` 16-row tiles per wave, `waves` along N.
+    int words = 4;
+    int waves = 4;
+    int mt = 1;
+    int64_t tiles_n = 0;      // workgroup tiles along N
+    int64_t tiles_m = 1;      // workgroup tiles along M (MFMA)
+    int splits = 1;           // K-splits across workgroups
+    int64_t split_len = 0;    // K-units per split (GEMV: 16-row chunks; MFMA: 32-row steps)
+    int64_t grid = 0;         // workgroups launched
+    size_t partial_floats = 0;  // fp32 split-K partials needed (0 when splits == 1)
+    size_t counters = 0;        // arrival counters needed
+};
+
+struct GemmArgs {
+    const uint16_t *a;
+    const int32_t *b;
+    const uint16_t *scales;
+    const int32_t *qzeros;
+    int64_t M, K, N, G;
+    int32_t zp;
+    uint16_t *out;
+    float *partials;     // plan.partial_floats floats (or null when unused)
+    uint32_t *counters;  // plan.counters zero-initialised words (or null)
+};
+
+GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G);
+
+hipError_t launch_gemv(const GemmArgs &args, const GemmPlan &plan, hipStream_t stream);
+hipError_t launch_mfma(const GemmArgs &args, const GemmPlan &plan, hipStream_t stream);
+hipError_t launch_repack(const int32_t *src, int32_t *dst, int64_t K, int64_t N, hipStream_t stream);
+
+// Decode-step glue (fp16 in/out, fp32 math).
+// y[m][0..width) = rn(x[m][0..width)) with x row stride ldx.
+hipError_t launch_rownorm(const uint16_t *x, int64_t M, int64_t ldx, int64_t width, uint16_t *y,
+                          hipStream_t stream);
+// y[m][i] = rn_row(silu(gu[m][i]) * gu[m][I + i]), gu is [M, 2I].
+hipError_t launch_swiglu_rownorm(const uint16_t *gu, int64_t M, int64_t I, uint16_t *y,
+                                 hipStream_t stream);
+
+}  // namespace w4a16
