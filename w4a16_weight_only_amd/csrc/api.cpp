@@ -12,7 +12,7 @@
 #include <string>
 #include <utility>
 
-#include "../../include/w4a16.h"
+#include "w4a16.h"
 #include "kernels.h"
 
 namespace w4a16 {
@@ -49,12 +49,13 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // ---------------------------------------------------------------- tuning ---
 // Plan knobs, overridable for tuning sweeps via W4A16_TUNE="key=value,...".
 struct Tune {
-    int64_t gemv_target_wg = 512;   // aim for about this many GEMV workgroups
-    int64_t gemv_min_rows = 2;      // minimum split length in units of row-lane passes
-    int64_t gemv_split_len = 0;     // force the GEMV split length (16-row chunks)
-    int64_t mfma_target_wg = 512;
-    int64_t mfma_max_splits = 16;
+    int64_t gemv_target_waves = 1600;  // aim for about this many GEMV waves
+    int64_t gemv_waves = 8;            // waves per GEMV workgroup (4 or 8)
+    int64_t gemv_splits = 0;           // force the GEMV K-split count
+    int64_t gemv_fold = 0;             // 1: bias/zero removed per chunk (fewer VALU ops)
+    int64_t mfma_target_waves = 0;  // 0: 1024 for 128-row wave tiles, else 2048
     int64_t mfma_splits = 0;        // force the MFMA split count
+    int64_t mfma_wide = 0;          // 1: 128x256 workgroup tiles for M > 64
     int64_t max_partial_bytes = 64ll << 20;
 };
 
@@ -73,11 +74,12 @@ const Tune &tune() {
             if (eq != std::string::npos) {
                 std::string k = kv.substr(0, eq);
                 int64_t val = std::atoll(kv.c_str() + eq + 1);
-                if (k == "gemv_target_wg") v.gemv_target_wg = val;
-                else if (k == "gemv_min_rows") v.gemv_min_rows = val;
-                else if (k == "gemv_split_len") v.gemv_split_len = val;
-                else if (k == "mfma_target_wg") v.mfma_target_wg = val;
-                else if (k == "mfma_max_splits") v.mfma_max_splits = val;
+                if (k == "gemv_target_waves") v.gemv_target_waves = val;
+                else if (k == "gemv_waves") v.gemv_waves = val;
+                else if (k == "gemv_splits") v.gemv_splits = val;
+                else if (k == "gemv_fold") v.gemv_fold = val;
+                else if (k == "mfma_target_waves") v.mfma_target_waves = val;
+                else if (k == "mfma_wide") v.mfma_wide = val;
                 else if (k == "mfma_splits") v.mfma_splits = val;
                 else if (k == "max_partial_bytes") v.max_partial_bytes = val;
             }
@@ -111,45 +113,57 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G) {
     GemmPlan p;
     const int64_t N8 = N / 8;
     if (M <= 8 && N % 32 == 0) {
+        // 256-column tiles (one 128-byte line of every weight row per
+        // workgroup); K-splits to give about gemv_target_waves waves, as few
+        // splits as possible (arrivals at one counter serialise).
         p.path = kPathGemv;
         p.words = gemv_words_for_m(M);
-        p.waves = 4;
+        p.fold = t.gemv_fold != 0;
         const int64_t CL = 32 / p.words, RL = 64 / CL;
         p.tiles_n = cdiv(N8, 32);
         const int64_t nchunks = K / 16;
-        int64_t len;
-        if (t.gemv_split_len > 0) {
-            len = t.gemv_split_len;
+        p.waves = t.gemv_waves == 4 ? 4 : 8;
+        int64_t splits;
+        if (t.gemv_splits > 0) {
+            splits = t.gemv_splits;
         } else {
-            const int64_t splits_target = std::max<int64_t>(1, cdiv(t.gemv_target_wg, p.tiles_n));
-            len = cdiv(nchunks, splits_target);
-            len = std::max<int64_t>(len, t.gemv_min_rows * RL);
-            len = cdiv(len, RL) * RL;
+            splits = cdiv(t.gemv_target_waves, p.tiles_n * p.waves);
+            // keep at least half of each workgroup's row lanes busy
+            splits = std::min<int64_t>(splits, std::max<int64_t>(1, nchunks / (p.waves * RL / 2)));
         }
-        len = std::min<int64_t>(std::max<int64_t>(len, 1), nchunks);
-        p.split_len = len;
-        p.splits = (int)cdiv(nchunks, len);
+        splits = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(splits, 32), nchunks));
+        p.split_len = cdiv(nchunks, splits);
+        p.splits = (int)cdiv(nchunks, p.split_len);
         p.tiles_m = 1;
     } else {
+        // MFMA: wave tile (16*mt rows) x 128 columns; `waves` along N and
+        // `kwaves` along K per workgroup; K-splits across workgroups until
+        // the grid has about mfma_target_waves waves (their fp32 partials are
+        // summed by a second kernel).
         p.path = kPathMfma;
-        p.waves = 2;
-        p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : (M <= 64 ? 4 : 8));
+        if (M <= 16) { p.mt = 1; p.waves = 2; p.kwaves = 4; }
+        else if (M <= 32) { p.mt = 2; p.waves = 2; p.kwaves = 4; }
+        else if (M <= 64) { p.mt = 4; p.waves = 2; p.kwaves = 2; }
+        else if (t.mfma_wide) { p.mt = 8; p.waves = 2; p.kwaves = 2; }
+        else { p.mt = 8; p.waves = 1; p.kwaves = 4; }
         p.tiles_n = cdiv(N8, 16 * p.waves);
         p.tiles_m = cdiv(M, 16 * p.mt);
         const int64_t nsteps = K / 32;
+        const int64_t wg_waves = (int64_t)p.waves * p.kwaves;
         const int64_t tiles = p.tiles_n * p.tiles_m;
-        int64_t splits = t.mfma_splits > 0 ? t.mfma_splits
-                                           : std::max<int64_t>(1, cdiv(t.mfma_target_wg, tiles));
-        splits = std::min<int64_t>(splits, t.mfma_max_splits);
-        const int64_t cap = t.max_partial_bytes / std::max<int64_t>(1, M * N * 4);
-        splits = std::max<int64_t>(1, std::min<int64_t>(splits, cap));
-        splits = std::min<int64_t>(splits, nsteps);
+        const int64_t target = t.mfma_target_waves > 0 ? t.mfma_target_waves : (p.mt >= 8 ? 1024 : 2048);
+        int64_t splits = t.mfma_splits > 0 ? t.mfma_splits : cdiv(target, tiles * wg_waves);
+        // at least two 32-row steps per K-wave, bounded partials
+        splits = std::min<int64_t>(splits, std::max<int64_t>(1, nsteps / (2 * p.kwaves)));
+        splits = std::min<int64_t>(splits, std::max<int64_t>(1, t.max_partial_bytes / std::max<int64_t>(1, M * N * 4)));
+        splits = std::max<int64_t>(1, splits);
         p.split_len = cdiv(nsteps, splits);
         p.splits = (int)cdiv(nsteps, p.split_len);
     }
     p.grid = p.tiles_n * p.tiles_m * p.splits;
+    p.grid = cdiv(p.grid, 8) * 8;  // XCD-aware index mapping needs a multiple of 8
     p.partial_floats = p.splits > 1 ? (size_t)(p.splits * M * N) : 0;
-    p.counters = p.splits > 1 ? (size_t)(p.tiles_n * p.tiles_m) : 0;
+    p.counters = (p.splits > 1 && p.path == kPathGemv) ? (size_t)(p.tiles_n * p.tiles_m) : 0;
     return p;
 }
 

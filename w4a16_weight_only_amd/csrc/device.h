@@ -39,20 +39,35 @@ __device__ __forceinline__ uint32_t gather_byte_pair(uint32_t lo, uint32_t hi) {
     return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
+// Masks and biases for the nibble -> fp16 conversion, held in VGPRs whose
+// values the compiler cannot see (an empty asm with a "+v" operand emits no
+// instruction).  gfx9 VOP3 encodings take no literal constants, so with
+// literals the compiler splits AND-OR into v_and + v_or; with register
+// operands it selects one v_and_or_b32 per pair.
+struct NibbleConsts {
+    uint32_t mask_lo, mask_hi, bias_lo, bias_hi;
+};
+
+__device__ __forceinline__ NibbleConsts nibble_consts() {
+    uint32_t a = kMaskLo, b = kMaskHi, c = kMagicLo, d = kMagicHi;
+    asm volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+    return NibbleConsts{a, b, c, d};
+}
+
 // Biased fp16 pair for nibble 2B (H = 0) or 2B+1 (H = 1) of the gathered pair
 // `p`: lanes hold (bias + q_lo_row, bias + q_hi_row), bias 1024 or 64.
 template <int H>
-__device__ __forceinline__ uint32_t biased_pair(uint32_t p) {
-    return H ? ((p & kMaskHi) | kMagicHi) : ((p & kMaskLo) | kMagicLo);
+__device__ __forceinline__ uint32_t biased_pair(uint32_t p, const NibbleConsts &k) {
+    return H ? ((p & k.mask_hi) | k.bias_hi) : ((p & k.mask_lo) | k.bias_lo);
 }
 
 // Bias-plus-zero constant for nibble position T (0..7) of a packed zero word:
 // (1024 + z) for even T, (64 + z) for odd T, in both fp16 lanes.
 template <int T>
-__device__ __forceinline__ f16x2 zero_pair_from_word(uint32_t zword) {
+__device__ __forceinline__ f16x2 zero_pair_from_word(uint32_t zword, const NibbleConsts &k) {
     constexpr int B = T / 2;
     uint32_t p = gather_byte_pair<B>(zword, zword);
-    return as_f16x2(biased_pair<T & 1>(p));
+    return as_f16x2(biased_pair<T & 1>(p, k));
 }
 
 // Same constant for a symmetric zero point z in [0, 15].
@@ -60,6 +75,58 @@ template <int T>
 __device__ __forceinline__ f16x2 zero_pair_const(uint32_t z) {
     uint32_t v = (T & 1) ? (kMagicHi | (z << 4) | (z << 20)) : (kMagicLo | z | (z << 16));
     return as_f16x2(v);
+}
+
+// Raw buffer resource over `bytes` bytes (< 2^32) at `base`: loads take a
+// per-lane byte offset plus a wave-uniform byte offset held in an SGPR, so a
+// stream of rows at a uniform stride costs no vector address arithmetic.
+// Out-of-range reads return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buffer_load_x4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ u32x2 buffer_load_x2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ uint32_t buffer_load_x1(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
+}
+
+// dot(x, y) + 0 into a fresh register (VOP3P form: no zeroing move first).
+__device__ __forceinline__ float dot2_first(f16x2 x, f16x2 y) {
+    float r;
+    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(x), "v"(y));
+    return r;
+}
+
+// Exchange for one transpose-reduce step across lane halves: returns
+// lo + hi where, in lanes whose `mask` bit is clear, lo/hi are this lane's
+// lower-half value and the partner's lower-half value, and in the other lanes
+// the two upper-half values.  mask 32 and 16 use the gfx950 lane-swap
+// instructions; mask 8 uses a DPP row rotation by 8 (lane ^ 8 in a row).
+template <int MASK>
+__device__ __forceinline__ float swap_add(float lo, float hi, int lane) {
+    if constexpr (MASK == 32 || MASK == 16) {
+        // Written as asm with both registers as in/out operands: with the
+        // two-result builtin this compiler added the first result to itself.
+        // The s_nops keep the swap clear of neighbouring VALU writes/reads,
+        // which the compiler cannot see through the asm.
+        float a = lo, b = hi;
+        if constexpr (MASK == 32)
+            asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+        else
+            asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+        return a + b;
+    } else {
+        static_assert(MASK == 8, "lane-xor 8 within a 16-lane row");
+        const float pl = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                             0u, __builtin_bit_cast(uint32_t, lo), 0x128, 0xf, 0xf, false));
+        const float ph = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                             0u, __builtin_bit_cast(uint32_t, hi), 0x128, 0xf, 0xf, false));
+        return (lane & 8) ? hi + ph : lo + pl;
+    }
 }
 
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t bits16) {
@@ -70,16 +137,24 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
     return __builtin_bit_cast(uint16_t, (f16)x);  // round-to-nearest-even
 }
 
-// Device-scope release/acquire around the split-K arrival counter: partial
-// sums written by workgroups on other XCDs must be visible through their L2s.
-__device__ __forceinline__ void fence_release_agent() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+// Split-K hand-off between workgroups that may sit on different XCDs (each
+// with its own L2).  Partial sums are written with device-scope stores (sc1:
+// coherent at device scope by themselves) and read back with device-scope
+// loads (sc1), so no whole-L2 write-back or invalidate is needed: a writer
+// waits for its stores to complete (vmcnt(0)) before it bumps the tile's
+// arrival counter, and the workgroup that brings the counter to `splits`
+// reads every split's partials.  An agent-scope release/acquire fence pair
+// would instead write back and invalidate the XCD's whole L2 once per wave.
+__device__ __forceinline__ void store_partial(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void fence_acquire_agent() {
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+__device__ __forceinline__ float load_partial(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima).
+__device__ __forceinline__ void wait_vm_zero() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ __forceinline__ uint32_t arrive_agent(uint32_t *counter) {
-    return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void reset_counter_agent(uint32_t *counter) {
     __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -2,25 +2,30 @@
 //
 // out = a . ((q - z) * s)  (vLLM PR #37352 write-up, "Code analysis" item 1).
 // Decode is bound by streaming the weights once (inference-engine article,
-// section 1.2), so this kernel is built around the weight stream:
+// section 1.2), so the kernel is organised around that stream:
 //
-//  * A workgroup owns a 256-column tile (32 packed words = 128 bytes of every
-//    weight row) and a K-split.  In a wave, CL "column lanes" cover the 128
-//    bytes of a row with WORDS-word loads (16 bytes when WORDS = 4) and RL =
-//    64/CL "row lanes" take different 16-row chunks, so every load
-//    instruction reads whole 128-byte lines.
-//  * Each lane unpacks its nibbles in registers two rows at a time (see
-//    device.h), subtracts the zero point exactly in fp16 and accumulates
-//    a_k*(q-z) for the row pair with one v_dot2_f32_f16 (fp32 accumulate).
-//    The 16-row chunk lies inside one K-group, so the group scale is applied
-//    once per chunk in fp32.  No matrix cores: at M <= 8 the work is a
-//    bandwidth-bound matrix-vector product.
+//  * A workgroup owns a 256-column tile (32 packed words = one 128-byte line
+//    of every weight row) and a K range.  In a wave, CL column lanes cover the
+//    line with WORDS-word loads (16 bytes when WORDS = 4) and RL = 64/CL row
+//    lanes take different 16-row chunks, so each load instruction reads whole
+//    lines (narrower tiles that split lines between workgroups cost up to 60%
+//    more time on MI355X).  Loads are unconditional -- lanes past N read a
+//    clamped, valid address and their columns are never stored -- so the
+//    compiler can wait for each row pair as it lands.
+//  * Each lane converts nibbles two rows at a time (device.h) and accumulates
+//    a_k * (q - z) for the row pair with one v_dot2_f32_f16 into fp32.  In the
+//    exact form the zero point is subtracted in fp16 before the dot (exact:
+//    small integers); in the folded form the dot takes (bias + q) and
+//    (bias + z) * sum(a) is removed once per 16-row chunk (one VALU op fewer
+//    per pair, fp32 rounding of the biased sum).  The group scale is applied
+//    once per chunk (a chunk lies in one K-group).  No matrix cores.
 //  * Row lanes are reduced with a transpose-reduce over lane-xor shuffles
-//    (each step halves the values a lane holds), waves through LDS, and
-//    K-splits through an fp32 partials buffer: the last workgroup to arrive at
-//    a tile's counter sums the splits in split order (deterministic; the
-//    reduce-in-shared-memory-not-float-atomics lesson of the same article,
-//    section 3.4) and resets the counter for the next call.
+//    (each step halves the values a lane holds), waves through LDS.  K-splits
+//    meet in an fp32 partials buffer: the last workgroup to arrive at a
+//    tile's counter loads every split's partials at once and sums them in
+//    split order (deterministic; an explicit reduction rather than float
+//    atomics, the lesson of the same article's section 3.4), then resets the
+//    counter for the next call.
 #include "device.h"
 #include "kernels.h"
 
@@ -30,11 +35,29 @@ namespace {
 constexpr int kTileWords = 32;  // 256 columns per workgroup tile
 constexpr int kTileCols = 256;
 constexpr int kChunkRows = 16;  // rows per lane chunk = 8 row pairs
+constexpr int kMaxSplits = 32;  // bound of the planner's K-split count
 
 template <int W>
 struct Words {
     uint32_t v[W];
 };
+
+template <int W>
+__device__ __forceinline__ Words<W> buffer_words(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff);
+template <>
+__device__ __forceinline__ Words<4> buffer_words<4>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x4 t = buffer_load_x4(r, voff, soff);
+    return Words<4>{{t.x, t.y, t.z, t.w}};
+}
+template <>
+__device__ __forceinline__ Words<2> buffer_words<2>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x2 t = buffer_load_x2(r, voff, soff);
+    return Words<2>{{t.x, t.y}};
+}
+template <>
+__device__ __forceinline__ Words<1> buffer_words<1>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return Words<1>{{buffer_load_x1(r, voff, soff)}};
+}
 
 template <int W>
 __device__ __forceinline__ Words<W> load_words(const uint32_t *p);
@@ -53,45 +76,72 @@ __device__ __forceinline__ Words<1> load_words<1>(const uint32_t *p) {
     return Words<1>{{*p}};
 }
 
-// One byte position B of one word pair: two columns (nibbles 2B, 2B+1) x two
-// rows, accumulated into p[m][col0 + 2B], p[m][col0 + 2B + 1].
-template <int M, int COLS, int B>
-__device__ __forceinline__ void dot_byte(uint32_t lo, uint32_t hi, const f16x2 *zc, int col0,
-                                         const uint32_t (&apair)[M], float (&p)[M][COLS]) {
-    uint32_t pr = gather_byte_pair<B>(lo, hi);
-    f16x2 v0 = as_f16x2(biased_pair<0>(pr)) - zc[col0 + 2 * B];
-    f16x2 v1 = as_f16x2(biased_pair<1>(pr)) - zc[col0 + 2 * B + 1];
+// One byte position B of one word pair: columns col0+2B, col0+2B+1, two rows.
+template <int M, int COLS, int B, bool FOLD, bool FIRST>
+__device__ __forceinline__ void dot_byte(uint32_t lo, uint32_t hi, int col0, const f16x2 *zc,
+                                         const uint32_t (&apair)[M], const NibbleConsts &nk,
+                                         float (&p)[M][COLS]) {
+    const uint32_t pr = gather_byte_pair<B>(lo, hi);
+    f16x2 v0 = as_f16x2(biased_pair<0>(pr, nk));
+    f16x2 v1 = as_f16x2(biased_pair<1>(pr, nk));
+    if (!FOLD) {
+        v0 = v0 - zc[col0 + 2 * B];
+        v1 = v1 - zc[col0 + 2 * B + 1];
+    }
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-        f16x2 av = as_f16x2(apair[m]);
-        p[m][col0 + 2 * B] = __builtin_amdgcn_fdot2(v0, av, p[m][col0 + 2 * B], false);
-        p[m][col0 + 2 * B + 1] = __builtin_amdgcn_fdot2(v1, av, p[m][col0 + 2 * B + 1], false);
+        const f16x2 av = as_f16x2(apair[m]);
+        if (FIRST) {
+            p[m][col0 + 2 * B] = dot2_first(v0, av);
+            p[m][col0 + 2 * B + 1] = dot2_first(v1, av);
+        } else {
+            p[m][col0 + 2 * B] = __builtin_amdgcn_fdot2(v0, av, p[m][col0 + 2 * B], false);
+            p[m][col0 + 2 * B + 1] = __builtin_amdgcn_fdot2(v1, av, p[m][col0 + 2 * B + 1], false);
+        }
     }
 }
 
-template <int M, int WORDS, int NWAVES, bool ASYM>
-__global__ __launch_bounds__(64 * NWAVES) void gemv_kernel(
+template <int T>
+__device__ __forceinline__ f16x2 zero_pair(bool asym, uint32_t zword, uint32_t zp, const NibbleConsts &nk) {
+    return asym ? zero_pair_from_word<T>(zword, nk) : zero_pair_const<T>(zp);
+}
+
+// Logical workgroup index for hardware index `bid` (grid a multiple of 8):
+// workgroups are dealt to the 8 XCDs round-robin, so this gives each XCD a
+// contiguous run of logical indices (neighbouring tiles and their scales).
+__device__ __forceinline__ int xcd_local_index(int bid, int grid) {
+    return (bid & 7) * (grid >> 3) + (bid >> 3);
+}
+
+template <int M, int WORDS, int NW, bool ASYM, bool FOLD>
+__global__ __launch_bounds__(64 * NW) void gemv_kernel(
     const uint16_t *__restrict__ a, const uint32_t *__restrict__ b,
     const uint16_t *__restrict__ scales, const uint32_t *__restrict__ qzeros, int K, int N, int G,
-    uint32_t zp, int split_len, int splits, uint16_t *__restrict__ out,
+    uint32_t zp, int tiles, int split_len, int splits, uint16_t *__restrict__ out,
     float *__restrict__ partials, uint32_t *__restrict__ counters) {
     constexpr int CL = kTileWords / WORDS;  // column lanes per row segment
     constexpr int RL = 64 / CL;             // row lanes
     constexpr int COLS = 8 * WORDS;         // columns per lane
     static_assert(COLS == 4 * RL, "four columns per lane after the row-lane reduction");
 
+    const int logical = xcd_local_index(blockIdx.x, gridDim.x);
+    if (logical >= tiles * splits) return;
+    const int tile = logical % tiles;
+    const int split = logical / tiles;
+
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int cl = lane % CL;
     const int rl = lane / CL;
     const int N8 = N >> 3;
-    const int tile = blockIdx.x;
-    const int split = blockIdx.y;
-    const int word0 = tile * kTileWords + cl * WORDS;
-    const bool col_ok = word0 < N8;  // N % 32 == 0: a lane's words are all in or all out
+    // Lanes past N read a valid (clamped) address; their columns are never stored.
+    const int word0 = min(tile * kTileWords + cl * WORDS, N8 - WORDS);
     const int nchunks = K / kChunkRows;
     const int c_begin = split * split_len;
     const int c_end = min(c_begin + split_len, nchunks);
+    const NibbleConsts nk = nibble_consts();
+    const __amdgpu_buffer_rsrc_t brs = buffer_rsrc(b, (uint32_t)((uint64_t)K * N8 * 4));
+    const uint32_t row_bytes = (uint32_t)N8 * 4u;
 
     float acc[M][COLS];
 #pragma unroll
@@ -99,193 +149,227 @@ __global__ __launch_bounds__(64 * NWAVES) void gemv_kernel(
 #pragma unroll
         for (int j = 0; j < COLS; ++j) acc[m][j] = 0.f;
 
-    for (int c = c_begin + wave * RL + rl; c < c_end; c += NWAVES * RL) {
+    for (int c = c_begin + wave * RL + rl; c < c_end; c += NW * RL) {
         const int k0 = c * kChunkRows;
         const int g = k0 / G;
 
-        Words<WORDS> w[kChunkRows];
-        if (col_ok) {
-#pragma unroll
-            for (int r = 0; r < kChunkRows; ++r)
-                w[r] = load_words<WORDS>(b + (size_t)(k0 + r) * N8 + word0);
-        } else {
-#pragma unroll
-            for (int r = 0; r < kChunkRows; ++r)
-#pragma unroll
-                for (int x = 0; x < WORDS; ++x) w[r].v[x] = 0u;
-        }
-        // a[m][k0 .. k0+15] as 8 fp16 pairs per row.
+        // Small loads first, the weight stream last, so that row pairs are
+        // consumed in order as they land.
         uint32_t av[M][8];
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             const u32x4 *ap = reinterpret_cast<const u32x4 *>(a + (size_t)m * K + k0);
-            u32x4 lo = ap[0], hi = ap[1];
+            const u32x4 lo = ap[0], hi = ap[1];
             av[m][0] = lo.x; av[m][1] = lo.y; av[m][2] = lo.z; av[m][3] = lo.w;
             av[m][4] = hi.x; av[m][5] = hi.y; av[m][6] = hi.z; av[m][7] = hi.w;
         }
-        // Scales of the lane's COLS columns in group g (COLS fp16 = WORDS x 16 bytes).
         uint32_t sw[COLS / 2];
-        if (col_ok) {
+        {
             const u32x4 *sp = reinterpret_cast<const u32x4 *>(scales + (size_t)g * N + word0 * 8);
 #pragma unroll
             for (int x = 0; x < WORDS; ++x) {
-                u32x4 t = sp[x];
+                const u32x4 t = sp[x];
                 sw[4 * x] = t.x; sw[4 * x + 1] = t.y; sw[4 * x + 2] = t.z; sw[4 * x + 3] = t.w;
             }
-        } else {
-#pragma unroll
-            for (int x = 0; x < COLS / 2; ++x) sw[x] = 0u;
         }
+        Words<WORDS> zw;
+#pragma unroll
+        for (int x = 0; x < WORDS; ++x) zw.v[x] = 0u;
+        if (ASYM) zw = load_words<WORDS>(qzeros + (size_t)g * N8 + word0);
+        Words<WORDS> w[kChunkRows];
+        const uint32_t voff = ((uint32_t)k0 * (uint32_t)N8 + (uint32_t)word0) * 4u;
+#pragma unroll
+        for (int r = 0; r < kChunkRows; ++r) w[r] = buffer_words<WORDS>(brs, voff, (uint32_t)r * row_bytes);
+
         f16x2 zc[COLS];
-        if (ASYM) {
-            Words<WORDS> zw;
-            if (col_ok) {
-                zw = load_words<WORDS>(qzeros + (size_t)g * N8 + word0);
-            } else {
-#pragma unroll
-                for (int x = 0; x < WORDS; ++x) zw.v[x] = 0u;
-            }
+        if (!FOLD) {
 #pragma unroll
             for (int x = 0; x < WORDS; ++x) {
-                zc[8 * x + 0] = zero_pair_from_word<0>(zw.v[x]);
-                zc[8 * x + 1] = zero_pair_from_word<1>(zw.v[x]);
-                zc[8 * x + 2] = zero_pair_from_word<2>(zw.v[x]);
-                zc[8 * x + 3] = zero_pair_from_word<3>(zw.v[x]);
-                zc[8 * x + 4] = zero_pair_from_word<4>(zw.v[x]);
-                zc[8 * x + 5] = zero_pair_from_word<5>(zw.v[x]);
-                zc[8 * x + 6] = zero_pair_from_word<6>(zw.v[x]);
-                zc[8 * x + 7] = zero_pair_from_word<7>(zw.v[x]);
-            }
-        } else {
-#pragma unroll
-            for (int x = 0; x < WORDS; ++x) {
-                zc[8 * x + 0] = zero_pair_const<0>(zp);
-                zc[8 * x + 1] = zero_pair_const<1>(zp);
-                zc[8 * x + 2] = zero_pair_const<2>(zp);
-                zc[8 * x + 3] = zero_pair_const<3>(zp);
-                zc[8 * x + 4] = zero_pair_const<4>(zp);
-                zc[8 * x + 5] = zero_pair_const<5>(zp);
-                zc[8 * x + 6] = zero_pair_const<6>(zp);
-                zc[8 * x + 7] = zero_pair_const<7>(zp);
+                zc[8 * x + 0] = zero_pair<0>(ASYM, zw.v[x], zp, nk);
+                zc[8 * x + 1] = zero_pair<1>(ASYM, zw.v[x], zp, nk);
+                zc[8 * x + 2] = zero_pair<2>(ASYM, zw.v[x], zp, nk);
+                zc[8 * x + 3] = zero_pair<3>(ASYM, zw.v[x], zp, nk);
+                zc[8 * x + 4] = zero_pair<4>(ASYM, zw.v[x], zp, nk);
+                zc[8 * x + 5] = zero_pair<5>(ASYM, zw.v[x], zp, nk);
+                zc[8 * x + 6] = zero_pair<6>(ASYM, zw.v[x], zp, nk);
+                zc[8 * x + 7] = zero_pair<7>(ASYM, zw.v[x], zp, nk);
             }
         }
 
         float p[M][COLS];
+        {  // row pair (k0, k0 + 1) starts the sums
+            uint32_t apair[M];
 #pragma unroll
-        for (int m = 0; m < M; ++m)
+            for (int m = 0; m < M; ++m) apair[m] = av[m][0];
 #pragma unroll
-            for (int j = 0; j < COLS; ++j) p[m][j] = 0.f;
-
+            for (int x = 0; x < WORDS; ++x) {
+                const uint32_t lo = w[0].v[x], hi = w[1].v[x];
+                dot_byte<M, COLS, 0, FOLD, true>(lo, hi, 8 * x, zc, apair, nk, p);
+                dot_byte<M, COLS, 1, FOLD, true>(lo, hi, 8 * x, zc, apair, nk, p);
+                dot_byte<M, COLS, 2, FOLD, true>(lo, hi, 8 * x, zc, apair, nk, p);
+                dot_byte<M, COLS, 3, FOLD, true>(lo, hi, 8 * x, zc, apair, nk, p);
+            }
+        }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {  // row pair (k0 + 2j, k0 + 2j + 1)
+        for (int j = 1; j < 8; ++j) {  // row pair (k0 + 2j, k0 + 2j + 1)
             uint32_t apair[M];
 #pragma unroll
             for (int m = 0; m < M; ++m) apair[m] = av[m][j];
 #pragma unroll
             for (int x = 0; x < WORDS; ++x) {
                 const uint32_t lo = w[2 * j].v[x], hi = w[2 * j + 1].v[x];
-                dot_byte<M, COLS, 0>(lo, hi, zc, 8 * x, apair, p);
-                dot_byte<M, COLS, 1>(lo, hi, zc, 8 * x, apair, p);
-                dot_byte<M, COLS, 2>(lo, hi, zc, 8 * x, apair, p);
-                dot_byte<M, COLS, 3>(lo, hi, zc, 8 * x, apair, p);
+                dot_byte<M, COLS, 0, FOLD, false>(lo, hi, 8 * x, zc, apair, nk, p);
+                dot_byte<M, COLS, 1, FOLD, false>(lo, hi, 8 * x, zc, apair, nk, p);
+                dot_byte<M, COLS, 2, FOLD, false>(lo, hi, 8 * x, zc, apair, nk, p);
+                dot_byte<M, COLS, 3, FOLD, false>(lo, hi, 8 * x, zc, apair, nk, p);
+            }
+        }
+
+        float asum[M];
+        if (FOLD) {
+            const f16x2 ones = as_f16x2(0x3c003c00u);
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                float s = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) s = __builtin_amdgcn_fdot2(as_f16x2(av[m][j]), ones, s, false);
+                asum[m] = s;
             }
         }
 #pragma unroll
         for (int j = 0; j < COLS; ++j) {
             const uint32_t bits = (j & 1) ? (sw[j >> 1] >> 16) : (sw[j >> 1] & 0xffffu);
             const float s = f16_bits_to_f32(bits);
+            if (FOLD) {
+                const uint32_t zq = ASYM ? ((zw.v[j >> 3] >> (4 * (j & 7))) & 0xfu) : zp;
+                const float zb = (float)((j & 1) ? 64u + zq : 1024u + zq);
 #pragma unroll
-            for (int m = 0; m < M; ++m) acc[m][j] = __builtin_fmaf(s, p[m][j], acc[m][j]);
-        }
-    }
-
-    // Transpose-reduce over the row lanes (lane bits 5 .. log2(CL)): after the
-    // step with mask 2^b the lanes with that bit set keep the upper half of
-    // their values.  Lane (cl, rl) ends with columns cl*COLS + 4*rl + 0..3.
+                for (int m = 0; m < M; ++m)
+                    acc[m][j] = __builtin_fmaf(s, __builtin_fmaf(-zb, asum[m], p[m][j]), acc[m][j]);
+            } else {
 #pragma unroll
-    for (int step = 0; (32 >> step) >= CL; ++step) {
-        const int mask = 32 >> step;
-        const int half = COLS >> (step + 1);
-        const bool upper = (lane & mask) != 0;
-#pragma unroll
-        for (int i = 0; i < half; ++i) {
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                const float lo = acc[m][i], hi = acc[m][half + i];
-                const float keep = upper ? hi : lo;
-                const float send = upper ? lo : hi;
-                acc[m][i] = keep + __shfl_xor(send, mask);
+                for (int m = 0; m < M; ++m) acc[m][j] = __builtin_fmaf(s, p[m][j], acc[m][j]);
             }
         }
     }
 
-    __shared__ float red[NWAVES][M][kTileCols];
+    // Transpose-reduce over the row lanes (lane bits 5 .. log2(CL)): after the
+    // step with mask 2^b the lanes with that bit set hold the sums of the
+    // upper half of the columns they held.  Lane (cl, rl) ends with columns
+    // cl*COLS + 4*rl + 0..3.
+    if constexpr (CL <= 32) {
+#pragma unroll
+        for (int i = 0; i < COLS / 2; ++i)
+#pragma unroll
+            for (int m = 0; m < M; ++m) acc[m][i] = swap_add<32>(acc[m][i], acc[m][COLS / 2 + i], lane);
+    }
+    if constexpr (CL <= 16) {
+#pragma unroll
+        for (int i = 0; i < COLS / 4; ++i)
+#pragma unroll
+            for (int m = 0; m < M; ++m) acc[m][i] = swap_add<16>(acc[m][i], acc[m][COLS / 4 + i], lane);
+    }
+    if constexpr (CL <= 8) {
+#pragma unroll
+        for (int i = 0; i < COLS / 8; ++i)
+#pragma unroll
+            for (int m = 0; m < M; ++m) acc[m][i] = swap_add<8>(acc[m][i], acc[m][COLS / 8 + i], lane);
+    }
+    static_assert(CL >= 8, "at most three row-lane reduction steps");
+
+    __shared__ float red[NW][M][kTileCols];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-        f32x4 v = {acc[m][0], acc[m][1], acc[m][2], acc[m][3]};
+        const f32x4 v = {acc[m][0], acc[m][1], acc[m][2], acc[m][3]};
         *reinterpret_cast<f32x4 *>(&red[wave][m][cl * COLS + 4 * rl]) = v;
     }
     __syncthreads();
 
+    // Epilogue: one (row, column) per thread and pass.
+    constexpr int PASSES = (M * kTileCols + 64 * NW - 1) / (64 * NW);
     const int col_base = tile * kTileCols;
-    for (int t = threadIdx.x; t < kTileCols; t += 64 * NWAVES) {
-        const int col = col_base + t;
-        if (col >= N) continue;
+    float sums[PASSES];
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-            float s = 0.f;
+    for (int i = 0; i < PASSES; ++i) {
+        const int t = threadIdx.x + i * 64 * NW;
+        float s = 0.f;
+        if (t < M * kTileCols) {
 #pragma unroll
-            for (int wv = 0; wv < NWAVES; ++wv) s += red[wv][m][t];
-            if (splits == 1)
-                out[(size_t)m * N + col] = f32_to_f16_bits(s);
-            else
-                partials[((size_t)split * M + m) * N + col] = s;
+            for (int wv = 0; wv < NW; ++wv) s += red[wv][t / kTileCols][t % kTileCols];
         }
+        sums[i] = s;
     }
-    if (splits == 1) return;
+    if (splits == 1) {
+#pragma unroll
+        for (int i = 0; i < PASSES; ++i) {
+            const int t = threadIdx.x + i * 64 * NW;
+            const int col = col_base + t % kTileCols;
+            if (t < M * kTileCols && col < N) out[(size_t)(t / kTileCols) * N + col] = f32_to_f16_bits(sums[i]);
+        }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < PASSES; ++i) {
+        const int t = threadIdx.x + i * 64 * NW;
+        const int col = col_base + t % kTileCols;
+        if (t < M * kTileCols && col < N)
+            store_partial(&partials[((size_t)split * M + t / kTileCols) * N + col], sums[i]);
+    }
 
     // Split-K: the last workgroup to arrive sums every split in split order.
-    fence_release_agent();
+    wait_vm_zero();
     __syncthreads();
     __shared__ uint32_t last;
     if (threadIdx.x == 0) last = (arrive_agent(&counters[tile]) == (uint32_t)(splits - 1)) ? 1u : 0u;
     __syncthreads();
     if (!last) return;
-    fence_acquire_agent();
-    for (int t = threadIdx.x; t < kTileCols; t += 64 * NWAVES) {
-        const int col = col_base + t;
-        if (col >= N) continue;
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
+    for (int i = 0; i < PASSES; ++i) {
+        const int t = threadIdx.x + i * 64 * NW;
+        const int col = col_base + t % kTileCols;
+        if (t < M * kTileCols && col < N) {
+            // Issue every split's load before the first add.
+            float v[kMaxSplits];
+#pragma unroll
+            for (int sp = 0; sp < kMaxSplits; ++sp)
+                v[sp] = sp < splits ? load_partial(&partials[((size_t)sp * M + t / kTileCols) * N + col]) : 0.f;
             float s = 0.f;
-            for (int sp = 0; sp < splits; ++sp) s += partials[((size_t)sp * M + m) * N + col];
-            out[(size_t)m * N + col] = f32_to_f16_bits(s);
+#pragma unroll
+            for (int sp = 0; sp < kMaxSplits; ++sp) s += v[sp];
+            out[(size_t)(t / kTileCols) * N + col] = f32_to_f16_bits(s);
         }
     }
     if (threadIdx.x == 0) reset_counter_agent(&counters[tile]);
 }
 
-template <int M, int WORDS>
-hipError_t launch_m(const GemmArgs &g, const GemmPlan &p, hipStream_t stream) {
-    constexpr int NW = 4;
-    dim3 grid((unsigned)p.tiles_n, (unsigned)p.splits, 1);
+template <int M, int WORDS, int NW, bool FOLD>
+hipError_t launch_v(const GemmArgs &g, const GemmPlan &p, hipStream_t stream) {
+    dim3 grid((unsigned)p.grid, 1, 1);
     dim3 block(64 * NW, 1, 1);
     const uint32_t *b = reinterpret_cast<const uint32_t *>(g.b);
     const uint32_t *qz = reinterpret_cast<const uint32_t *>(g.qzeros);
     if (g.qzeros)
-        hipLaunchKernelGGL((gemv_kernel<M, WORDS, NW, true>), grid, block, 0, stream, g.a, b,
-                           g.scales, qz, (int)g.K, (int)g.N, (int)g.G, (uint32_t)g.zp,
+        hipLaunchKernelGGL((gemv_kernel<M, WORDS, NW, true, FOLD>), grid, block, 0, stream, g.a, b, g.scales,
+                           qz, (int)g.K, (int)g.N, (int)g.G, (uint32_t)g.zp, (int)p.tiles_n,
                            (int)p.split_len, p.splits, g.out, g.partials, g.counters);
     else
-        hipLaunchKernelGGL((gemv_kernel<M, WORDS, NW, false>), grid, block, 0, stream, g.a, b,
-                           g.scales, qz, (int)g.K, (int)g.N, (int)g.G, (uint32_t)g.zp,
+        hipLaunchKernelGGL((gemv_kernel<M, WORDS, NW, false, FOLD>), grid, block, 0, stream, g.a, b, g.scales,
+                           qz, (int)g.K, (int)g.N, (int)g.G, (uint32_t)g.zp, (int)p.tiles_n,
                            (int)p.split_len, p.splits, g.out, g.partials, g.counters);
     return hipGetLastError();
+}
+
+template <int M, int WORDS>
+hipError_t launch_m(const GemmArgs &g, const GemmPlan &p, hipStream_t stream) {
+    if (p.fold)
+        return p.waves == 8 ? launch_v<M, WORDS, 8, true>(g, p, stream) : launch_v<M, WORDS, 4, true>(g, p, stream);
+    return p.waves == 8 ? launch_v<M, WORDS, 8, false>(g, p, stream) : launch_v<M, WORDS, 4, false>(g, p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gemv(const GemmArgs &g, const GemmPlan &p, hipStream_t stream) {
+    if (p.splits > kMaxSplits) return hipErrorInvalidValue;
     switch (g.M) {
         case 1: return launch_m<1, 4>(g, p, stream);
         case 2: return launch_m<2, 4>(g, p, stream);

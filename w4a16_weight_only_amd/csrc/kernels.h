@@ -19,6 +19,8 @@ struct GemmPlan {
     int words = 4;
     int waves = 4;
     int mt = 1;
+    int kwaves = 1;           // MFMA: waves dividing a workgroup's K range (LDS-reduced)
+    bool fold = false;        // GEMV: remove bias and zero per chunk instead of per pair
     int64_t tiles_n = 0;      // workgroup tiles along N
     int64_t tiles_m = 1;      // workgroup tiles along M (MFMA)
     int splits = 1;           // K-splits across workgroups
