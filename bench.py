@@ -240,6 +240,14 @@ def bench_decode(torch, w4, stream, Ms, steps, warmup):
     return res
 
 
+EXTRA_ROWS = {
+    "batched_M32": lambda t, w, st, k, wu: bench_gemm(t, w, st, 32, 4096, 12800, 128, True, k, wu, 3),
+    "prefill_M256": lambda t, w, st, k, wu: bench_gemm(t, w, st, 256, 12800, 4096, 128, True, k, wu, 4),
+    "repack_K4096_N12800": lambda t, w, st, k, wu: bench_repack(t, w, st, 4096, 12800, k, wu),
+    "decode_step": lambda t, w, st, k, wu: bench_decode(t, w, st, [1, 32], max(5, k // 20), 3),
+}
+
+
 def cpu_baseline(seconds=10.0):
     """The oracle (plain single-threaded C, fp64) on the same M=1 workload,
     repeated for about `seconds`."""
@@ -279,8 +287,11 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline only (no extra rows, no CPU baseline)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--profile", action="store_true",
-                    help="for rocprofv3 runs: the headline launches plus one 256 MiB device copy "
-                         "(a plain copy kernel of known size, to calibrate HBM byte counters)")
+                    help="for rocprofv3 runs: one 256 MiB device copy first (a plain copy kernel of "
+                         "known size, to calibrate HBM byte counters); implies --quick unless --only")
+    ap.add_argument("--only", default="",
+                    help="comma-separated extra rows to run after the headline (%s); no CPU baseline"
+                         % ",".join(EXTRA_ROWS))
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the W4A16 linear "
@@ -309,7 +320,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         log("profile: 256 MiB device copy done")
-        args.quick = True
+        args.quick = not args.only
 
     log("headline: M=1 K=4096 N=12800 G=128 sym, %d steps" % args.steps)
     head = bench_gemm(torch, w4, stream, 1, 4096, 12800, 128, False, args.steps, args.warmup, seed=2)
@@ -317,15 +328,18 @@ def main():
 
     extra = {}
     cpu = None
-    if not args.quick:
-        log("batched M=32")
-        extra["batched_M32"] = bench_gemm(torch, w4, stream, 32, 4096, 12800, 128, True, args.steps, args.warmup, 3)
-        log("prefill M=256")
-        extra["prefill_M256"] = bench_gemm(torch, w4, stream, 256, 12800, 4096, 128, True, args.steps, args.warmup, 4)
-        log("repack 4096x12800")
-        extra["repack_K4096_N12800"] = bench_repack(torch, w4, stream, 4096, 12800, args.steps, args.warmup)
-        log("decode step, 40 layers")
-        extra["decode_step"] = bench_decode(torch, w4, stream, [1, 32], max(5, args.steps // 20), 3)
+    if args.only:
+        rows = [r for r in args.only.split(",") if r]
+        bad = [r for r in rows if r not in EXTRA_ROWS]
+        if bad:
+            print("unknown rows %s (choose from %s)" % (bad, ",".join(EXTRA_ROWS)), file=sys.stderr)
+            sys.exit(2)
+    else:
+        rows = [] if args.quick else list(EXTRA_ROWS)
+    for r in rows:
+        log(r)
+        extra[r] = EXTRA_ROWS[r](torch, w4, stream, args.steps, args.warmup)
+    if not args.quick and not args.only:
         log("cpu baseline (oracle) ~%.0f s" % args.cpu_seconds)
         cpu = cpu_baseline(args.cpu_seconds)
 
