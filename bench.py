@@ -240,11 +240,32 @@ def bench_decode(torch, w4, stream, Ms, steps, warmup):
     return res
 
 
+def bench_copy_context(torch, stream, nbytes, steps, warmup):
+    """Context only: a plain device elementwise copy (torch's own kernel) that
+    moves the same number of HBM bytes as one headline call (half read, half
+    written), over rotated buffers, timed like the headline."""
+    n = nbytes // 8  # int32 elements per side
+    copies = max(2, -(-512 * 2 ** 20 // nbytes))
+    src = [torch.empty(n, dtype=torch.int32, device="cuda").random_() for _ in range(copies)]
+    dst = [torch.empty_like(src[0]) for _ in range(copies)]
+
+    def launch(i):
+        torch.neg(src[i % copies], out=dst[i % copies])
+
+    ms, _ = timed_graph(torch, stream, launch, steps, warmup)
+    del src, dst
+    torch.cuda.empty_cache()
+    return dict(bytes=8 * n, us_per_call=ms * 1e3, gbs=8 * n / (ms * 1e-3) / 1e9,
+                hbm_frac=8 * n / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+
+
 EXTRA_ROWS = {
     "batched_M32": lambda t, w, st, k, wu: bench_gemm(t, w, st, 32, 4096, 12800, 128, True, k, wu, 3),
     "prefill_M256": lambda t, w, st, k, wu: bench_gemm(t, w, st, 256, 12800, 4096, 128, True, k, wu, 4),
     "repack_K4096_N12800": lambda t, w, st, k, wu: bench_repack(t, w, st, 4096, 12800, k, wu),
     "decode_step": lambda t, w, st, k, wu: bench_decode(t, w, st, [1, 32], max(5, k // 20), 3),
+    "copy_context_27MB": lambda t, w, st, k, wu: bench_copy_context(
+        t, st, alg_bytes(1, 4096, 12800, 128, False), k, wu),
 }
 
 
