@@ -138,7 +138,8 @@ size_t w4a16_decode_workspace_bytes(int64_t M, const w4a16_linear *lin, int64_t 
  * x / (1 + exp(-x)).  Intermediates are stored as fp16.
  *
  *   lin        host array of 4*n_layers linears: qkv, o, gate_up, down per layer
- *              (shapes must chain as above, else INVALID_ARG).
+ *              (shapes must chain as above, else INVALID_ARG; H and I must be
+ *              multiples of 8 and at most 32768, else UNSUPPORTED).
  *   x_in       device fp16 [M, H]; x_out device fp16 [M, H] (may equal x_in).
  *   M          1..8192 rows.
  *   workspace  device scratch of at least w4a16_decode_workspace_bytes(...)

@@ -155,6 +155,11 @@ def test_decode_step_rejects(lib):
     assert call(arr, 1, A, O, 3, W, 100, None) == INVALID               # workspace too small
     assert call(ctypes.cast(_stack(bad=True), ctypes.c_void_p), 1, A, O, 3, W, 1 << 20, None) == INVALID
     assert call(arr, 1, A, O, 3, ctypes.c_void_p(A.value), 1 << 20, None) == INVALID  # overlap
+    # glue rows live in registers: H and I at most 32768
+    wide = ctypes.cast(_stack(I=32800), ctypes.c_void_p)
+    assert lib.w4a16_decode_workspace_bytes(3, wide, 1) == 0
+    assert call(wide, 1, A, O, 3, W, 1 << 30, None) == UNSUPPORTED
+    assert "32768" in lib.w4a16_last_error().decode()
 
 
 def test_python_binding_rejects_host_tensors_and_bad_dtypes(lib):

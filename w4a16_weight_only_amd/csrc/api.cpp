@@ -282,6 +282,8 @@ int check_stack(const w4a16_linear *lin, int64_t n_layers, DecodeShape *sh) {
                 return fail(W4A16_ERR_UNSUPPORTED, "stack tensors must be 16-byte aligned");
             d.maxN = std::max(d.maxN, L[j].N);
         }
+        if (H % 8 != 0 || I % 8 != 0 || H > kGlueMaxWidth || I > kGlueMaxWidth)
+            return fail(W4A16_ERR_UNSUPPORTED, "decode step needs H and I multiples of 8 and at most 32768");
         d.I = std::max(d.I, I);
         d.NQ = std::max(d.NQ, L[0].N);
     }

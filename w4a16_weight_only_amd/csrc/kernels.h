@@ -48,7 +48,10 @@ hipError_t launch_gemv(const GemmArgs &args, const GemmPlan &plan, hipStream_t s
 hipError_t launch_mfma(const GemmArgs &args, const GemmPlan &plan, hipStream_t stream);
 hipError_t launch_repack(const int32_t *src, int32_t *dst, int64_t K, int64_t N, hipStream_t stream);
 
-// Decode-step glue (fp16 in/out, fp32 math).
+// Decode-step glue (fp16 in/out, fp32 math).  Widths (and row strides) must
+// be multiples of 8 and at most kGlueMaxWidth; the launchers return
+// hipErrorInvalidValue otherwise.
+constexpr int64_t kGlueMaxWidth = 32768;
 // y[m][0..width) = rn(x[m][0..width)) with x row stride ldx.
 hipError_t launch_rownorm(const uint16_t *x, int64_t M, int64_t ldx, int64_t width, uint16_t *y,
                           hipStream_t stream);
