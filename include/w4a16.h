@@ -99,8 +99,10 @@ int w4a16_repack(const int32_t *src_nk8, int32_t *dst_kn8, int64_t K, int64_t N,
  *
  * Errors: INVALID_ARG for NULL b_packed/scales (or a/out with M > 0), M < 0, K/N/G <= 0,
  * N % 8 != 0, K % G != 0, zp_bias outside [0, 15] without qzeros, or `out`
- * overlapping an input; UNSUPPORTED for G % 32 != 0 or a pointer that is not
- * 16-byte aligned; WORKSPACE if scratch allocation fails; HIP on launch failure.
+ * overlapping an input; UNSUPPORTED for G % 32 != 0, a pointer that is not
+ * 16-byte aligned, or sizes past the kernels' 32-bit ranges (M > 2^20,
+ * K or N > 2^26, M*K or M*N >= 2^31, K*N/8 >= 2^30); WORKSPACE if scratch
+ * allocation fails; HIP on launch failure.
  */
 int w4a16_gemm(const uint16_t *a, const int32_t *b_packed, const uint16_t *scales,
                const int32_t *qzeros, int64_t M, int64_t K, int64_t N, int64_t G,

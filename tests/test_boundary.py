@@ -75,6 +75,7 @@ def gemm(lib, a=A, b=B, s=S, z=None, M=1, K=256, N=256, G=64, zp=8, o=O):
     (dict(o=ctypes.c_void_p(S.value + 16)), INVALID),      # out overlaps scales
     (dict(z=Z, o=ctypes.c_void_p(Z.value)), INVALID),      # out overlaps qzeros
     (dict(M=1 << 21), UNSUPPORTED),
+    (dict(K=1 << 16, N=1 << 17, G=64), UNSUPPORTED),        # packed weights >= 4 GiB
 ])
 def test_gemm_rejects(lib, kw, status):
     assert gemm(lib, **kw) == status

@@ -56,6 +56,7 @@ struct Tune {
     int64_t mfma_target_waves = 0;  // 0: 1024 for 128-row wave tiles, else 2048
     int64_t mfma_splits = 0;        // force the MFMA split count
     int64_t mfma_wide = 0;          // 1: 128x256 workgroup tiles for M > 64
+    int64_t mfma_cfg = 0;           // force (mt, waves, kwaves): 1..5 = (1,2,4) (2,2,4) (4,2,2) (8,1,4) (8,2,2)
     int64_t max_partial_bytes = 64ll << 20;
 };
 
@@ -81,6 +82,7 @@ const Tune &tune() {
                 else if (k == "mfma_target_waves") v.mfma_target_waves = val;
                 else if (k == "mfma_wide") v.mfma_wide = val;
                 else if (k == "mfma_splits") v.mfma_splits = val;
+                else if (k == "mfma_cfg") v.mfma_cfg = val;
                 else if (k == "max_partial_bytes") v.max_partial_bytes = val;
             }
             pos = end + 1;
@@ -97,8 +99,9 @@ int validate_sizes(int64_t M, int64_t K, int64_t N, int64_t G) {
     if (N % 8 != 0) return fail(W4A16_ERR_INVALID_ARG, "N must be a multiple of 8");
     if (K % G != 0) return fail(W4A16_ERR_INVALID_ARG, "K must be a multiple of G");
     if (G % 32 != 0) return fail(W4A16_ERR_UNSUPPORTED, "G must be a multiple of 32");
-    if (M > (1ll << 20) || K > (1ll << 26) || N > (1ll << 26) || M * N > (1ll << 31) ||
-        M * K > (1ll << 31) || K * (N / 8) > (1ll << 31))
+    // Every tensor must fit a buffer resource (byte extent < 2^32).
+    if (M > (1ll << 20) || K > (1ll << 26) || N > (1ll << 26) || M * N >= (1ll << 31) ||
+        M * K >= (1ll << 31) || K * (N / 8) >= (1ll << 30))
         return fail(W4A16_ERR_UNSUPPORTED, "problem too large for 32-bit kernel indexing");
     return W4A16_OK;
 }
@@ -143,19 +146,27 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G) {
         p.path = kPathMfma;
         if (M <= 16) { p.mt = 1; p.waves = 2; p.kwaves = 4; }
         else if (M <= 32) { p.mt = 2; p.waves = 2; p.kwaves = 4; }
-        else if (M <= 64) { p.mt = 4; p.waves = 2; p.kwaves = 2; }
-        else if (t.mfma_wide) { p.mt = 8; p.waves = 2; p.kwaves = 2; }
-        else { p.mt = 8; p.waves = 1; p.kwaves = 4; }
+        else if (M <= 64 || !t.mfma_wide) { p.mt = 4; p.waves = 2; p.kwaves = 2; }
+        else { p.mt = 8; p.waves = 2; p.kwaves = 2; }
+        static const int kCfg[5][3] = {{1, 2, 4}, {2, 2, 4}, {4, 2, 2}, {8, 1, 4}, {8, 2, 2}};
+        if (t.mfma_cfg >= 1 && t.mfma_cfg <= 5) {
+            p.mt = kCfg[t.mfma_cfg - 1][0];
+            p.waves = kCfg[t.mfma_cfg - 1][1];
+            p.kwaves = kCfg[t.mfma_cfg - 1][2];
+        }
         p.tiles_n = cdiv(N8, 16 * p.waves);
         p.tiles_m = cdiv(M, 16 * p.mt);
         const int64_t nsteps = K / 32;
         const int64_t wg_waves = (int64_t)p.waves * p.kwaves;
         const int64_t tiles = p.tiles_n * p.tiles_m;
         const int64_t target = t.mfma_target_waves > 0 ? t.mfma_target_waves : (p.mt >= 8 ? 1024 : 2048);
-        int64_t splits = t.mfma_splits > 0 ? t.mfma_splits : cdiv(target, tiles * wg_waves);
+        // Round down: these workgroups hold one per CU, and a grid past one
+        // round of the chip would run its last workgroups as a second wave.
+        int64_t splits = t.mfma_splits > 0 ? t.mfma_splits : target / (tiles * wg_waves);
         // at least two 32-row steps per K-wave, bounded partials
         splits = std::min<int64_t>(splits, std::max<int64_t>(1, nsteps / (2 * p.kwaves)));
         splits = std::min<int64_t>(splits, std::max<int64_t>(1, t.max_partial_bytes / std::max<int64_t>(1, M * N * 4)));
+        splits = std::min<int64_t>(splits, mfma_max_splits(p.mt, p.waves, p.kwaves));
         splits = std::max<int64_t>(1, splits);
         p.split_len = cdiv(nsteps, splits);
         p.splits = (int)cdiv(nsteps, p.split_len);
@@ -163,7 +174,7 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G) {
     p.grid = p.tiles_n * p.tiles_m * p.splits;
     p.grid = cdiv(p.grid, 8) * 8;  // XCD-aware index mapping needs a multiple of 8
     p.partial_floats = p.splits > 1 ? (size_t)(p.splits * M * N) : 0;
-    p.counters = (p.splits > 1 && p.path == kPathGemv) ? (size_t)(p.tiles_n * p.tiles_m) : 0;
+    p.counters = p.splits > 1 ? (size_t)(p.tiles_n * p.tiles_m) : 0;
     return p;
 }
 

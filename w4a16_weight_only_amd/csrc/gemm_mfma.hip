@@ -14,23 +14,81 @@
 // the epilogue stores 16 contiguous bytes per row.  Dequantisation is
 // (q - z) exact in fp16 (device.h), times the group scale rounded to fp16.
 //
-// Work split.  A wave computes (16*MT rows) x (128 columns) over a share of
-// the K range.  A workgroup has NWN waves side by side along N and NWK waves
-// dividing its K range (contiguous blocks of 32-row steps, loads issued two
-// steps ahead of use); the NWK partial tiles are
-// summed through LDS in fixed order.  When the grid also splits K across
-// workgroups, each split writes fp32 partials and a second, fully parallel
-// kernel sums the splits in split order (deterministic; the kernel boundary
-// orders the two).  Workgroup indices are remapped so that neighbouring
-// column tiles run on the same XCD and share its L2.
+// Pipeline.  A wave computes (16*MT rows) x (128 columns) over a contiguous
+// block of 32-row K-steps.  The loop is unrolled by four over a ring of four
+// packed-word slots and two A-operand slots, so nothing is copied between
+// iterations: the MFMAs of step s run while the VALU dequantises step s+1
+// into the B operand registers the MFMAs have just read (explicit scheduling
+// regions keep that order), A for step s+1 and B for step s+4 are in flight.
+// Loads are issued in the order they are consumed, so waiting for the data of
+// one step never waits for a later prefetch.  All loads are buffer loads whose
+// per-row/per-step offset is an SGPR: no vector address arithmetic.
+//
+// Reduction.  A workgroup has NWN waves side by side along N and NWK waves
+// dividing its K range; the NWK partial tiles are summed through LDS in fixed
+// order.  When the grid also splits K across workgroups, every split writes
+// its fp32 tile with device-coherent stores and bumps the tile's arrival
+// counter; the workgroup that arrives last reads all splits back and sums
+// them in split order (deterministic), writes fp16 and resets the counter.
 #include "device.h"
 #include "kernels.h"
+
+#include <type_traits>
 
 namespace w4a16 {
 namespace {
 
-// Dequantise the 8 B operands (one per nibble position) from the 8 words of
-// rows k0+8*kq .. +7 of one packed column-of-words.
+// The last workgroup of a split-K tile keeps at most kSplitLoads 16-byte
+// partial loads in flight per thread (a chunk of units x every split).
+constexpr int kSplitLoads = 32;
+
+template <int MT, int NWN, int NWK>
+struct Cfg {
+    static constexpr int kThreads = 64 * NWN * NWK;
+    static constexpr int kTileRows = 16 * MT;
+    static constexpr int kTileCols = 128 * NWN;
+    // f32x4 units of the workgroup tile per thread in the split-K reduction.
+    static constexpr int kUnits = kTileRows * (kTileCols / 4) / kThreads;
+    static constexpr int kMaxSplits = MT >= 4 ? 4 : 8;
+    static constexpr int kChunk = kSplitLoads / kMaxSplits < kUnits ? kSplitLoads / kMaxSplits : kUnits;
+    static_assert(kUnits >= 1 && kTileRows * (kTileCols / 4) % kThreads == 0, "whole units per thread");
+    static_assert(kChunk >= 1 && kUnits % kChunk == 0, "whole chunks");
+};
+
+// Scale pairs (s_t, s_t) for the 8 columns of one word from their fp16 bits.
+__device__ __forceinline__ void scale_pairs(const u32x4 &sv, f16x2 (&sp)[8]) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        sp[2 * x] = as_f16x2(__builtin_amdgcn_perm(sv[x], sv[x], 0x01000100u));
+        sp[2 * x + 1] = as_f16x2(__builtin_amdgcn_perm(sv[x], sv[x], 0x03020302u));
+    }
+}
+
+template <bool ASYM>
+__device__ __forceinline__ void zero_pairs(uint32_t zw, uint32_t zp, const NibbleConsts &nk, f16x2 (&zc)[8]) {
+    if constexpr (ASYM) {
+        zc[0] = zero_pair_from_word<0>(zw, nk);
+        zc[1] = zero_pair_from_word<1>(zw, nk);
+        zc[2] = zero_pair_from_word<2>(zw, nk);
+        zc[3] = zero_pair_from_word<3>(zw, nk);
+        zc[4] = zero_pair_from_word<4>(zw, nk);
+        zc[5] = zero_pair_from_word<5>(zw, nk);
+        zc[6] = zero_pair_from_word<6>(zw, nk);
+        zc[7] = zero_pair_from_word<7>(zw, nk);
+    } else {
+        zc[0] = zero_pair_const<0>(zp);
+        zc[1] = zero_pair_const<1>(zp);
+        zc[2] = zero_pair_const<2>(zp);
+        zc[3] = zero_pair_const<3>(zp);
+        zc[4] = zero_pair_const<4>(zp);
+        zc[5] = zero_pair_const<5>(zp);
+        zc[6] = zero_pair_const<6>(zp);
+        zc[7] = zero_pair_const<7>(zp);
+    }
+}
+
+// Dequantise byte position B (nibbles 2B, 2B+1) of the 8 words of rows
+// k0+8*kq .. +7 of one packed column-of-words into B operands 2B and 2B+1.
 template <int B>
 __device__ __forceinline__ void dequant_byte(const uint32_t (&wd)[8], const f16x2 (&zc)[8],
                                              const f16x2 (&sp)[8], const NibbleConsts &nk,
@@ -47,21 +105,25 @@ __device__ __forceinline__ void dequant_byte(const uint32_t (&wd)[8], const f16x
     }
 }
 
+
 template <int MT, int NWN, int NWK, bool ASYM>
 __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
     const uint16_t *__restrict__ a, const uint32_t *__restrict__ b,
     const uint16_t *__restrict__ scales, const uint32_t *__restrict__ qzeros, int M, int K, int N,
     int G, uint32_t zp, int tiles_n, int tiles_m, int split_len, int splits,
-    uint16_t *__restrict__ out, float *__restrict__ partials) {
+    uint16_t *__restrict__ out, float *__restrict__ partials, uint32_t *__restrict__ counters) {
+    using C = Cfg<MT, NWN, NWK>;
     // Logical workgroup: XCD-contiguous runs (grid is a multiple of 8).
     const int logical = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-    if (logical >= tiles_n * tiles_m * splits) return;
+    if (logical >= tiles_n * tiles_m * splits) return;  // whole workgroup
     const int tile_n = logical % tiles_n;
     const int tile_m = (logical / tiles_n) % tiles_m;
     const int split = logical / (tiles_n * tiles_m);
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // Wave-uniform (the compiler cannot prove threadIdx.x >> 6 is): keeps the
+    // per-step buffer offsets in SGPRs.
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wn = wave % NWN;
     const int wk = wave / NWN;
     const int j16 = lane & 15;  // A row within the tile / B column within the tile
@@ -70,190 +132,285 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
     const int word = (tile_n * NWN + wn) * 16 + j16;
     const bool col_ok = word < N8;
     const int wordc = col_ok ? word : N8 - 1;  // clamped: loads stay in bounds
-    const int m0 = tile_m * 16 * MT;
+    const int m0 = tile_m * C::kTileRows;
     const int nsteps = K / 32;
     const int s_begin = split * split_len;
     const int s_end = min(s_begin + split_len, nsteps);
     const NibbleConsts nk = nibble_consts();
 
+    const uint32_t row_bytes = (uint32_t)N8 * 4u;
+    const __amdgpu_buffer_rsrc_t brs = buffer_rsrc(b, (uint32_t)((uint64_t)K * N8 * 4));
+    const __amdgpu_buffer_rsrc_t ars = buffer_rsrc(a, (uint32_t)((uint64_t)M * K * 2));
+    const __amdgpu_buffer_rsrc_t srs = buffer_rsrc(scales, (uint32_t)((uint64_t)(K / G) * N * 2));
+    const __amdgpu_buffer_rsrc_t zrs = buffer_rsrc(qzeros, ASYM ? (uint32_t)((uint64_t)(K / G) * row_bytes) : 0u);
+    const uint32_t b_voff = ((uint32_t)(8 * kq) * (uint32_t)N8 + (uint32_t)wordc) * 4u;
+    const uint32_t s_voff = (uint32_t)wordc * 16u;
+    const uint32_t z_voff = (uint32_t)wordc * 4u;
+    // A row tile mt of this wave starts 16*mt rows below row tile 0: a
+    // wave-uniform byte offset, so one lane offset serves every tile.  Rows
+    // past M read row M-1 instead (valid memory; results never stored), which
+    // only happens in a workgroup's last row tiles when 16*MT does not divide M.
+    const uint32_t a_row_bytes = (uint32_t)K * 2u;
+    const bool a_full = m0 + C::kTileRows <= M;
+    const uint32_t a_voff0 = ((uint32_t)(m0 + j16) * (uint32_t)K + 8u * kq) * 2u;
+    uint32_t a_voff_tail[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+        a_voff_tail[mt] = ((uint32_t)min(m0 + 16 * mt + j16, M - 1) * (uint32_t)K + 8u * kq) * 2u;
+
+    // Accumulators start from distinct (opaque) zeros: with one shared zero
+    // constant the register allocator gave MFMA results and their srcC
+    // different registers and copied the accumulators every step.
     f32x4 acc[MT][8];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int t = 0; t < 8; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < 8; ++t) {
+            f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            asm volatile("" : "+v"(z));
+            acc[mt][t] = z;
+        }
 
     // This K-wave's contiguous block of 32-row steps (groups change rarely).
     const int per_wave = (s_end - s_begin + NWK - 1) / NWK;
     const int w_begin = min(s_begin + wk * per_wave, s_end);
-    const int w_end = min(w_begin + per_wave, s_end);
+    const int n = min(w_begin + per_wave, s_end) - w_begin;
+    auto stc = [&](int i) { return w_begin + min(i, n - 1); };  // clamped step index
 
-    // Software pipeline: weight words two steps ahead, activations and the
-    // group's scale/zero words one step ahead, so the loop never waits on a
-    // load issued in the same iteration.
-    auto load_w = [&](int st, uint32_t (&wd)[8]) {
-        const uint32_t *bp = b + (size_t)(st * 32 + 8 * kq) * N8 + wordc;
+    auto load_b = [&](int st, uint32_t (&w)[8]) {
+        const uint32_t base = (uint32_t)st * 32u * row_bytes;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) wd[r] = bp[(size_t)r * N8];
+        for (int r = 0; r < 8; ++r) w[r] = buffer_load_x1(brs, b_voff, base + (uint32_t)r * row_bytes);
     };
     auto load_a = [&](int st, f16x8 (&av)[MT]) {
+        if (a_full) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int row = m0 + 16 * mt + j16;
-            av[mt] = row < M ? *reinterpret_cast<const f16x8 *>(a + (size_t)row * K + st * 32 + 8 * kq)
-                             : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            for (int mt = 0; mt < MT; ++mt)
+                av[mt] = __builtin_bit_cast(
+                    f16x8, buffer_load_x4(ars, a_voff0, (uint32_t)st * 64u + (uint32_t)(16 * mt) * a_row_bytes));
+        } else {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                av[mt] = __builtin_bit_cast(f16x8, buffer_load_x4(ars, a_voff_tail[mt], (uint32_t)st * 64u));
         }
     };
     auto load_sz = [&](int st, u32x4 &sv, uint32_t &zw) {
-        const int g = st * 32 / G;
-        sv = *reinterpret_cast<const u32x4 *>(scales + (size_t)g * N + wordc * 8);
-        zw = ASYM ? qzeros[(size_t)g * N8 + wordc] : 0u;
+        const uint32_t g = (uint32_t)(st * 32 / G);
+        sv = buffer_load_x4(srs, s_voff, g * (uint32_t)N * 2u);
+        if constexpr (ASYM) zw = buffer_load_x1(zrs, z_voff, g * row_bytes);
+    };
+    // MFMAs for B operand pair (T, T+1) of one step, every row tile.
+    auto mfma_pair = [&](const f16x8 (&av)[MT], const f16x8 (&bop)[8], auto tc) {
+        constexpr int T = decltype(tc)::value;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            acc[mt][T] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[mt], bop[T], acc[mt][T], 0, 0, 0);
+            acc[mt][T + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[mt], bop[T + 1], acc[mt][T + 1], 0, 0, 0);
+        }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I2 = std::integral_constant<int, 2>;
+    using I4 = std::integral_constant<int, 4>;
+    using I6 = std::integral_constant<int, 6>;
+
+    // Ring of four packed-word / scale / zero slots (B data for steps s..s+3)
+    // and two A-operand slots; one set of B operands `bop`.
+    // B ring depth (steps of B prefetch): 4, or 2 where 128 accumulator
+    // registers per wave leave no room for more.
+    constexpr int kRing = MT >= 8 ? 2 : 4;
+    uint32_t w[kRing][8];
+    u32x4 sv[kRing];
+    uint32_t zw[kRing] = {};
+    f16x8 av[2][MT], bop[8];
+    f16x2 sp[8], zc[8];
+
+    // One K-step s held in ring slot U (A slot U & 1).  Four scheduling
+    // regions, each issuing the MFMAs of one B operand pair of step s next to
+    // the VALU work that rewrites the pair the previous region consumed:
+    //   1: MFMA pair 0,1 | dequantise pair 6,7 of step s; scale/zero of s+1
+    //   2: MFMA pair 2,3 | dequantise pair 0,1 of step s+1
+    //   3: MFMA pair 4,5 | dequantise pair 2,3 of step s+1
+    //   4: MFMA pair 6,7 | dequantise pair 4,5 of step s+1
+    // A for s+1 is requested at the top, B/scale/zero for s+4 after region 1
+    // frees slot U.  Steps past the block clamp their loads (data unused).
+    auto step = [&](int s, auto uc) {
+        constexpr int U = decltype(uc)::value;
+        constexpr int AC = U & 1, AN = AC ^ 1, WN = (U + 1) % kRing;
+        load_a(stc(s + 1), av[AN]);
+        f16x2 spn[8], zcn[8];
+        mfma_pair(av[AC], bop, I0{});
+        dequant_byte<3>(w[U], zc, sp, nk, bop);
+        scale_pairs(sv[WN], spn);
+        zero_pairs<ASYM>(zw[WN], zp, nk, zcn);
+        __builtin_amdgcn_sched_barrier(0);
+        load_b(stc(s + kRing), w[U]);
+        load_sz(stc(s + kRing), sv[U], zw[U]);
+        mfma_pair(av[AC], bop, I2{});
+        dequant_byte<0>(w[WN], zcn, spn, nk, bop);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_pair(av[AC], bop, I4{});
+        dequant_byte<1>(w[WN], zcn, spn, nk, bop);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_pair(av[AC], bop, I6{});
+        dequant_byte<2>(w[WN], zcn, spn, nk, bop);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+            sp[x] = spn[x];
+            zc[x] = zcn[x];
+        }
     };
 
-    uint32_t w0[8], w1[8];
-    f16x8 a0[MT];
-    u32x4 sv0;
-    uint32_t zw0;
-    if (w_begin < w_end) {
-        load_w(w_begin, w0);
-        load_a(w_begin, a0);
-        load_sz(w_begin, sv0, zw0);
-    }
-    if (w_begin + 1 < w_end) load_w(w_begin + 1, w1);
-
-    f16x2 sp[8], zc[8];
-    int gcur = -1;
-    for (int st = w_begin; st < w_end; ++st) {
-        // prefetch
-        uint32_t w2[8];
-        f16x8 a1[MT];
-        u32x4 sv1;
-        uint32_t zw1;
-        const bool more1 = st + 1 < w_end, more2 = st + 2 < w_end;
-        if (more2) load_w(st + 2, w2);
-        if (more1) {
-            load_a(st + 1, a1);
-            load_sz(st + 1, sv1, zw1);
-        }
-
-        const int g = st * 32 / G;
-        if (g != gcur) {
-            gcur = g;
+    if (n > 0) {
+        load_b(stc(0), w[0]);
+        load_sz(stc(0), sv[0], zw[0]);
+        load_a(stc(0), av[0]);
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const uint32_t lo = sv0[x] & 0xffffu, hi = sv0[x] >> 16;
-                sp[2 * x] = as_f16x2(lo | (lo << 16));
-                sp[2 * x + 1] = as_f16x2(hi | (hi << 16));
-            }
-            if (ASYM) {
-                zc[0] = zero_pair_from_word<0>(zw0, nk);
-                zc[1] = zero_pair_from_word<1>(zw0, nk);
-                zc[2] = zero_pair_from_word<2>(zw0, nk);
-                zc[3] = zero_pair_from_word<3>(zw0, nk);
-                zc[4] = zero_pair_from_word<4>(zw0, nk);
-                zc[5] = zero_pair_from_word<5>(zw0, nk);
-                zc[6] = zero_pair_from_word<6>(zw0, nk);
-                zc[7] = zero_pair_from_word<7>(zw0, nk);
-            } else {
-                zc[0] = zero_pair_const<0>(zp);
-                zc[1] = zero_pair_const<1>(zp);
-                zc[2] = zero_pair_const<2>(zp);
-                zc[3] = zero_pair_const<3>(zp);
-                zc[4] = zero_pair_const<4>(zp);
-                zc[5] = zero_pair_const<5>(zp);
-                zc[6] = zero_pair_const<6>(zp);
-                zc[7] = zero_pair_const<7>(zp);
+        for (int r = 1; r < kRing; ++r) {
+            load_b(stc(r), w[r]);
+            load_sz(stc(r), sv[r], zw[r]);
+        }
+        scale_pairs(sv[0], sp);
+        zero_pairs<ASYM>(zw[0], zp, nk, zc);
+        dequant_byte<0>(w[0], zc, sp, nk, bop);
+        dequant_byte<1>(w[0], zc, sp, nk, bop);
+        dequant_byte<2>(w[0], zc, sp, nk, bop);
+        int i = 0;
+        for (; i + kRing <= n; i += kRing) {
+            step(i, I0{});
+            step(i + 1, std::integral_constant<int, 1>{});
+            if constexpr (kRing == 4) {
+                step(i + 2, I2{});
+                step(i + 3, std::integral_constant<int, 3>{});
             }
         }
-
-        f16x8 bop[8];
-        dequant_byte<0>(w0, zc, sp, nk, bop);
-        dequant_byte<1>(w0, zc, sp, nk, bop);
-        dequant_byte<2>(w0, zc, sp, nk, bop);
-        dequant_byte<3>(w0, zc, sp, nk, bop);
-
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-                acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0[mt], bop[t], acc[mt][t], 0, 0, 0);
-
-        // rotate the pipeline
-#pragma unroll
-        for (int r = 0; r < 8; ++r) { w0[r] = w1[r]; w1[r] = w2[r]; }
-        if (more1) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) a0[mt] = a1[mt];
-            sv0 = sv1;
-            zw0 = zw1;
+        if (i < n) step(i, I0{});
+        if constexpr (kRing == 4) {
+            if (i + 1 < n) step(i + 1, std::integral_constant<int, 1>{});
+            if (i + 2 < n) step(i + 2, I2{});
         }
     }
 
     // Sum the NWK partial tiles in order wk = 0, 1, ... through LDS, one
-    // K-wave at a time (each round moves MT * 8 KB per N-wave).
+    // K-wave at a time (each round moves MT * 8 KB per N-wave).  Every wave
+    // stays to the end so that the workgroup barriers below see all of them.
+    // The adds go one row tile (8 vectors) at a time, with scheduling
+    // barriers, so that the LDS reads are not all hoisted into registers.
     if constexpr (NWK > 1) {
         __shared__ f32x4 red[NWN][MT * 8][64];
 #pragma unroll
         for (int r = 1; r < NWK; ++r) {
             if (wk == r) {
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
+                for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
                     for (int t = 0; t < 8; ++t) red[wn][mt * 8 + t][lane] = acc[mt][t];
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
             __syncthreads();
             if (wk == 0) {
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
+                for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
                     for (int t = 0; t < 8; ++t) acc[mt][t] += red[wn][mt * 8 + t][lane];
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
             __syncthreads();
         }
-        if (wk != 0) return;
     }
-    if (!col_ok) return;
+    const bool owner = wk == 0 && col_ok;
 
     // acc[mt][t][v] = C[m0 + 16*mt + 4*kq + v][8*word + t].
+    if (splits == 1) {
+        if (!owner) return;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int row = m0 + 16 * mt + 4 * kq + v;
-            if (row >= M) continue;
-            if (splits == 1) {
+            for (int v = 0; v < 4; ++v) {
+                const int row = m0 + 16 * mt + 4 * kq + v;
+                if (row >= M) continue;
                 f16x8 o;
 #pragma unroll
                 for (int t = 0; t < 8; ++t) o[t] = (f16)acc[mt][t][v];
                 *reinterpret_cast<f16x8 *>(out + (size_t)row * N + word * 8) = o;
-            } else {
-                f32x4 *dst = reinterpret_cast<f32x4 *>(partials + ((size_t)split * M + row) * N + word * 8);
-                dst[0] = f32x4{acc[mt][0][v], acc[mt][1][v], acc[mt][2][v], acc[mt][3][v]};
-                dst[1] = f32x4{acc[mt][4][v], acc[mt][5][v], acc[mt][6][v], acc[mt][7][v]};
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
-}
-
-// out[m][8c .. 8c+7] = fp16(sum over s of partials[s][m][8c .. 8c+7]), s in order.
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ partials, int splits,
-                                                            int M, int N, uint16_t *__restrict__ out) {
-    const int N8 = N >> 3;
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (int64_t)M * N8) return;
-    const int64_t row = idx / N8, c8 = idx % N8;
-    const size_t plane = (size_t)M * N;
-    const f32x4 *src = reinterpret_cast<const f32x4 *>(partials + (size_t)row * N + c8 * 8);
-    f32x4 s0 = src[0], s1 = src[1];
-    for (int s = 1; s < splits; ++s) {
-        const f32x4 *p = reinterpret_cast<const f32x4 *>(partials + s * plane + (size_t)row * N + c8 * 8);
-        s0 += p[0];
-        s1 += p[1];
+        return;
     }
-    const f16x8 o = {(f16)s0.x, (f16)s0.y, (f16)s0.z, (f16)s0.w, (f16)s1.x, (f16)s1.y, (f16)s1.z, (f16)s1.w};
-    *reinterpret_cast<f16x8 *>(out + (size_t)row * N + c8 * 8) = o;
+
+    // Split-K: this split's tile to partials[split] (device-coherent stores).
+    const __amdgpu_buffer_rsrc_t prs = buffer_rsrc(partials, (uint32_t)((uint64_t)splits * M * N * 4));
+    const uint32_t plane = (uint32_t)M * (uint32_t)N * 4u;
+    if (owner) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int row = m0 + 16 * mt + 4 * kq + v;
+                if (row >= M) continue;
+                const uint32_t off = ((uint32_t)row * (uint32_t)N + (uint32_t)word * 8u) * 4u;
+                buffer_store_f32x4_sc1(f32x4{acc[mt][0][v], acc[mt][1][v], acc[mt][2][v], acc[mt][3][v]}, prs,
+                                       off, (uint32_t)split * plane);
+                buffer_store_f32x4_sc1(f32x4{acc[mt][4][v], acc[mt][5][v], acc[mt][6][v], acc[mt][7][v]}, prs,
+                                       off + 16u, (uint32_t)split * plane);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    wait_vm_zero();
+    __syncthreads();
+    __shared__ uint32_t last;
+    const int tile = tile_m * tiles_n + tile_n;
+    if (threadIdx.x == 0) last = (arrive_agent(&counters[tile]) == (uint32_t)(splits - 1)) ? 1u : 0u;
+    __syncthreads();
+    if (!last) return;
+
+    // Last arrival: every thread sums kUnits 16-byte units of the tile over
+    // all splits, in split order; per chunk of units every split's load is
+    // issued before the first add.
+    constexpr int kRowUnits = C::kTileCols / 4;
+    const int col0 = tile_n * C::kTileCols;
+    typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int u0 = 0; u0 < C::kUnits; u0 += C::kChunk) {
+        f32x4 v[C::kChunk][C::kMaxSplits];
+#pragma unroll
+        for (int u = 0; u < C::kChunk; ++u) {
+            const int idx = threadIdx.x + (u0 + u) * C::kThreads;
+            const int row = m0 + idx / kRowUnits;
+            const int col = col0 + 4 * (idx % kRowUnits);
+            const bool ok = row < M && col < N;
+            const uint32_t off = ok ? ((uint32_t)row * (uint32_t)N + (uint32_t)col) * 4u : 0u;
+#pragma unroll
+            for (int sp = 0; sp < C::kMaxSplits; ++sp)
+                v[u][sp] = (ok && sp < splits) ? buffer_load_f32x4_sc1(prs, off, (uint32_t)sp * plane)
+                                               : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < C::kChunk; ++u) {
+            const int idx = threadIdx.x + (u0 + u) * C::kThreads;
+            const int row = m0 + idx / kRowUnits;
+            const int col = col0 + 4 * (idx % kRowUnits);
+            if (row >= M || col >= N) continue;
+            f32x4 s = v[u][0];
+#pragma unroll
+            for (int sp = 1; sp < C::kMaxSplits; ++sp) s += v[u][sp];
+            const u16x4 o = {f32_to_f16_bits(s.x), f32_to_f16_bits(s.y), f32_to_f16_bits(s.z),
+                             f32_to_f16_bits(s.w)};
+            *reinterpret_cast<u16x4 *>(out + (size_t)row * N + col) = o;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (threadIdx.x == 0) reset_counter_agent(&counters[tile]);
 }
 
 template <int MT, int NWN, int NWK>
 hipError_t launch_cfg(const GemmArgs &g, const GemmPlan &p, hipStream_t stream) {
+    if (p.splits > Cfg<MT, NWN, NWK>::kMaxSplits) return hipErrorInvalidValue;
+    if (p.splits > 1 && (!g.partials || !g.counters)) return hipErrorInvalidValue;
     dim3 grid((unsigned)p.grid, 1, 1);
     dim3 block(64 * NWN * NWK, 1, 1);
     const uint32_t *b = reinterpret_cast<const uint32_t *>(g.b);
@@ -261,20 +418,24 @@ hipError_t launch_cfg(const GemmArgs &g, const GemmPlan &p, hipStream_t stream) 
     if (g.qzeros)
         hipLaunchKernelGGL((mfma_kernel<MT, NWN, NWK, true>), grid, block, 0, stream, g.a, b, g.scales, qz,
                            (int)g.M, (int)g.K, (int)g.N, (int)g.G, (uint32_t)g.zp, (int)p.tiles_n,
-                           (int)p.tiles_m, (int)p.split_len, p.splits, g.out, g.partials);
+                           (int)p.tiles_m, (int)p.split_len, p.splits, g.out, g.partials, g.counters);
     else
         hipLaunchKernelGGL((mfma_kernel<MT, NWN, NWK, false>), grid, block, 0, stream, g.a, b, g.scales, qz,
                            (int)g.M, (int)g.K, (int)g.N, (int)g.G, (uint32_t)g.zp, (int)p.tiles_n,
-                           (int)p.tiles_m, (int)p.split_len, p.splits, g.out, g.partials);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.splits == 1) return e;
-    const int64_t n = g.M * (g.N / 8);
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                       g.partials, p.splits, (int)g.M, (int)g.N, g.out);
+                           (int)p.tiles_m, (int)p.split_len, p.splits, g.out, g.partials, g.counters);
     return hipGetLastError();
 }
 
 }  // namespace
+
+int mfma_max_splits(int mt, int waves, int kwaves) {
+    if (mt == 1 && waves == 2 && kwaves == 4) return Cfg<1, 2, 4>::kMaxSplits;
+    if (mt == 2 && waves == 2 && kwaves == 4) return Cfg<2, 2, 4>::kMaxSplits;
+    if (mt == 4 && waves == 2 && kwaves == 2) return Cfg<4, 2, 2>::kMaxSplits;
+    if (mt == 8 && waves == 1 && kwaves == 4) return Cfg<8, 1, 4>::kMaxSplits;
+    if (mt == 8 && waves == 2 && kwaves == 2) return Cfg<8, 2, 2>::kMaxSplits;
+    return 1;
+}
 
 hipError_t launch_mfma(const GemmArgs &g, const GemmPlan &p, hipStream_t stream) {
     // (MT, NWN, NWK) combinations the planner emits.

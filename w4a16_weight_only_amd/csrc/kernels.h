@@ -46,6 +46,9 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G);
 
 hipError_t launch_gemv(const GemmArgs &args, const GemmPlan &plan, hipStream_t stream);
 hipError_t launch_mfma(const GemmArgs &args, const GemmPlan &plan, hipStream_t stream);
+// Largest K-split count the MFMA kernel's in-kernel reduction takes for a
+// (mt, waves, kwaves) configuration.
+int mfma_max_splits(int mt, int waves, int kwaves);
 hipError_t launch_repack(const int32_t *src, int32_t *dst, int64_t K, int64_t N, hipStream_t stream);
 
 // Decode-step glue (fp16 in/out, fp32 math).  Widths (and row strides) must
