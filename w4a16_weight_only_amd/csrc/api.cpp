@@ -56,7 +56,7 @@ struct Tune {
     int64_t mfma_target_waves = 0;  // 0: 1024 for 128-row wave tiles, else 2048
     int64_t mfma_splits = 0;        // force the MFMA split count
     int64_t mfma_wide = 0;          // 1: 128x256 workgroup tiles for M > 64
-    int64_t mfma_cfg = 0;           // force (mt, waves, kwaves): 1..5 = (1,2,4) (2,2,4) (4,2,2) (8,1,4) (8,2,2)
+    int64_t mfma_cfg = 0;  // force (mt, waves, kwaves): 1..6 = (1,2,4) (2,2,4) (4,2,2) (8,1,4) (8,2,2) (2,1,8)
     int64_t max_partial_bytes = 64ll << 20;
 };
 
@@ -140,16 +140,19 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G) {
         p.tiles_m = 1;
     } else {
         // MFMA: wave tile (16*mt rows) x 128 columns; `waves` along N and
-        // `kwaves` along K per workgroup; K-splits across workgroups until
-        // the grid has about mfma_target_waves waves (their fp32 partials are
-        // summed by a second kernel).
+        // `kwaves` along K per workgroup (one workgroup per CU); K-splits
+        // across workgroups until the grid has about mfma_target_waves waves
+        // (the last workgroup of a tile sums the splits' fp32 partials).
+        // Measured on MI355X: at M = 32 the 128-column, 8-K-wave shape beats
+        // 256-column tiles on the 8B-class decode shapes (fewer splits, less
+        // partial traffic); for M > 32, 64-row wave tiles beat 128-row ones.
         p.path = kPathMfma;
         if (M <= 16) { p.mt = 1; p.waves = 2; p.kwaves = 4; }
-        else if (M <= 32) { p.mt = 2; p.waves = 2; p.kwaves = 4; }
+        else if (M <= 32) { p.mt = 2; p.waves = 1; p.kwaves = 8; }
         else if (M <= 64 || !t.mfma_wide) { p.mt = 4; p.waves = 2; p.kwaves = 2; }
         else { p.mt = 8; p.waves = 2; p.kwaves = 2; }
-        static const int kCfg[5][3] = {{1, 2, 4}, {2, 2, 4}, {4, 2, 2}, {8, 1, 4}, {8, 2, 2}};
-        if (t.mfma_cfg >= 1 && t.mfma_cfg <= 5) {
+        static const int kCfg[6][3] = {{1, 2, 4}, {2, 2, 4}, {4, 2, 2}, {8, 1, 4}, {8, 2, 2}, {2, 1, 8}};
+        if (t.mfma_cfg >= 1 && t.mfma_cfg <= 6) {
             p.mt = kCfg[t.mfma_cfg - 1][0];
             p.waves = kCfg[t.mfma_cfg - 1][1];
             p.kwaves = kCfg[t.mfma_cfg - 1][2];

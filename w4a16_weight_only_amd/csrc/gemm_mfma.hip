@@ -434,6 +434,7 @@ int mfma_max_splits(int mt, int waves, int kwaves) {
     if (mt == 4 && waves == 2 && kwaves == 2) return Cfg<4, 2, 2>::kMaxSplits;
     if (mt == 8 && waves == 1 && kwaves == 4) return Cfg<8, 1, 4>::kMaxSplits;
     if (mt == 8 && waves == 2 && kwaves == 2) return Cfg<8, 2, 2>::kMaxSplits;
+    if (mt == 2 && waves == 1 && kwaves == 8) return Cfg<2, 1, 8>::kMaxSplits;
     return 1;
 }
 
@@ -444,6 +445,7 @@ hipError_t launch_mfma(const GemmArgs &g, const GemmPlan &p, hipStream_t stream)
     if (p.mt == 4 && p.waves == 2 && p.kwaves == 2) return launch_cfg<4, 2, 2>(g, p, stream);
     if (p.mt == 8 && p.waves == 1 && p.kwaves == 4) return launch_cfg<8, 1, 4>(g, p, stream);
     if (p.mt == 8 && p.waves == 2 && p.kwaves == 2) return launch_cfg<8, 2, 2>(g, p, stream);
+    if (p.mt == 2 && p.waves == 1 && p.kwaves == 8) return launch_cfg<2, 1, 8>(g, p, stream);
     return hipErrorInvalidValue;
 }
 
