@@ -85,7 +85,9 @@ def small_cases():
     for M in (9, 15, 16, 17, 32, 33, 64, 65, 100, 128, 200, 256):  # MFMA path, ragged words/rows
         cases.append((M, 512, 520, 64, M % 2 == 1))
     cases += [(1, 256, 264, 64, True), (7, 384, 8, 128, False),  # N % 32 != 0 at small M
-              (40, 2048, 1024, 2048, True), (256, 1280, 512, 128, True)]
+              (40, 2048, 1024, 2048, True), (256, 1280, 512, 128, True),
+              (96, 96, 256, 32, True),     # large-M kernel: K-groups with no steps
+              (72, 160, 136, 32, False)]   # large-M kernel: ragged rows and columns
     return cases
 
 

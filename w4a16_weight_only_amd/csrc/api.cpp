@@ -53,10 +53,9 @@ struct Tune {
     int64_t gemv_waves = 8;            // waves per GEMV workgroup (4 or 8)
     int64_t gemv_splits = 0;           // force the GEMV K-split count
     int64_t gemv_fold = 0;             // 1: bias/zero removed per chunk (fewer VALU ops)
-    int64_t mfma_target_waves = 0;  // 0: 1024 for 128-row wave tiles, else 2048
+    int64_t mfma_target_waves = 2048;  // aim for about this many MFMA-path waves
     int64_t mfma_splits = 0;        // force the MFMA split count
-    int64_t mfma_wide = 0;          // 1: 128x256 workgroup tiles for M > 64
-    int64_t mfma_cfg = 0;  // force (mt, waves, kwaves): 1..6 = (1,2,4) (2,2,4) (4,2,2) (8,1,4) (8,2,2) (2,1,8)
+    int64_t mfma_cfg = 0;  // force (mt, waves, kwaves): 1..4 = (1,2,4) (2,2,4) (4,2,2) (2,1,8)
     int64_t max_partial_bytes = 64ll << 20;
 };
 
@@ -80,7 +79,6 @@ const Tune &tune() {
                 else if (k == "gemv_splits") v.gemv_splits = val;
                 else if (k == "gemv_fold") v.gemv_fold = val;
                 else if (k == "mfma_target_waves") v.mfma_target_waves = val;
-                else if (k == "mfma_wide") v.mfma_wide = val;
                 else if (k == "mfma_splits") v.mfma_splits = val;
                 else if (k == "mfma_cfg") v.mfma_cfg = val;
                 else if (k == "max_partial_bytes") v.max_partial_bytes = val;
@@ -149,10 +147,9 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G) {
         p.path = kPathMfma;
         if (M <= 16) { p.mt = 1; p.waves = 2; p.kwaves = 4; }
         else if (M <= 32) { p.mt = 2; p.waves = 1; p.kwaves = 8; }
-        else if (M <= 64 || !t.mfma_wide) { p.mt = 4; p.waves = 2; p.kwaves = 2; }
-        else { p.mt = 8; p.waves = 2; p.kwaves = 2; }
-        static const int kCfg[6][3] = {{1, 2, 4}, {2, 2, 4}, {4, 2, 2}, {8, 1, 4}, {8, 2, 2}, {2, 1, 8}};
-        if (t.mfma_cfg >= 1 && t.mfma_cfg <= 6) {
+        else { p.mt = 4; p.waves = 2; p.kwaves = 2; }
+        static const int kCfg[4][3] = {{1, 2, 4}, {2, 2, 4}, {4, 2, 2}, {2, 1, 8}};
+        if (t.mfma_cfg >= 1 && t.mfma_cfg <= 4) {
             p.mt = kCfg[t.mfma_cfg - 1][0];
             p.waves = kCfg[t.mfma_cfg - 1][1];
             p.kwaves = kCfg[t.mfma_cfg - 1][2];
@@ -162,7 +159,7 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G) {
         const int64_t nsteps = K / 32;
         const int64_t wg_waves = (int64_t)p.waves * p.kwaves;
         const int64_t tiles = p.tiles_n * p.tiles_m;
-        const int64_t target = t.mfma_target_waves > 0 ? t.mfma_target_waves : (p.mt >= 8 ? 1024 : 2048);
+        const int64_t target = t.mfma_target_waves > 0 ? t.mfma_target_waves : 2048;
         // Round down: these workgroups hold one per CU, and a grid past one
         // round of the chip would run its last workgroups as a second wave.
         int64_t splits = t.mfma_splits > 0 ? t.mfma_splits : target / (tiles * wg_waves);

@@ -49,11 +49,49 @@ struct Cfg {
     static constexpr int kTileCols = 128 * NWN;
     // f32x4 units of the workgroup tile per thread in the split-K reduction.
     static constexpr int kUnits = kTileRows * (kTileCols / 4) / kThreads;
-    static constexpr int kMaxSplits = MT >= 4 ? 4 : 8;
+    static constexpr int kMaxSplits = MT >= 4 ? 4 : 8;  // in-flight loads of the last workgroup
     static constexpr int kChunk = kSplitLoads / kMaxSplits < kUnits ? kSplitLoads / kMaxSplits : kUnits;
     static_assert(kUnits >= 1 && kTileRows * (kTileCols / 4) % kThreads == 0, "whole units per thread");
     static_assert(kChunk >= 1 && kUnits % kChunk == 0, "whole chunks");
 };
+
+// Values a region must produce where it stands: an empty asm that reads and
+// "rewrites" them keeps IR passes from sinking their computation into a
+// later region (emits no instruction).
+__device__ __forceinline__ void pin(f16x8 &a, f16x8 &b) { asm volatile("" : "+v"(a), "+v"(b)); }
+__device__ __forceinline__ void pin2(f16x2 &a, f16x2 &b, f16x2 &c, f16x2 &d) {
+    asm volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+
+// Scheduling pattern for one region: (one MFMA, then V VALU) NMFMA times.
+template <int NMFMA, int V>
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+    for (int i = 0; i < NMFMA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, V, 0);  // VALU
+    }
+}
+
+// Compile-time loop: f(integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+template <int A, int B>
+struct Gcd : Gcd<B, A % B> {};
+template <int A>
+struct Gcd<A, 0> : std::integral_constant<int, A> {};
+
+// Pipeline depths: steps of B (packed words, scales, zeros) and of A in
+// flight.  (A third A slot measured no faster at MT = 4.)
+template <int MT>
+struct RingW : std::integral_constant<int, 4> {};
+template <int MT>
+struct RingA : std::integral_constant<int, 2> {};
 
 // Scale pairs (s_t, s_t) for the 8 columns of one word from their fp16 bits.
 __device__ __forceinline__ void scale_pairs(const u32x4 &sv, f16x2 (&sp)[8]) {
@@ -175,7 +213,7 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
     const int per_wave = (s_end - s_begin + NWK - 1) / NWK;
     const int w_begin = min(s_begin + wk * per_wave, s_end);
     const int n = min(w_begin + per_wave, s_end) - w_begin;
-    auto stc = [&](int i) { return w_begin + min(i, n - 1); };  // clamped step index
+    auto stc = [&](int i) __attribute__((always_inline)) { return w_begin + min(i, n - 1); };  // clamped step index
 
     auto load_b = [&](int st, uint32_t (&w)[8]) {
         const uint32_t base = (uint32_t)st * 32u * row_bytes;
@@ -194,7 +232,7 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
                 av[mt] = __builtin_bit_cast(f16x8, buffer_load_x4(ars, a_voff_tail[mt], (uint32_t)st * 64u));
         }
     };
-    auto load_sz = [&](int st, u32x4 &sv, uint32_t &zw) {
+    auto load_sz = [&](int st, u32x4 &sv, uint32_t &zw) __attribute__((always_inline)) {
         const uint32_t g = (uint32_t)(st * 32 / G);
         sv = buffer_load_x4(srs, s_voff, g * (uint32_t)N * 2u);
         if constexpr (ASYM) zw = buffer_load_x1(zrs, z_voff, g * row_bytes);
@@ -217,11 +255,13 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
     // and two A-operand slots; one set of B operands `bop`.
     // B ring depth (steps of B prefetch): 4, or 2 where 128 accumulator
     // registers per wave leave no room for more.
-    constexpr int kRing = MT >= 8 ? 2 : 4;
+    constexpr int kRing = RingW<MT>::value;   // B / scale / zero slots
+    constexpr int kRingA = RingA<MT>::value;  // A slots
+    constexpr int kUnroll = kRing * kRingA / Gcd<kRing, kRingA>::value;
     uint32_t w[kRing][8];
     u32x4 sv[kRing];
     uint32_t zw[kRing] = {};
-    f16x8 av[2][MT], bop[8];
+    f16x8 av[kRingA][MT], bop[8];
     f16x2 sp[8], zc[8];
 
     // One K-step s held in ring slot U (A slot U & 1).  Four scheduling
@@ -233,26 +273,42 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
     //   4: MFMA pair 6,7 | dequantise pair 4,5 of step s+1
     // A for s+1 is requested at the top, B/scale/zero for s+4 after region 1
     // frees slot U.  Steps past the block clamp their loads (data unused).
-    auto step = [&](int s, auto uc) {
+    // Inside a region, alternate one MFMA with a share of the region's VALU
+    // work (28 conversion ops per operand pair; the first region also builds
+    // the next step's scale and zero pairs), so that the matrix core and the
+    // VALU stay busy together; left alone the scheduler clusters them.
+    constexpr int kValuPair = (28 + 2 * MT - 1) / (2 * MT);
+    constexpr int kValuFirst = (28 + 8 + (ASYM ? 16 : 0) + 2 * MT - 1) / (2 * MT);
+    auto step = [&](int s, auto uc) __attribute__((always_inline)) {
         constexpr int U = decltype(uc)::value;
-        constexpr int AC = U & 1, AN = AC ^ 1, WN = (U + 1) % kRing;
-        load_a(stc(s + 1), av[AN]);
+        constexpr int AC = U % kRingA, AN = (U + kRingA - 1) % kRingA, WC = U % kRing, WN = (U + 1) % kRing;
+        load_a(stc(s + kRingA - 1), av[AN]);
         f16x2 spn[8], zcn[8];
         mfma_pair(av[AC], bop, I0{});
-        dequant_byte<3>(w[U], zc, sp, nk, bop);
+        dequant_byte<3>(w[WC], zc, sp, nk, bop);
         scale_pairs(sv[WN], spn);
         zero_pairs<ASYM>(zw[WN], zp, nk, zcn);
+        interleave<2 * MT, kValuFirst>();
+        pin(bop[6], bop[7]);
+#pragma unroll
+        for (int x = 0; x < 8; x += 2) pin2(spn[x], spn[x + 1], zcn[x], zcn[x + 1]);
         __builtin_amdgcn_sched_barrier(0);
-        load_b(stc(s + kRing), w[U]);
-        load_sz(stc(s + kRing), sv[U], zw[U]);
+        load_b(stc(s + kRing), w[WC]);
+        load_sz(stc(s + kRing), sv[WC], zw[WC]);
         mfma_pair(av[AC], bop, I2{});
         dequant_byte<0>(w[WN], zcn, spn, nk, bop);
+        interleave<2 * MT, kValuPair>();
+        pin(bop[0], bop[1]);
         __builtin_amdgcn_sched_barrier(0);
         mfma_pair(av[AC], bop, I4{});
         dequant_byte<1>(w[WN], zcn, spn, nk, bop);
+        interleave<2 * MT, kValuPair>();
+        pin(bop[2], bop[3]);
         __builtin_amdgcn_sched_barrier(0);
         mfma_pair(av[AC], bop, I6{});
         dequant_byte<2>(w[WN], zcn, spn, nk, bop);
+        interleave<2 * MT, kValuPair>();
+        pin(bop[4], bop[5]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
@@ -262,9 +318,11 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
     };
 
     if (n > 0) {
+        // Issue order = consumption order: B(0), A(0 .. kRingA-2), B(1 ..).
         load_b(stc(0), w[0]);
         load_sz(stc(0), sv[0], zw[0]);
-        load_a(stc(0), av[0]);
+#pragma unroll
+        for (int r = 0; r + 1 < kRingA; ++r) load_a(stc(r), av[r]);
 #pragma unroll
         for (int r = 1; r < kRing; ++r) {
             load_b(stc(r), w[r]);
@@ -276,19 +334,11 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
         dequant_byte<1>(w[0], zc, sp, nk, bop);
         dequant_byte<2>(w[0], zc, sp, nk, bop);
         int i = 0;
-        for (; i + kRing <= n; i += kRing) {
-            step(i, I0{});
-            step(i + 1, std::integral_constant<int, 1>{});
-            if constexpr (kRing == 4) {
-                step(i + 2, I2{});
-                step(i + 3, std::integral_constant<int, 3>{});
-            }
-        }
-        if (i < n) step(i, I0{});
-        if constexpr (kRing == 4) {
-            if (i + 1 < n) step(i + 1, std::integral_constant<int, 1>{});
-            if (i + 2 < n) step(i + 2, I2{});
-        }
+        for (; i + kUnroll <= n; i += kUnroll)
+            static_for<0, kUnroll>([&](auto uc) __attribute__((always_inline)) { step(i + decltype(uc)::value, uc); });
+        static_for<0, kUnroll - 1>([&](auto uc) __attribute__((always_inline)) {
+            if (i + decltype(uc)::value < n) step(i + decltype(uc)::value, uc);
+        });
     }
 
     // Sum the NWK partial tiles in order wk = 0, 1, ... through LDS, one
@@ -426,14 +476,13 @@ hipError_t launch_cfg(const GemmArgs &g, const GemmPlan &p, hipStream_t stream) 
     return hipGetLastError();
 }
 
+
 }  // namespace
 
 int mfma_max_splits(int mt, int waves, int kwaves) {
     if (mt == 1 && waves == 2 && kwaves == 4) return Cfg<1, 2, 4>::kMaxSplits;
     if (mt == 2 && waves == 2 && kwaves == 4) return Cfg<2, 2, 4>::kMaxSplits;
     if (mt == 4 && waves == 2 && kwaves == 2) return Cfg<4, 2, 2>::kMaxSplits;
-    if (mt == 8 && waves == 1 && kwaves == 4) return Cfg<8, 1, 4>::kMaxSplits;
-    if (mt == 8 && waves == 2 && kwaves == 2) return Cfg<8, 2, 2>::kMaxSplits;
     if (mt == 2 && waves == 1 && kwaves == 8) return Cfg<2, 1, 8>::kMaxSplits;
     return 1;
 }
@@ -443,8 +492,6 @@ hipError_t launch_mfma(const GemmArgs &g, const GemmPlan &p, hipStream_t stream)
     if (p.mt == 1 && p.waves == 2 && p.kwaves == 4) return launch_cfg<1, 2, 4>(g, p, stream);
     if (p.mt == 2 && p.waves == 2 && p.kwaves == 4) return launch_cfg<2, 2, 4>(g, p, stream);
     if (p.mt == 4 && p.waves == 2 && p.kwaves == 2) return launch_cfg<4, 2, 2>(g, p, stream);
-    if (p.mt == 8 && p.waves == 1 && p.kwaves == 4) return launch_cfg<8, 1, 4>(g, p, stream);
-    if (p.mt == 8 && p.waves == 2 && p.kwaves == 2) return launch_cfg<8, 2, 2>(g, p, stream);
     if (p.mt == 2 && p.waves == 1 && p.kwaves == 8) return launch_cfg<2, 1, 8>(g, p, stream);
     return hipErrorInvalidValue;
 }
