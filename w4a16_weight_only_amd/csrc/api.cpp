@@ -143,33 +143,44 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G) {
         // (the last workgroup of a tile sums the splits' fp32 partials).
         // Measured on MI355X: at M = 32 the 128-column, 8-K-wave shape beats
         // 256-column tiles on the 8B-class decode shapes (fewer splits, less
-        // partial traffic); for M > 32, 64-row wave tiles beat 128-row ones.
+        // partial traffic).  Above M = 32, 64-row wave tiles with 2 or 4
+        // K-waves per workgroup: 4 (two waves per SIMD) wherever that needs
+        // fewer K-splits, since partial traffic is what the split count costs.
         p.path = kPathMfma;
-        if (M <= 16) { p.mt = 1; p.waves = 2; p.kwaves = 4; }
-        else if (M <= 32) { p.mt = 2; p.waves = 1; p.kwaves = 8; }
-        else { p.mt = 4; p.waves = 2; p.kwaves = 2; }
-        static const int kCfg[4][3] = {{1, 2, 4}, {2, 2, 4}, {4, 2, 2}, {2, 1, 8}};
-        if (t.mfma_cfg >= 1 && t.mfma_cfg <= 4) {
-            p.mt = kCfg[t.mfma_cfg - 1][0];
-            p.waves = kCfg[t.mfma_cfg - 1][1];
-            p.kwaves = kCfg[t.mfma_cfg - 1][2];
+        auto fill = [&](int mt, int waves, int kwaves) {
+            p.mt = mt;
+            p.waves = waves;
+            p.kwaves = kwaves;
+            p.tiles_n = cdiv(N8, 16 * p.waves);
+            p.tiles_m = cdiv(M, 16 * p.mt);
+            const int64_t nsteps = K / 32;
+            const int64_t wg_waves = (int64_t)p.waves * p.kwaves;
+            const int64_t tiles = p.tiles_n * p.tiles_m;
+            const int64_t target = t.mfma_target_waves > 0 ? t.mfma_target_waves : 2048;
+            // Round down: these workgroups hold one per CU, and a grid past one
+            // round of the chip would run its last workgroups as a second wave.
+            int64_t splits = t.mfma_splits > 0 ? t.mfma_splits : target / (tiles * wg_waves);
+            // at least two 32-row steps per K-wave, bounded partials
+            splits = std::min<int64_t>(splits, std::max<int64_t>(1, nsteps / (2 * p.kwaves)));
+            splits = std::min<int64_t>(splits, std::max<int64_t>(1, t.max_partial_bytes / std::max<int64_t>(1, M * N * 4)));
+            splits = std::min<int64_t>(splits, mfma_max_splits(p.mt, p.waves, p.kwaves));
+            splits = std::max<int64_t>(1, splits);
+            p.split_len = cdiv(nsteps, splits);
+            p.splits = (int)cdiv(nsteps, p.split_len);
+        };
+        static const int kCfg[5][3] = {{1, 2, 4}, {2, 2, 4}, {4, 2, 2}, {2, 1, 8}, {4, 2, 4}};
+        if (t.mfma_cfg >= 1 && t.mfma_cfg <= 5) {
+            fill(kCfg[t.mfma_cfg - 1][0], kCfg[t.mfma_cfg - 1][1], kCfg[t.mfma_cfg - 1][2]);
+        } else if (M <= 16) {
+            fill(1, 2, 4);
+        } else if (M <= 32) {
+            fill(2, 1, 8);
+        } else {
+            fill(4, 2, 4);
+            const int s4 = p.splits;
+            fill(4, 2, 2);
+            if (s4 < p.splits) fill(4, 2, 4);
         }
-        p.tiles_n = cdiv(N8, 16 * p.waves);
-        p.tiles_m = cdiv(M, 16 * p.mt);
-        const int64_t nsteps = K / 32;
-        const int64_t wg_waves = (int64_t)p.waves * p.kwaves;
-        const int64_t tiles = p.tiles_n * p.tiles_m;
-        const int64_t target = t.mfma_target_waves > 0 ? t.mfma_target_waves : 2048;
-        // Round down: these workgroups hold one per CU, and a grid past one
-        // round of the chip would run its last workgroups as a second wave.
-        int64_t splits = t.mfma_splits > 0 ? t.mfma_splits : target / (tiles * wg_waves);
-        // at least two 32-row steps per K-wave, bounded partials
-        splits = std::min<int64_t>(splits, std::max<int64_t>(1, nsteps / (2 * p.kwaves)));
-        splits = std::min<int64_t>(splits, std::max<int64_t>(1, t.max_partial_bytes / std::max<int64_t>(1, M * N * 4)));
-        splits = std::min<int64_t>(splits, mfma_max_splits(p.mt, p.waves, p.kwaves));
-        splits = std::max<int64_t>(1, splits);
-        p.split_len = cdiv(nsteps, splits);
-        p.splits = (int)cdiv(nsteps, p.split_len);
     }
     p.grid = p.tiles_n * p.tiles_m * p.splits;
     p.grid = cdiv(p.grid, 8) * 8;  // XCD-aware index mapping needs a multiple of 8

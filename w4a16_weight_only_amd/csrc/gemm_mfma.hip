@@ -88,8 +88,9 @@ struct Gcd<A, 0> : std::integral_constant<int, A> {};
 
 // Pipeline depths: steps of B (packed words, scales, zeros) and of A in
 // flight.  (A third A slot measured no faster at MT = 4.)
-template <int MT>
-struct RingW : std::integral_constant<int, 4> {};
+// Two B slots where eight waves of 64-row tiles share a CU (256 VGPRs each).
+template <int MT, int NWK>
+struct RingW : std::integral_constant<int, (MT == 4 && NWK == 4) ? 2 : 4> {};
 template <int MT>
 struct RingA : std::integral_constant<int, 2> {};
 
@@ -255,7 +256,7 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
     // and two A-operand slots; one set of B operands `bop`.
     // B ring depth (steps of B prefetch): 4, or 2 where 128 accumulator
     // registers per wave leave no room for more.
-    constexpr int kRing = RingW<MT>::value;   // B / scale / zero slots
+    constexpr int kRing = RingW<MT, NWK>::value;  // B / scale / zero slots
     constexpr int kRingA = RingA<MT>::value;  // A slots
     constexpr int kUnroll = kRing * kRingA / Gcd<kRing, kRingA>::value;
     uint32_t w[kRing][8];
@@ -484,6 +485,7 @@ int mfma_max_splits(int mt, int waves, int kwaves) {
     if (mt == 2 && waves == 2 && kwaves == 4) return Cfg<2, 2, 4>::kMaxSplits;
     if (mt == 4 && waves == 2 && kwaves == 2) return Cfg<4, 2, 2>::kMaxSplits;
     if (mt == 2 && waves == 1 && kwaves == 8) return Cfg<2, 1, 8>::kMaxSplits;
+    if (mt == 4 && waves == 2 && kwaves == 4) return Cfg<4, 2, 4>::kMaxSplits;
     return 1;
 }
 
@@ -493,6 +495,7 @@ hipError_t launch_mfma(const GemmArgs &g, const GemmPlan &p, hipStream_t stream)
     if (p.mt == 2 && p.waves == 2 && p.kwaves == 4) return launch_cfg<2, 2, 4>(g, p, stream);
     if (p.mt == 4 && p.waves == 2 && p.kwaves == 2) return launch_cfg<4, 2, 2>(g, p, stream);
     if (p.mt == 2 && p.waves == 1 && p.kwaves == 8) return launch_cfg<2, 1, 8>(g, p, stream);
+    if (p.mt == 4 && p.waves == 2 && p.kwaves == 4) return launch_cfg<4, 2, 4>(g, p, stream);
     return hipErrorInvalidValue;
 }
 
