@@ -274,6 +274,29 @@ int run_gemm(const uint16_t *a, const int32_t *b, const uint16_t *s, const int32
     return ok();
 }
 
+// GEMV whose activations are the glue transform (act 1: row-norm, act 2:
+// SwiGLU + row-norm) of `src` (row stride ld), for the decode step.
+int run_gemm_act(int act, const uint16_t *src, int64_t ld, const w4a16_linear &L, int64_t M, int64_t K, int64_t N,
+                 uint16_t *out, hipStream_t stream) {
+    const GemmPlan plan = plan_gemm(M, K, N, L.G);
+    GemmArgs args{nullptr, L.b_packed, L.scales, L.qzeros, M, K, N, L.G, L.zp_bias, out, nullptr, nullptr};
+    int rc = get_scratch(stream, plan, &args.partials, &args.counters);
+    if (rc != W4A16_OK) return rc;
+    hipError_t e = launch_gemv_act(args, plan, act, src, ld, stream);
+    if (e != hipSuccess) return fail(W4A16_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+    return ok();
+}
+
+// The three glue steps inside a layer fold into the next GEMV when all three
+// of those linears run the default GEMV shape (M <= 8, 8 waves, exact form).
+bool fused_glue(const w4a16_linear *L, int64_t M, int64_t H, int64_t I) {
+    const GemmPlan p1 = plan_gemm(M, H, H, L[1].G), p2 = plan_gemm(M, H, 2 * I, L[2].G),
+                   p3 = plan_gemm(M, I, H, L[3].G);
+    for (const GemmPlan *p : {&p1, &p2, &p3})
+        if (p->path != kPathGemv || p->waves != 8 || p->fold) return false;
+    return true;
+}
+
 // Decode-step workspace layout: T (GEMM outputs, M x maxN fp16) then Hb
 // (re-normalised inputs, M x max(H, I) fp16), each 256-byte aligned.
 struct DecodeShape {
@@ -393,6 +416,18 @@ int w4a16_decode_step(const w4a16_linear *lin, int64_t n_layers, const uint16_t 
     for (int64_t l = 0; l < n_layers; ++l) {
         const w4a16_linear *L = lin + 4 * l;
         const int64_t H = d.H, I = L[2].N / 2;
+        if (fused_glue(L, M, H, I)) {
+            // Row-norm and SwiGLU folded into the consuming GEMVs: o and d land
+            // in Hb, q and gu in T; only the layer's output norm is a kernel.
+            if ((rc = run_gemm(x, L[0].b_packed, L[0].scales, L[0].qzeros, M, H, L[0].N, L[0].G, L[0].zp_bias, T, stream)) ||
+                (rc = run_gemm_act(1, T, L[0].N, L[1], M, H, H, Hb, stream)) ||
+                (rc = run_gemm_act(1, Hb, H, L[2], M, H, 2 * I, T, stream)) ||
+                (rc = run_gemm_act(2, T, 2 * I, L[3], M, I, H, Hb, stream)) ||
+                (rc = glue(launch_rownorm(Hb, M, H, H, x_out, stream))))
+                return rc;
+            x = x_out;
+            continue;
+        }
         if ((rc = run_gemm(x, L[0].b_packed, L[0].scales, L[0].qzeros, M, H, L[0].N, L[0].G, L[0].zp_bias, T, stream)) ||
             (rc = glue(launch_rownorm(T, M, L[0].N, H, Hb, stream))) ||
             (rc = run_gemm(Hb, L[1].b_packed, L[1].scales, L[1].qzeros, M, H, H, L[1].G, L[1].zp_bias, T, stream)) ||

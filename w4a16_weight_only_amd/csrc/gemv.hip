@@ -113,9 +113,24 @@ __device__ __forceinline__ int xcd_local_index(int bid, int grid) {
     return (bid & 7) * (grid >> 3) + (bid >> 3);
 }
 
-template <int M, int WORDS, int NW, bool ASYM, bool FOLD>
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// Activation transform applied as the activations are loaded (the decode
+// step's glue between linears, folded into the consuming GEMV):
+//   ACT 0: a as given
+//   ACT 1: a[m][k] = fp16(src[m][k] * inv_m),  inv_m = 1/sqrt(mean_{k<K} src[m][k]^2 + 1e-6)
+//   ACT 2: t[m][k] = silu(src[m][k]) * src[m][K + k],  a[m][k] = fp16(t * inv_m), inv over t
+// src rows are `ld` elements apart; math in fp32, one RNE rounding to fp16.
+template <int ACT>
+__device__ __forceinline__ float act_value(const u32x4 &x, const u32x4 &y, int e) {
+    const float v = f16_bits_to_f32((x[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+    if constexpr (ACT == 2) return silu_mul(v, f16_bits_to_f32((y[e >> 1] >> (16 * (e & 1))) & 0xffffu));
+    else return v;
+}
+
+template <int M, int WORDS, int NW, bool ASYM, bool FOLD, int ACT>
 __global__ __launch_bounds__(64 * NW) void gemv_kernel(
-    const uint16_t *__restrict__ a, const uint32_t *__restrict__ b,
+    const uint16_t *__restrict__ a, const uint16_t *__restrict__ src, int ld, const uint32_t *__restrict__ b,
     const uint16_t *__restrict__ scales, const uint32_t *__restrict__ qzeros, int K, int N, int G,
     uint32_t zp, int tiles, int split_len, int splits, uint16_t *__restrict__ out,
     float *__restrict__ partials, uint32_t *__restrict__ counters) {
@@ -149,6 +164,46 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
 #pragma unroll
         for (int j = 0; j < COLS; ++j) acc[m][j] = 0.f;
 
+    // Row scales of the transformed activations: every workgroup sums the
+    // squares of its rows' full K range (16-byte loads, xor-shuffle within
+    // waves, waves through LDS in order).
+    __shared__ float s_inv[M];
+    if constexpr (ACT != 0) {
+        __shared__ float s_part[NW][M];
+        float ss[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) ss[m] = 0.f;
+        for (int k = (int)threadIdx.x * 8; k < K; k += 64 * NW * 8) {
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const uint16_t *row = src + (size_t)m * ld;
+                const u32x4 x = *reinterpret_cast<const u32x4 *>(row + k);
+                u32x4 y = x;
+                if constexpr (ACT == 2) y = *reinterpret_cast<const u32x4 *>(row + K + k);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float t = act_value<ACT>(x, y, e);
+                    ss[m] = __builtin_fmaf(t, t, ss[m]);
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            float v = ss[m];
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+            if (lane == 0) s_part[wave][m] = v;
+        }
+        __syncthreads();
+        if (threadIdx.x < M) {
+            float t = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) t += s_part[w][threadIdx.x];
+            s_inv[threadIdx.x] = 1.0f / sqrtf(t / (float)K + 1e-6f);
+        }
+        __syncthreads();
+    }
+
     for (int c = c_begin + wave * RL + rl; c < c_end; c += NW * RL) {
         const int k0 = c * kChunkRows;
         const int g = k0 / G;
@@ -158,10 +213,25 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
         uint32_t av[M][8];
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            const u32x4 *ap = reinterpret_cast<const u32x4 *>(a + (size_t)m * K + k0);
-            const u32x4 lo = ap[0], hi = ap[1];
-            av[m][0] = lo.x; av[m][1] = lo.y; av[m][2] = lo.z; av[m][3] = lo.w;
-            av[m][4] = hi.x; av[m][5] = hi.y; av[m][6] = hi.z; av[m][7] = hi.w;
+            if constexpr (ACT == 0) {
+                const u32x4 *ap = reinterpret_cast<const u32x4 *>(a + (size_t)m * K + k0);
+                const u32x4 lo = ap[0], hi = ap[1];
+                av[m][0] = lo.x; av[m][1] = lo.y; av[m][2] = lo.z; av[m][3] = lo.w;
+                av[m][4] = hi.x; av[m][5] = hi.y; av[m][6] = hi.z; av[m][7] = hi.w;
+            } else {
+                const uint16_t *row = src + (size_t)m * ld + k0;
+                const float inv = s_inv[m];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const u32x4 x = *reinterpret_cast<const u32x4 *>(row + 8 * h);
+                    u32x4 y = x;
+                    if constexpr (ACT == 2) y = *reinterpret_cast<const u32x4 *>(row + K + 8 * h);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        av[m][4 * h + j] = (uint32_t)f32_to_f16_bits(act_value<ACT>(x, y, 2 * j) * inv) |
+                                           ((uint32_t)f32_to_f16_bits(act_value<ACT>(x, y, 2 * j + 1) * inv) << 16);
+                }
+            }
         }
         uint32_t sw[COLS / 2];
         {
@@ -342,43 +412,53 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
     if (threadIdx.x == 0) reset_counter_agent(&counters[tile]);
 }
 
-template <int M, int WORDS, int NW, bool FOLD>
-hipError_t launch_v(const GemmArgs &g, const GemmPlan &p, hipStream_t stream) {
+template <int M, int WORDS, int NW, bool FOLD, int ACT>
+hipError_t launch_v(const GemmArgs &g, const GemmPlan &p, const uint16_t *src, int ld, hipStream_t stream) {
     dim3 grid((unsigned)p.grid, 1, 1);
     dim3 block(64 * NW, 1, 1);
     const uint32_t *b = reinterpret_cast<const uint32_t *>(g.b);
     const uint32_t *qz = reinterpret_cast<const uint32_t *>(g.qzeros);
     if (g.qzeros)
-        hipLaunchKernelGGL((gemv_kernel<M, WORDS, NW, true, FOLD>), grid, block, 0, stream, g.a, b, g.scales,
-                           qz, (int)g.K, (int)g.N, (int)g.G, (uint32_t)g.zp, (int)p.tiles_n,
+        hipLaunchKernelGGL((gemv_kernel<M, WORDS, NW, true, FOLD, ACT>), grid, block, 0, stream, g.a, src, ld, b,
+                           g.scales, qz, (int)g.K, (int)g.N, (int)g.G, (uint32_t)g.zp, (int)p.tiles_n,
                            (int)p.split_len, p.splits, g.out, g.partials, g.counters);
     else
-        hipLaunchKernelGGL((gemv_kernel<M, WORDS, NW, false, FOLD>), grid, block, 0, stream, g.a, b, g.scales,
-                           qz, (int)g.K, (int)g.N, (int)g.G, (uint32_t)g.zp, (int)p.tiles_n,
+        hipLaunchKernelGGL((gemv_kernel<M, WORDS, NW, false, FOLD, ACT>), grid, block, 0, stream, g.a, src, ld, b,
+                           g.scales, qz, (int)g.K, (int)g.N, (int)g.G, (uint32_t)g.zp, (int)p.tiles_n,
                            (int)p.split_len, p.splits, g.out, g.partials, g.counters);
     return hipGetLastError();
 }
 
 template <int M, int WORDS>
-hipError_t launch_m(const GemmArgs &g, const GemmPlan &p, hipStream_t stream) {
+hipError_t launch_m(const GemmArgs &g, const GemmPlan &p, int act, const uint16_t *src, int ld, hipStream_t stream) {
+    if (act == 1) return launch_v<M, WORDS, 8, false, 1>(g, p, src, ld, stream);
+    if (act == 2) return launch_v<M, WORDS, 8, false, 2>(g, p, src, ld, stream);
     if (p.fold)
-        return p.waves == 8 ? launch_v<M, WORDS, 8, true>(g, p, stream) : launch_v<M, WORDS, 4, true>(g, p, stream);
-    return p.waves == 8 ? launch_v<M, WORDS, 8, false>(g, p, stream) : launch_v<M, WORDS, 4, false>(g, p, stream);
+        return p.waves == 8 ? launch_v<M, WORDS, 8, true, 0>(g, p, src, ld, stream)
+                            : launch_v<M, WORDS, 4, true, 0>(g, p, src, ld, stream);
+    return p.waves == 8 ? launch_v<M, WORDS, 8, false, 0>(g, p, src, ld, stream)
+                        : launch_v<M, WORDS, 4, false, 0>(g, p, src, ld, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gemv(const GemmArgs &g, const GemmPlan &p, hipStream_t stream) {
+    return launch_gemv_act(g, p, 0, nullptr, 0, stream);
+}
+
+hipError_t launch_gemv_act(const GemmArgs &g, const GemmPlan &p, int act, const uint16_t *src, int64_t ld,
+                           hipStream_t stream) {
     if (p.splits > kMaxSplits) return hipErrorInvalidValue;
+    if (act != 0 && (p.fold || p.waves != 8 || !src || ld % 8 != 0 || g.K % 8 != 0)) return hipErrorInvalidValue;
     switch (g.M) {
-        case 1: return launch_m<1, 4>(g, p, stream);
-        case 2: return launch_m<2, 4>(g, p, stream);
-        case 3: return launch_m<3, 2>(g, p, stream);
-        case 4: return launch_m<4, 2>(g, p, stream);
-        case 5: return launch_m<5, 1>(g, p, stream);
-        case 6: return launch_m<6, 1>(g, p, stream);
-        case 7: return launch_m<7, 1>(g, p, stream);
-        case 8: return launch_m<8, 1>(g, p, stream);
+        case 1: return launch_m<1, 4>(g, p, act, src, (int)ld, stream);
+        case 2: return launch_m<2, 4>(g, p, act, src, (int)ld, stream);
+        case 3: return launch_m<3, 2>(g, p, act, src, (int)ld, stream);
+        case 4: return launch_m<4, 2>(g, p, act, src, (int)ld, stream);
+        case 5: return launch_m<5, 1>(g, p, act, src, (int)ld, stream);
+        case 6: return launch_m<6, 1>(g, p, act, src, (int)ld, stream);
+        case 7: return launch_m<7, 1>(g, p, act, src, (int)ld, stream);
+        case 8: return launch_m<8, 1>(g, p, act, src, (int)ld, stream);
         default: return hipErrorInvalidValue;
     }
 }

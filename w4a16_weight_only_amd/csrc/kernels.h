@@ -45,6 +45,13 @@ struct GemmArgs {
 GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G);
 
 hipError_t launch_gemv(const GemmArgs &args, const GemmPlan &plan, hipStream_t stream);
+// GEMV whose activations are transformed as they are loaded (decode-step
+// glue folded in): act 1: a = fp16(src * inv_row), act 2: a = fp16(silu(g) *
+// u * inv_row) with g = src[:, :K], u = src[:, K:2K]; inv_row =
+// 1/sqrt(mean(v^2) + 1e-6) over the transformed row; src rows ld elements
+// apart (ld and K multiples of 8).  Needs plan.waves == 8 and !plan.fold.
+hipError_t launch_gemv_act(const GemmArgs &args, const GemmPlan &plan, int act, const uint16_t *src,
+                           int64_t ld, hipStream_t stream);
 hipError_t launch_mfma(const GemmArgs &args, const GemmPlan &plan, hipStream_t stream);
 // Largest K-split count the MFMA kernel's in-kernel reduction takes for a
 // (mt, waves, kwaves) configuration.
