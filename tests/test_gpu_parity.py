@@ -110,11 +110,21 @@ def test_gemm_deterministic(M):
     assert np.array_equal(o1.view(np.uint16), o2.view(np.uint16))
 
 
+def f16_ulp(x):
+    """Spacing of fp16 values at |x| (subnormal spacing below 2^-14)."""
+    e = np.floor(np.log2(np.maximum(np.abs(x.astype(np.float64)), 2.0 ** -14)))
+    return 2.0 ** (e - 10)
+
+
 @pytest.mark.parametrize("M", [1, 5, 8, 12, 32, 256])
 def test_gemm_identities(M):
     """All-8 nibbles with zero point 8 give exactly 0; qzeros all 8 equal the
-    symmetric call bit for bit; doubling every scale doubles the output exactly."""
+    symmetric call bit for bit; doubling every scale doubles the output --
+    exactly where the K-splits meet in fp32, and to within one fp16 step where
+    the GEMV's K-splits meet in 2^-26 fixed point (each split's partial is
+    rounded to that grid, which does not commute with doubling)."""
     K, N, G = 1024, 512, 128
+    path, splits, _ = w4.w4a16_gemm_plan(M, K, N, G)
     p = synth.problem(M, K, N, G, False, seed=55 + M)
     a, b, s = dev(p["a"]), dev(p["b_packed"]), dev(p["scales"])
     eights = torch.full_like(b, np.uint32(0x88888888).view(np.int32).item())
@@ -124,8 +134,40 @@ def test_gemm_identities(M):
     sym = host(w4.w4a16_gemm(a, b, s, None, G, 8))
     asym = host(w4.w4a16_gemm(a, b, s, qz8, G, 3))
     assert np.array_equal(sym.view(np.uint16), asym.view(np.uint16))
-    dbl = host(w4.w4a16_gemm(a, b, s * 2, None, G, 8))
-    assert np.array_equal(dbl.astype(np.float64), 2 * sym.astype(np.float64))
+    dbl = host(w4.w4a16_gemm(a, b, s * 2, None, G, 8)).astype(np.float64)
+    two = 2 * sym.astype(np.float64)
+    if path == 1 and splits > 1:
+        assert np.all(np.abs(dbl - two) <= f16_ulp(two))
+    else:
+        assert np.array_equal(dbl, two)
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 12800), (4, 4096, 2048), (1, 256, 256), (32, 1024, 512)])
+def test_gemm_nonfinite_and_overflow(M, K, N):
+    """An inf activation makes exactly the oracle's non-finite outputs
+    non-finite (the GEMV's fixed-point K-split hand-off reports them as NaN);
+    activations of +-60000 against all-15 nibbles overflow fp16 to inf of the
+    oracle's sign, also where K-split partials saturate."""
+    G = 128 if K >= 128 else K
+    path, splits, _ = w4.w4a16_gemm_plan(M, K, N, G)
+    note("nonfinite M=%d K=%d N=%d path=%d splits=%d" % (M, K, N, path, splits))
+    p = synth.problem(M, K, N, G, False, seed=4242 + M)
+    a = p["a"].copy()
+    a[0, K // 3] = np.float16(np.inf)
+    got = run_gemm(dict(p, a=a), qzeros=False)
+    want = oracle.gemm(a, p["b_packed"], p["scales"], None, G, 8)
+    assert np.array_equal(np.isfinite(got), np.isfinite(want))
+    fin = np.isfinite(want)
+    check_close(np.where(fin, got, 0).astype(np.float16), np.where(fin, want, 0).astype(np.float16), "finite part")
+
+    big = np.full((M, K), 60000.0, dtype=np.float16)
+    big[M // 2:] = -60000.0
+    fifteens = np.full_like(p["b_packed"], np.uint32(0xFFFFFFFF).view(np.int32))
+    ones = np.ones_like(p["scales"])
+    got = run_gemm(dict(p, a=big, b_packed=fifteens, scales=ones), qzeros=False)
+    want = oracle.gemm(big, fifteens, ones, None, G, 8)
+    assert np.all(np.isinf(want))
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
 
 
 def test_gemm_m0_and_into_out():

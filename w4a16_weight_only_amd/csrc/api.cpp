@@ -115,8 +115,7 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G) {
     const int64_t N8 = N / 8;
     if (M <= 8 && N % 32 == 0) {
         // 256-column tiles (one 128-byte line of every weight row per
-        // workgroup); K-splits to give about gemv_target_waves waves, as few
-        // splits as possible (arrivals at one counter serialise).
+        // workgroup); K-splits to give about gemv_target_waves waves.
         p.path = kPathGemv;
         p.words = gemv_words_for_m(M);
         p.fold = t.gemv_fold != 0;
@@ -184,8 +183,14 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G) {
     }
     p.grid = p.tiles_n * p.tiles_m * p.splits;
     p.grid = cdiv(p.grid, 8) * 8;  // XCD-aware index mapping needs a multiple of 8
-    p.partial_floats = p.splits > 1 ? (size_t)(p.splits * M * N) : 0;
-    p.counters = p.splits > 1 ? (size_t)(p.tiles_n * p.tiles_m) : 0;
+    if (p.path == kPathGemv) {
+        // one 64-bit fixed-point slot per output (two counter words)
+        p.partial_floats = 0;
+        p.counters = p.splits > 1 ? (size_t)(2 * M * N) : 0;
+    } else {
+        p.partial_floats = p.splits > 1 ? (size_t)(p.splits * M * N) : 0;
+        p.counters = p.splits > 1 ? (size_t)(p.tiles_n * p.tiles_m) : 0;
+    }
     return p;
 }
 
@@ -194,9 +199,10 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G) {
 namespace {
 
 // ------------------------------------------------- library-owned scratch ---
-// Split-K partials and arrival counters, one set per (device, stream).  The
-// counters are zeroed once at allocation; each split-K tile's last workgroup
-// resets its counter, so they are zero again whenever the stream is idle.
+// Split-K partials and arrival counters / fixed-point slots, one set per
+// (device, stream).  The counter words are zeroed once at allocation; the
+// last arrival at each counter or slot zeroes it again, so they are zero
+// whenever the stream is idle.
 struct Scratch {
     float *partials = nullptr;
     size_t partial_cap = 0;  // floats

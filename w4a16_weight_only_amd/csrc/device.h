@@ -162,6 +162,48 @@ __device__ __forceinline__ void store_partial(float *p, float v) {
 __device__ __forceinline__ float load_partial(const float *p) {
     return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Split-K reduction in exact fixed point, so the result does not depend on the
+// order in which splits arrive.  Each output owns one zero-initialised 64-bit
+// slot:
+//   bits 58..63  arrivals
+//   bits 52..57  non-finite partials
+//   bits  0..51  sum over the finite partials p of round(p * 2^26) + 2^46
+// A split adds its partial (saturated to |p| <= 2^20 - 1) with one atomic.
+// The arrival that brings the count to `splits` holds the total (the value it
+// got back plus its own addition), writes the output and zeroes the slot for
+// the next call.  At most 32 splits, so no field carries into the next.
+constexpr int kFixFracBits = 26;
+constexpr int kSlotPoisonShift = 52;
+constexpr int kSlotCountShift = 58;
+constexpr int64_t kFixBias = 1ll << 46;
+constexpr float kFixMax = 1048575.0f;  // 2^20 - 1
+
+__device__ __forceinline__ uint64_t slot_contribution(float p) {
+    uint64_t add = 1ull << kSlotCountShift;
+    if (__builtin_isfinite(p)) {
+        const float c = fminf(fmaxf(p, -kFixMax), kFixMax);
+        add += (uint64_t)((int64_t)rintf(c * (float)(1 << kFixFracBits)) + kFixBias);
+    } else {
+        add += 1ull << kSlotPoisonShift;
+    }
+    return add;
+}
+__device__ __forceinline__ uint64_t slot_add(uint64_t *slot, uint64_t v) {
+    return __hip_atomic_fetch_add(slot, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool slot_last(uint64_t old, int splits) {
+    return (old >> kSlotCountShift) == (uint64_t)(splits - 1);
+}
+// fp16 output for a slot's final value (NaN if any partial was not finite).
+__device__ __forceinline__ uint16_t slot_result_f16(uint64_t total, int splits) {
+    if ((total >> kSlotPoisonShift) & 63u) return 0x7e00u;
+    const int64_t s = (int64_t)(total & ((1ull << kSlotPoisonShift) - 1)) - (int64_t)splits * kFixBias;
+    return f32_to_f16_bits((float)((double)s * (1.0 / (double)(1 << kFixFracBits))));
+}
+__device__ __forceinline__ void slot_reset(uint64_t *slot) {
+    __hip_atomic_store(slot, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima).
 __device__ __forceinline__ void wait_vm_zero() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ __forceinline__ uint32_t arrive_agent(uint32_t *counter) {

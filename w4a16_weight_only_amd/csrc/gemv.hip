@@ -21,11 +21,13 @@
 //    once per chunk (a chunk lies in one K-group).  No matrix cores.
 //  * Row lanes are reduced with a transpose-reduce over lane-xor shuffles
 //    (each step halves the values a lane holds), waves through LDS.  K-splits
-//    meet in an fp32 partials buffer: the last workgroup to arrive at a
-//    tile's counter loads every split's partials at once and sums them in
-//    split order (deterministic; an explicit reduction rather than float
-//    atomics, the lesson of the same article's section 3.4), then resets the
-//    counter for the next call.
+//    meet in one 64-bit slot per output: each split adds its fp32 partial as
+//    an exact fixed-point integer together with an arrival count, and the
+//    split whose atomic completes the count writes the fp16 output from the
+//    value the atomic returned (device.h).  Integer addition is associative,
+//    so the result is the same whatever the arrival order (no float atomics,
+//    the lesson of the same article's section 3.4), and the hand-off costs
+//    one atomic round trip instead of store, counter and reload.
 #include "device.h"
 #include "kernels.h"
 
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
     const uint16_t *__restrict__ a, const uint16_t *__restrict__ src, int ld, const uint32_t *__restrict__ b,
     const uint16_t *__restrict__ scales, const uint32_t *__restrict__ qzeros, int K, int N, int G,
     uint32_t zp, int tiles, int split_len, int splits, uint16_t *__restrict__ out,
-    float *__restrict__ partials, uint32_t *__restrict__ counters) {
+    uint32_t *__restrict__ counters) {
     constexpr int CL = kTileWords / WORDS;  // column lanes per row segment
     constexpr int RL = 64 / CL;             // row lanes
     constexpr int COLS = 8 * WORDS;         // columns per lane
@@ -378,38 +380,29 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
         }
         return;
     }
-#pragma unroll
-    for (int i = 0; i < PASSES; ++i) {
-        const int t = threadIdx.x + i * 64 * NW;
-        const int col = col_base + t % kTileCols;
-        if (t < M * kTileCols && col < N)
-            store_partial(&partials[((size_t)split * M + t / kTileCols) * N + col], sums[i]);
-    }
 
-    // Split-K: the last workgroup to arrive sums every split in split order.
-    wait_vm_zero();
-    __syncthreads();
-    __shared__ uint32_t last;
-    if (threadIdx.x == 0) last = (arrive_agent(&counters[tile]) == (uint32_t)(splits - 1)) ? 1u : 0u;
-    __syncthreads();
-    if (!last) return;
+    // Split-K: one fixed-point atomic per output and split (device.h); every
+    // atomic is issued before the first result is looked at.
+    uint64_t *slots = reinterpret_cast<uint64_t *>(counters);
+    uint64_t add[PASSES], old[PASSES];
 #pragma unroll
     for (int i = 0; i < PASSES; ++i) {
         const int t = threadIdx.x + i * 64 * NW;
         const int col = col_base + t % kTileCols;
-        if (t < M * kTileCols && col < N) {
-            // Issue every split's load before the first add.
-            float v[kMaxSplits];
+        add[i] = slot_contribution(sums[i]);
+        old[i] = 0;
+        if (t < M * kTileCols && col < N) old[i] = slot_add(&slots[(size_t)(t / kTileCols) * N + col], add[i]);
+    }
 #pragma unroll
-            for (int sp = 0; sp < kMaxSplits; ++sp)
-                v[sp] = sp < splits ? load_partial(&partials[((size_t)sp * M + t / kTileCols) * N + col]) : 0.f;
-            float s = 0.f;
-#pragma unroll
-            for (int sp = 0; sp < kMaxSplits; ++sp) s += v[sp];
-            out[(size_t)(t / kTileCols) * N + col] = f32_to_f16_bits(s);
+    for (int i = 0; i < PASSES; ++i) {
+        const int t = threadIdx.x + i * 64 * NW;
+        const int col = col_base + t % kTileCols;
+        if (t < M * kTileCols && col < N && slot_last(old[i], splits)) {
+            const size_t o = (size_t)(t / kTileCols) * N + col;
+            out[o] = slot_result_f16(old[i] + add[i], splits);
+            slot_reset(&slots[o]);
         }
     }
-    if (threadIdx.x == 0) reset_counter_agent(&counters[tile]);
 }
 
 template <int M, int WORDS, int NW, bool FOLD, int ACT>
@@ -421,11 +414,11 @@ hipError_t launch_v(const GemmArgs &g, const GemmPlan &p, const uint16_t *src, i
     if (g.qzeros)
         hipLaunchKernelGGL((gemv_kernel<M, WORDS, NW, true, FOLD, ACT>), grid, block, 0, stream, g.a, src, ld, b,
                            g.scales, qz, (int)g.K, (int)g.N, (int)g.G, (uint32_t)g.zp, (int)p.tiles_n,
-                           (int)p.split_len, p.splits, g.out, g.partials, g.counters);
+                           (int)p.split_len, p.splits, g.out, g.counters);
     else
         hipLaunchKernelGGL((gemv_kernel<M, WORDS, NW, false, FOLD, ACT>), grid, block, 0, stream, g.a, src, ld, b,
                            g.scales, qz, (int)g.K, (int)g.N, (int)g.G, (uint32_t)g.zp, (int)p.tiles_n,
-                           (int)p.split_len, p.splits, g.out, g.partials, g.counters);
+                           (int)p.split_len, p.splits, g.out, g.counters);
     return hipGetLastError();
 }
 

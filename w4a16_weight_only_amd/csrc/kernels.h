@@ -27,7 +27,8 @@ struct GemmPlan {
     int64_t split_len = 0;    // K-units per split (GEMV: 16-row chunks; MFMA: 32-row steps)
     int64_t grid = 0;         // workgroups launched
     size_t partial_floats = 0;  // fp32 split-K partials needed (0 when splits == 1)
-    size_t counters = 0;        // arrival counters needed
+    size_t counters = 0;        // zero-initialised words needed: MFMA arrival counters,
+                                // GEMV 64-bit fixed-point slots (two words per output)
 };
 
 struct GemmArgs {
