@@ -162,6 +162,18 @@ int w4a16_decode_step(const w4a16_linear *lin, int64_t n_layers, const uint16_t 
 int w4a16_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t G, int32_t *path,
                     int32_t *splits, int64_t *grid);
 
+/* Replace the planner's tuning overrides (the same "key=value,..." form the
+ * environment variable W4A16_TUNE gives at first use; NULL or "" restores the
+ * defaults).  Keys: gemv_target_waves, gemv_waves (4 or 8), gemv_splits,
+ * gemv_fold (1 folded form, 0 exact form, -1 folded for symmetric zero
+ * point at M <= 2), gemv_max_m,
+ * mfma_target_waves, mfma_splits, mfma_cfg (1..5), max_partial_bytes.  Every
+ * choice computes the same product; they differ in speed and in fp32
+ * rounding.  Unknown keys or malformed values: W4A16_ERR_INVALID_ARG and the
+ * current settings stay.  Affects calls planned after it returns; not
+ * meant to race with calls in flight on other threads. */
+int w4a16_set_tuning(const char *spec);
+
 /* Free library-owned scratch on every device after synchronising the streams
  * that used it.  Safe to call at any time no w4a16 call is in flight. */
 int w4a16_release(void);

@@ -51,6 +51,22 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, n)
 
 
+def test_set_tuning_changes_the_plan_and_rejects_bad_specs(lib):
+    default = w4.w4a16_gemm_plan(1, 4096, 12800, 128)
+    try:
+        w4.w4a16_set_tuning("gemv_splits=2")
+        assert w4.w4a16_gemm_plan(1, 4096, 12800, 128)[1] == 2
+        w4.w4a16_set_tuning("gemv_max_m=0")
+        assert w4.w4a16_gemm_plan(1, 4096, 12800, 128)[0] == 2
+        for bad in ("bogus=1", "gemv_splits", "gemv_splits=x", "gemv_splits=3q"):
+            with pytest.raises(RuntimeError):
+                w4.w4a16_set_tuning(bad)
+            assert w4.w4a16_gemm_plan(1, 4096, 12800, 128)[0] == 2  # unchanged
+    finally:
+        w4.w4a16_set_tuning(None)
+    assert w4.w4a16_gemm_plan(1, 4096, 12800, 128) == default
+
+
 def test_status_strings(lib):
     for code, name in w4.STATUS.items():
         assert lib.w4a16_status_string(code).decode() == name

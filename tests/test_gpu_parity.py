@@ -101,6 +101,29 @@ def test_gemm_matches_oracle(M, K, N, G, asym):
     check_close(got, want, "M=%d K=%d N=%d" % (M, K, N))
 
 
+TUNED_FORMS = ["gemv_fold=0", "gemv_fold=1", "gemv_waves=4", "gemv_waves=4,gemv_fold=1",
+               "gemv_splits=1", "gemv_splits=7", "gemv_max_m=0", "mfma_cfg=4", "mfma_cfg=5,mfma_splits=3"]
+
+
+@pytest.mark.parametrize("spec", TUNED_FORMS)
+def test_gemm_tuned_forms_match_oracle(spec):
+    """Every planner override computes the same product (the exact and folded
+    GEMV forms, 4- and 8-wave workgroups, forced split counts, the MFMA path
+    at small M, the alternative MFMA tile shapes)."""
+    try:
+        w4.w4a16_set_tuning(spec)
+        for M, K, N, G, asym in [(1, 1024, 544, 128, False), (2, 2048, 1024, 64, True), (3, 512, 800, 128, True),
+                                 (5, 1024, 288, 256, False), (8, 1024, 544, 128, True), (20, 1024, 520, 128, True)]:
+            path, splits, grid = w4.w4a16_gemm_plan(M, K, N, G)
+            note("tuned %s M=%d K=%d N=%d path=%d splits=%d grid=%d" % (spec, M, K, N, path, splits, grid))
+            p = synth.problem(M, K, N, G, asym, seed=300 + M)
+            got = run_gemm(p)
+            want = oracle.gemm(p["a"], p["b_packed"], p["scales"], p["qzeros"], G, 8)
+            check_close(got, want, "%s M=%d" % (spec, M))
+    finally:
+        w4.w4a16_set_tuning(None)
+
+
 @pytest.mark.parametrize("M", [1, 4, 8, 16, 32, 256])
 def test_gemm_deterministic(M):
     p = synth.problem(M, 4096, 2048, 128, True, seed=77)
@@ -116,13 +139,17 @@ def f16_ulp(x):
     return 2.0 ** (e - 10)
 
 
-@pytest.mark.parametrize("M", [1, 5, 8, 12, 32, 256])
+@pytest.mark.parametrize("M", [1, 2, 5, 8, 12, 32, 256])
 def test_gemm_identities(M):
-    """All-8 nibbles with zero point 8 give exactly 0; qzeros all 8 equal the
-    symmetric call bit for bit; doubling every scale doubles the output --
-    exactly where the K-splits meet in fp32, and to within one fp16 step where
-    the GEMV's K-splits meet in 2^-26 fixed point (each split's partial is
-    rounded to that grid, which does not commute with doubling)."""
+    """All-8 nibbles with zero point 8 give exactly 0 (also in the folded GEMV
+    form, whose zero correction runs the same dot chain); qzeros all 8 equal
+    the symmetric call bit for bit where both take the same arithmetic form
+    (the default folds only symmetric GEMVs at M <= 2: there, within the
+    tolerance, and bit for bit with the exact form forced); doubling every
+    scale doubles the output -- exactly where the K-splits meet in fp32, and
+    to within one fp16 step where the GEMV's K-splits meet in 2^-26 fixed point
+    (each split's partial is rounded to that grid, which does not commute with
+    doubling)."""
     K, N, G = 1024, 512, 128
     path, splits, _ = w4.w4a16_gemm_plan(M, K, N, G)
     p = synth.problem(M, K, N, G, False, seed=55 + M)
@@ -133,7 +160,17 @@ def test_gemm_identities(M):
     qz8 = torch.full((K // G, N // 8), np.uint32(0x88888888).view(np.int32).item(), dtype=torch.int32, device="cuda")
     sym = host(w4.w4a16_gemm(a, b, s, None, G, 8))
     asym = host(w4.w4a16_gemm(a, b, s, qz8, G, 3))
-    assert np.array_equal(sym.view(np.uint16), asym.view(np.uint16))
+    if path == 1 and M <= 2:
+        check_close(asym, sym, "asym vs folded sym")
+        try:
+            w4.w4a16_set_tuning("gemv_fold=0")
+            sym0 = host(w4.w4a16_gemm(a, b, s, None, G, 8))
+            asym0 = host(w4.w4a16_gemm(a, b, s, qz8, G, 3))
+        finally:
+            w4.w4a16_set_tuning(None)
+        assert np.array_equal(sym0.view(np.uint16), asym0.view(np.uint16))
+    else:
+        assert np.array_equal(sym.view(np.uint16), asym.view(np.uint16))
     dbl = host(w4.w4a16_gemm(a, b, s * 2, None, G, 8)).astype(np.float64)
     two = 2 * sym.astype(np.float64)
     if path == 1 and splits > 1:

@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
                                   ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]
     L.w4a16_release.restype = ctypes.c_int
     L.w4a16_release.argtypes = []
+    L.w4a16_set_tuning.restype = ctypes.c_int
+    L.w4a16_set_tuning.argtypes = [ctypes.c_char_p]
     _lib = L
     return L
 
@@ -198,6 +200,12 @@ def w4a16_gemm_plan(M, K, N, G):
     path, splits, grid = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
     _check(lib().w4a16_gemm_plan(M, K, N, G, ctypes.byref(path), ctypes.byref(splits), ctypes.byref(grid)))
     return path.value, splits.value, grid.value
+
+
+def w4a16_set_tuning(spec=None):
+    """Replace the planner's tuning overrides ("key=value,..."; None restores
+    the defaults)."""
+    _check(lib().w4a16_set_tuning(spec.encode() if spec else None))
 
 
 def w4a16_release():

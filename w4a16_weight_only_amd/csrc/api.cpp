@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -47,47 +48,68 @@ bool overlaps(const void *p, size_t pn, const void *q, size_t qn) {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // ---------------------------------------------------------------- tuning ---
-// Plan knobs, overridable for tuning sweeps via W4A16_TUNE="key=value,...".
+// Plan knobs, overridable for tuning sweeps: "key=value,..." from the
+// environment variable W4A16_TUNE at first use, or from w4a16_set_tuning().
 struct Tune {
     int64_t gemv_target_waves = 1600;  // aim for about this many GEMV waves
     int64_t gemv_waves = 8;            // waves per GEMV workgroup (4 or 8)
     int64_t gemv_splits = 0;           // force the GEMV K-split count
-    int64_t gemv_fold = 0;             // 1: bias/zero removed per chunk (fewer VALU ops)
+    int64_t gemv_fold = -1;            // bias/zero removed per chunk: 1 always, 0 never, -1 symmetric M <= 2
+    int64_t gemv_max_m = 8;            // largest M sent to the GEMV path (at most 8)
     int64_t mfma_target_waves = 2048;  // aim for about this many MFMA-path waves
-    int64_t mfma_splits = 0;        // force the MFMA split count
-    int64_t mfma_cfg = 0;  // force (mt, waves, kwaves): 1..4 = (1,2,4) (2,2,4) (4,2,2) (2,1,8)
+    int64_t mfma_splits = 0;           // force the MFMA split count
+    int64_t mfma_cfg = 0;  // force (mt, waves, kwaves): 1..5 = (1,2,4) (2,2,4) (4,2,2) (2,1,8) (4,2,4)
     int64_t max_partial_bytes = 64ll << 20;
 };
 
+// Returns false on an unknown key or a malformed entry (nothing applied).
+bool parse_tune(const char *spec, Tune *out) {
+    Tune v;
+    std::string s(spec ? spec : "");
+    size_t pos = 0;
+    while (pos < s.size()) {
+        size_t end = s.find(',', pos);
+        if (end == std::string::npos) end = s.size();
+        const std::string kv = s.substr(pos, end - pos);
+        pos = end + 1;
+        if (kv.empty()) continue;
+        const size_t eq = kv.find('=');
+        if (eq == std::string::npos) return false;
+        const std::string k = kv.substr(0, eq);
+        char *tail = nullptr;
+        const long long val = std::strtoll(kv.c_str() + eq + 1, &tail, 10);
+        if (tail == kv.c_str() + eq + 1 || *tail != '\0') return false;
+        if (k == "gemv_target_waves") v.gemv_target_waves = val;
+        else if (k == "gemv_waves") v.gemv_waves = val;
+        else if (k == "gemv_splits") v.gemv_splits = val;
+        else if (k == "gemv_fold") v.gemv_fold = val;
+        else if (k == "gemv_max_m") v.gemv_max_m = val;
+        else if (k == "mfma_target_waves") v.mfma_target_waves = val;
+        else if (k == "mfma_splits") v.mfma_splits = val;
+        else if (k == "mfma_cfg") v.mfma_cfg = val;
+        else if (k == "max_partial_bytes") v.max_partial_bytes = val;
+        else return false;
+    }
+    *out = v;
+    return true;
+}
+
+// The active knobs: an immutable snapshot, replaced whole by w4a16_set_tuning
+// (earlier snapshots are kept alive, so a plan being computed concurrently
+// keeps a valid view).
+std::atomic<const Tune *> g_tune{nullptr};
+
 const Tune &tune() {
-    static Tune t = [] {
-        Tune v;
-        const char *env = std::getenv("W4A16_TUNE");
-        if (!env) return v;
-        std::string s(env);
-        size_t pos = 0;
-        while (pos < s.size()) {
-            size_t end = s.find(',', pos);
-            if (end == std::string::npos) end = s.size();
-            std::string kv = s.substr(pos, end - pos);
-            size_t eq = kv.find('=');
-            if (eq != std::string::npos) {
-                std::string k = kv.substr(0, eq);
-                int64_t val = std::atoll(kv.c_str() + eq + 1);
-                if (k == "gemv_target_waves") v.gemv_target_waves = val;
-                else if (k == "gemv_waves") v.gemv_waves = val;
-                else if (k == "gemv_splits") v.gemv_splits = val;
-                else if (k == "gemv_fold") v.gemv_fold = val;
-                else if (k == "mfma_target_waves") v.mfma_target_waves = val;
-                else if (k == "mfma_splits") v.mfma_splits = val;
-                else if (k == "mfma_cfg") v.mfma_cfg = val;
-                else if (k == "max_partial_bytes") v.max_partial_bytes = val;
-            }
-            pos = end + 1;
-        }
+    const Tune *t = g_tune.load(std::memory_order_acquire);
+    if (t) return *t;
+    static const Tune *from_env = [] {
+        Tune *v = new Tune();
+        if (!parse_tune(std::getenv("W4A16_TUNE"), v)) *v = Tune();
         return v;
     }();
-    return t;
+    const Tune *expect = nullptr;
+    g_tune.compare_exchange_strong(expect, from_env, std::memory_order_acq_rel);
+    return *g_tune.load(std::memory_order_acquire);
 }
 
 // ---------------------------------------------------------- validation ---
@@ -113,12 +135,17 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G) {
     const Tune &t = tune();
     GemmPlan p;
     const int64_t N8 = N / 8;
-    if (M <= 8 && N % 32 == 0) {
+    if (M <= std::min<int64_t>(8, t.gemv_max_m) && N % 32 == 0) {
         // 256-column tiles (one 128-byte line of every weight row per
         // workgroup); K-splits to give about gemv_target_waves waves.
         p.path = kPathGemv;
         p.words = gemv_words_for_m(M);
-        p.fold = t.gemv_fold != 0;
+        // The folded form drops one packed subtract per weight pair; measured
+        // on MI355X it pays where the dot products are few (M <= 2, where the
+        // exact form also runs out of registers at M = 2).  By default only
+        // with a symmetric zero point, where it keeps all-zp columns exactly 0.
+        p.fold = t.gemv_fold < 0 ? M <= 2 : t.gemv_fold != 0;
+        p.fold_asym = t.gemv_fold > 0;
         const int64_t CL = 32 / p.words, RL = 64 / CL;
         p.tiles_n = cdiv(N8, 32);
         const int64_t nchunks = K / 16;
@@ -294,12 +321,12 @@ int run_gemm_act(int act, const uint16_t *src, int64_t ld, const w4a16_linear &L
 }
 
 // The three glue steps inside a layer fold into the next GEMV when all three
-// of those linears run the default GEMV shape (M <= 8, 8 waves, exact form).
+// of those linears run the default GEMV shape (M <= 8, 8 waves).
 bool fused_glue(const w4a16_linear *L, int64_t M, int64_t H, int64_t I) {
     const GemmPlan p1 = plan_gemm(M, H, H, L[1].G), p2 = plan_gemm(M, H, 2 * I, L[2].G),
                    p3 = plan_gemm(M, I, H, L[3].G);
     for (const GemmPlan *p : {&p1, &p2, &p3})
-        if (p->path != kPathGemv || p->waves != 8 || p->fold) return false;
+        if (p->path != kPathGemv || p->waves != 8) return false;
     return true;
 }
 
@@ -445,6 +472,17 @@ int w4a16_decode_step(const w4a16_linear *lin, int64_t n_layers, const uint16_t 
             return rc;
         x = x_out;
     }
+    return ok();
+}
+
+int w4a16_set_tuning(const char *spec) {
+    Tune *v = new Tune();
+    if (!parse_tune(spec, v)) {
+        delete v;
+        return fail(W4A16_ERR_INVALID_ARG, "malformed tuning spec or unknown key");
+    }
+    tune();  // the environment's snapshot is taken first, then replaced
+    g_tune.store(v, std::memory_order_release);
     return ok();
 }
 

@@ -15,9 +15,9 @@
 //  * Each lane converts nibbles two rows at a time (device.h) and accumulates
 //    a_k * (q - z) for the row pair with one v_dot2_f32_f16 into fp32.  In the
 //    exact form the zero point is subtracted in fp16 before the dot (exact:
-//    small integers); in the folded form the dot takes (bias + q) and
-//    (bias + z) * sum(a) is removed once per 16-row chunk (one VALU op fewer
-//    per pair, fp32 rounding of the biased sum).  The group scale is applied
+//    small integers); in the folded form the dot takes (bias + q) and the
+//    zero term is removed once per 16-row chunk (one VALU op fewer per pair,
+//    fp32 rounding of the biased sums).  The group scale is applied
 //    once per chunk (a chunk lies in one K-group).  No matrix cores.
 //  * Row lanes are reduced with a transpose-reduce over lane-xor shuffles
 //    (each step halves the values a lane holds), waves through LDS.  K-splits
@@ -297,23 +297,46 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
             }
         }
 
-        float asum[M];
+        // Folded form: remove (bias + z) * sum(a) per chunk.  Symmetric zero
+        // point: the correction is the same dot2 chain as the sums, run on the
+        // constant (bias + zp) pair, so a column whose nibbles all equal zp
+        // cancels to exactly 0.  Packed zeros vary by column: (bias + z) times
+        // the chunk's activation sum.
+        float corr[M][2], asum[M];
         if (FOLD) {
-            const f16x2 ones = as_f16x2(0x3c003c00u);
+            if constexpr (!ASYM) {
+                const f16x2 b0 = zero_pair_const<0>(zp), b1 = zero_pair_const<1>(zp);
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-                float s = 0.f;
+                for (int m = 0; m < M; ++m) {
+                    float c0 = dot2_first(b0, as_f16x2(av[m][0])), c1 = dot2_first(b1, as_f16x2(av[m][0]));
 #pragma unroll
-                for (int j = 0; j < 8; ++j) s = __builtin_amdgcn_fdot2(as_f16x2(av[m][j]), ones, s, false);
-                asum[m] = s;
+                    for (int j = 1; j < 8; ++j) {
+                        c0 = __builtin_amdgcn_fdot2(b0, as_f16x2(av[m][j]), c0, false);
+                        c1 = __builtin_amdgcn_fdot2(b1, as_f16x2(av[m][j]), c1, false);
+                    }
+                    corr[m][0] = c0;
+                    corr[m][1] = c1;
+                }
+            } else {
+                const f16x2 ones = as_f16x2(0x3c003c00u);
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    float s = 0.f;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) s = __builtin_amdgcn_fdot2(as_f16x2(av[m][j]), ones, s, false);
+                    asum[m] = s;
+                }
             }
         }
 #pragma unroll
         for (int j = 0; j < COLS; ++j) {
             const uint32_t bits = (j & 1) ? (sw[j >> 1] >> 16) : (sw[j >> 1] & 0xffffu);
             const float s = f16_bits_to_f32(bits);
-            if (FOLD) {
-                const uint32_t zq = ASYM ? ((zw.v[j >> 3] >> (4 * (j & 7))) & 0xfu) : zp;
+            if (FOLD && !ASYM) {
+#pragma unroll
+                for (int m = 0; m < M; ++m) acc[m][j] = __builtin_fmaf(s, p[m][j] - corr[m][j & 1], acc[m][j]);
+            } else if (FOLD) {
+                const uint32_t zq = (zw.v[j >> 3] >> (4 * (j & 7))) & 0xfu;
                 const float zb = (float)((j & 1) ? 64u + zq : 1024u + zq);
 #pragma unroll
                 for (int m = 0; m < M; ++m)
@@ -405,32 +428,35 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
     }
 }
 
-template <int M, int WORDS, int NW, bool FOLD, int ACT>
-hipError_t launch_v(const GemmArgs &g, const GemmPlan &p, const uint16_t *src, int ld, hipStream_t stream) {
-    dim3 grid((unsigned)p.grid, 1, 1);
-    dim3 block(64 * NW, 1, 1);
-    const uint32_t *b = reinterpret_cast<const uint32_t *>(g.b);
-    const uint32_t *qz = reinterpret_cast<const uint32_t *>(g.qzeros);
-    if (g.qzeros)
-        hipLaunchKernelGGL((gemv_kernel<M, WORDS, NW, true, FOLD, ACT>), grid, block, 0, stream, g.a, src, ld, b,
-                           g.scales, qz, (int)g.K, (int)g.N, (int)g.G, (uint32_t)g.zp, (int)p.tiles_n,
-                           (int)p.split_len, p.splits, g.out, g.counters);
-    else
-        hipLaunchKernelGGL((gemv_kernel<M, WORDS, NW, false, FOLD, ACT>), grid, block, 0, stream, g.a, src, ld, b,
-                           g.scales, qz, (int)g.K, (int)g.N, (int)g.G, (uint32_t)g.zp, (int)p.tiles_n,
-                           (int)p.split_len, p.splits, g.out, g.counters);
+template <int M, int WORDS, int NW, bool ASYM, bool FOLD, int ACT>
+hipError_t launch_k(const GemmArgs &g, const GemmPlan &p, const uint16_t *src, int ld, hipStream_t stream) {
+    hipLaunchKernelGGL((gemv_kernel<M, WORDS, NW, ASYM, FOLD, ACT>), dim3((unsigned)p.grid), dim3(64 * NW), 0, stream,
+                       g.a, src, ld, reinterpret_cast<const uint32_t *>(g.b), g.scales,
+                       reinterpret_cast<const uint32_t *>(g.qzeros), (int)g.K, (int)g.N, (int)g.G, (uint32_t)g.zp,
+                       (int)p.tiles_n, (int)p.split_len, p.splits, g.out, g.counters);
     return hipGetLastError();
+}
+
+template <int M, int WORDS, int NW, int ACT>
+hipError_t launch_v(const GemmArgs &g, const GemmPlan &p, const uint16_t *src, int ld, hipStream_t stream) {
+    // With the glue transform in the activation loads the folded form costs
+    // more registers than it saves VALU work (measured on MI355X): exact form.
+    if (ACT != 0)
+        return g.qzeros ? launch_k<M, WORDS, NW, true, false, ACT>(g, p, src, ld, stream)
+                        : launch_k<M, WORDS, NW, false, false, ACT>(g, p, src, ld, stream);
+    if (g.qzeros)
+        return p.fold_asym ? launch_k<M, WORDS, NW, true, true, ACT>(g, p, src, ld, stream)
+                           : launch_k<M, WORDS, NW, true, false, ACT>(g, p, src, ld, stream);
+    return p.fold ? launch_k<M, WORDS, NW, false, true, ACT>(g, p, src, ld, stream)
+                  : launch_k<M, WORDS, NW, false, false, ACT>(g, p, src, ld, stream);
 }
 
 template <int M, int WORDS>
 hipError_t launch_m(const GemmArgs &g, const GemmPlan &p, int act, const uint16_t *src, int ld, hipStream_t stream) {
-    if (act == 1) return launch_v<M, WORDS, 8, false, 1>(g, p, src, ld, stream);
-    if (act == 2) return launch_v<M, WORDS, 8, false, 2>(g, p, src, ld, stream);
-    if (p.fold)
-        return p.waves == 8 ? launch_v<M, WORDS, 8, true, 0>(g, p, src, ld, stream)
-                            : launch_v<M, WORDS, 4, true, 0>(g, p, src, ld, stream);
-    return p.waves == 8 ? launch_v<M, WORDS, 8, false, 0>(g, p, src, ld, stream)
-                        : launch_v<M, WORDS, 4, false, 0>(g, p, src, ld, stream);
+    if (act == 1) return launch_v<M, WORDS, 8, 1>(g, p, src, ld, stream);
+    if (act == 2) return launch_v<M, WORDS, 8, 2>(g, p, src, ld, stream);
+    return p.waves == 8 ? launch_v<M, WORDS, 8, 0>(g, p, src, ld, stream)
+                        : launch_v<M, WORDS, 4, 0>(g, p, src, ld, stream);
 }
 
 }  // namespace
@@ -442,7 +468,7 @@ hipError_t launch_gemv(const GemmArgs &g, const GemmPlan &p, hipStream_t stream)
 hipError_t launch_gemv_act(const GemmArgs &g, const GemmPlan &p, int act, const uint16_t *src, int64_t ld,
                            hipStream_t stream) {
     if (p.splits > kMaxSplits) return hipErrorInvalidValue;
-    if (act != 0 && (p.fold || p.waves != 8 || !src || ld % 8 != 0 || g.K % 8 != 0)) return hipErrorInvalidValue;
+    if (act != 0 && (p.waves != 8 || !src || ld % 8 != 0 || g.K % 8 != 0)) return hipErrorInvalidValue;
     switch (g.M) {
         case 1: return launch_m<1, 4>(g, p, act, src, (int)ld, stream);
         case 2: return launch_m<2, 4>(g, p, act, src, (int)ld, stream);

@@ -20,7 +20,8 @@ struct GemmPlan {
     int waves = 4;
     int mt = 1;
     int kwaves = 1;           // MFMA: waves dividing a workgroup's K range (LDS-reduced)
-    bool fold = false;        // GEMV: remove bias and zero per chunk instead of per pair
+    bool fold = false;        // GEMV, symmetric zero point: remove bias and zero per chunk, not per pair
+    bool fold_asym = false;   // the same with packed zeros
     int64_t tiles_n = 0;      // workgroup tiles along N
     int64_t tiles_m = 1;      // workgroup tiles along M (MFMA)
     int splits = 1;           // K-splits across workgroups
@@ -50,7 +51,7 @@ hipError_t launch_gemv(const GemmArgs &args, const GemmPlan &plan, hipStream_t s
 // glue folded in): act 1: a = fp16(src * inv_row), act 2: a = fp16(silu(g) *
 // u * inv_row) with g = src[:, :K], u = src[:, K:2K]; inv_row =
 // 1/sqrt(mean(v^2) + 1e-6) over the transformed row; src rows ld elements
-// apart (ld and K multiples of 8).  Needs plan.waves == 8 and !plan.fold.
+// apart (ld and K multiples of 8).  Needs plan.waves == 8.
 hipError_t launch_gemv_act(const GemmArgs &args, const GemmPlan &plan, int act, const uint16_t *src,
                            int64_t ld, hipStream_t stream);
 hipError_t launch_mfma(const GemmArgs &args, const GemmPlan &plan, hipStream_t stream);
