@@ -53,6 +53,9 @@ struct Cfg {
     static constexpr int kChunk = kSplitLoads / kMaxSplits < kUnits ? kSplitLoads / kMaxSplits : kUnits;
     static_assert(kUnits >= 1 && kTileRows * (kTileCols / 4) % kThreads == 0, "whole units per thread");
     static_assert(kChunk >= 1 && kUnits % kChunk == 0, "whole chunks");
+    // Row tiles per K-wave reduction round: every wave's share of a round
+    // (MTC * 8 KB) for all NWN * NWK waves within 128 KB of LDS.
+    static constexpr int kRedTiles = (NWN * NWK * MT * 8 <= 128) ? MT : (NWN * NWK * 8 * 2 <= 128 ? 2 : 1);
 };
 
 // Values a region must produce where it stands: an empty asm that reads and
@@ -342,75 +345,78 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
         });
     }
 
-    // Sum the NWK partial tiles in order wk = 0, 1, ... through LDS, one
-    // K-wave at a time (each round moves MT * 8 KB per N-wave).  Every wave
-    // stays to the end so that the workgroup barriers below see all of them.
-    // The adds go one row tile (8 vectors) at a time, with scheduling
-    // barriers, so that the LDS reads are not all hoisted into registers.
-    if constexpr (NWK > 1) {
-        __shared__ f32x4 red[NWN][MT * 8][64];
-#pragma unroll
-        for (int r = 1; r < NWK; ++r) {
-            if (wk == r) {
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-                    for (int t = 0; t < 8; ++t) red[wn][mt * 8 + t][lane] = acc[mt][t];
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-            __syncthreads();
-            if (wk == 0) {
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-                    for (int t = 0; t < 8; ++t) acc[mt][t] += red[wn][mt * 8 + t][lane];
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-            __syncthreads();
-        }
-    }
-    const bool owner = wk == 0 && col_ok;
-
-    // acc[mt][t][v] = C[m0 + 16*mt + 4*kq + v][8*word + t].
-    if (splits == 1) {
-        if (!owner) return;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int row = m0 + 16 * mt + 4 * kq + v;
-                if (row >= M) continue;
-                f16x8 o;
-#pragma unroll
-                for (int t = 0; t < 8; ++t) o[t] = (f16)acc[mt][t][v];
-                *reinterpret_cast<f16x8 *>(out + (size_t)row * N + word * 8) = o;
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        return;
-    }
-
-    // Split-K: this split's tile to partials[split] (device-coherent stores).
-    const __amdgpu_buffer_rsrc_t prs = buffer_rsrc(partials, (uint32_t)((uint64_t)splits * M * N * 4));
+    // K-wave reduction and tile store.  A "row slot" (mt, v) is the row
+    // m0 + 16*mt + 4*kq + v of every lane, 8 columns 8*word + 0..7 per lane:
+    // acc[mt][0..7][v].  Every wave writes its slots to LDS at once (in rounds
+    // of MTC row tiles, so the buffer stays within LDS); after one barrier,
+    // each K-wave of an N-wave group sums its share of the slots over the
+    // group's NWK waves in order wk = 0, 1, ... (deterministic) and stores
+    // those rows itself: fp16 when the grid does not split K, else fp32 with
+    // device-coherent stores into partials[split].
+    typedef f16 f16x8_t __attribute__((ext_vector_type(8)));
+    const __amdgpu_buffer_rsrc_t prs =
+        buffer_rsrc(partials, splits > 1 ? (uint32_t)((uint64_t)splits * M * N * 4) : 0u);
     const uint32_t plane = (uint32_t)M * (uint32_t)N * 4u;
-    if (owner) {
+    auto store_slot = [&](int mt, int v, const f32x4 &lo, const f32x4 &hi) __attribute__((always_inline)) {
+        const int row = m0 + 16 * mt + 4 * kq + v;
+        if (row >= M || !col_ok) return;
+        if (splits == 1) {
+            f16x8_t o;
+            o[0] = (f16)lo.x; o[1] = (f16)lo.y; o[2] = (f16)lo.z; o[3] = (f16)lo.w;
+            o[4] = (f16)hi.x; o[5] = (f16)hi.y; o[6] = (f16)hi.z; o[7] = (f16)hi.w;
+            *reinterpret_cast<f16x8_t *>(out + (size_t)row * N + word * 8) = o;
+        } else {
+            const uint32_t off = ((uint32_t)row * (uint32_t)N + (uint32_t)word * 8u) * 4u;
+            buffer_store_f32x4_sc1(lo, prs, off, (uint32_t)split * plane);
+            buffer_store_f32x4_sc1(hi, prs, off + 16u, (uint32_t)split * plane);
+        }
+    };
+    auto slot_lo = [&](int mt, int v) __attribute__((always_inline)) {
+        return f32x4{acc[mt][0][v], acc[mt][1][v], acc[mt][2][v], acc[mt][3][v]};
+    };
+    auto slot_hi = [&](int mt, int v) __attribute__((always_inline)) {
+        return f32x4{acc[mt][4][v], acc[mt][5][v], acc[mt][6][v], acc[mt][7][v]};
+    };
+    if constexpr (NWK == 1) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int row = m0 + 16 * mt + 4 * kq + v;
-                if (row >= M) continue;
-                const uint32_t off = ((uint32_t)row * (uint32_t)N + (uint32_t)word * 8u) * 4u;
-                buffer_store_f32x4_sc1(f32x4{acc[mt][0][v], acc[mt][1][v], acc[mt][2][v], acc[mt][3][v]}, prs,
-                                       off, (uint32_t)split * plane);
-                buffer_store_f32x4_sc1(f32x4{acc[mt][4][v], acc[mt][5][v], acc[mt][6][v], acc[mt][7][v]}, prs,
-                                       off + 16u, (uint32_t)split * plane);
-            }
+            for (int v = 0; v < 4; ++v) store_slot(mt, v, slot_lo(mt, v), slot_hi(mt, v));
             __builtin_amdgcn_sched_barrier(0);
         }
+    } else {
+        constexpr int MTC = C::kRedTiles;               // row tiles per round
+        constexpr int SLOTS = MTC * 4;                  // row slots per round
+        constexpr int PER = (SLOTS + NWK - 1) / NWK;    // slots per reducing wave
+        static_assert(MT % MTC == 0, "whole rounds");
+        __shared__ f32x4 red[NWN][NWK][SLOTS][2][64];
+#pragma unroll
+        for (int r0 = 0; r0 < MT; r0 += MTC) {
+            if (r0 > 0) __syncthreads();  // previous round's reads are done
+#pragma unroll
+            for (int q = 0; q < SLOTS; ++q) {
+                red[wn][wk][q][0][lane] = slot_lo(r0 + q / 4, q % 4);
+                red[wn][wk][q][1][lane] = slot_hi(r0 + q / 4, q % 4);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const int q = wk * PER + i;
+                if (q < SLOTS) {
+                    f32x4 lo = red[wn][0][q][0][lane], hi = red[wn][0][q][1][lane];
+#pragma unroll
+                    for (int src = 1; src < NWK; ++src) {
+                        lo += red[wn][src][q][0][lane];
+                        hi += red[wn][src][q][1][lane];
+                    }
+                    store_slot(r0 + q / 4, q % 4, lo, hi);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
     }
+    if (splits == 1) return;
+
     wait_vm_zero();
     __syncthreads();
     __shared__ uint32_t last;
