@@ -259,11 +259,39 @@ def bench_copy_context(torch, stream, nbytes, steps, warmup):
                 hbm_frac=8 * n / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
 
 
+def bench_fp16_dense(torch, stream, steps, warmup):
+    """Context only: the same products with dense fp16 weights through torch's
+    own GEMM (the vendor BLAS), weights rotated past the last-level cache and
+    timed like the W4A16 rows.  Shows the byte saving of 4-bit weights at
+    M = 1 and the compute side at M = 32 and 256."""
+    rows = {}
+    for (M, K, N) in [(1, 4096, 12800), (32, 4096, 12800), (256, 12800, 4096)]:
+        copies = max(2, -(-768 * 2 ** 20 // (K * N * 2)))
+        g = torch.Generator(device="cuda").manual_seed(M + K + N)
+        A = torch.randn(M, K, device="cuda", dtype=torch.float16, generator=g)
+        W = [torch.randn(K, N, device="cuda", dtype=torch.float16, generator=g) for _ in range(copies)]
+        O = torch.empty(M, N, device="cuda", dtype=torch.float16)
+
+        def launch(i):
+            torch.matmul(A, W[i % copies], out=O)
+
+        ms, _ = timed_graph(torch, stream, launch, steps, warmup)
+        us = ms * 1e3
+        rows["M%d_K%d_N%d" % (M, K, N)] = dict(
+            us_per_call=us, weight_bytes=K * N * 2, gbs=K * N * 2 / (us * 1e-6) / 1e9,
+            tflops=2.0 * M * N * K / (us * 1e-6) / 1e12,
+            mfma_frac=2.0 * M * N * K / (us * 1e-6) / 1e12 / FP16_PEAK_TFLOPS)
+        del A, W, O
+        torch.cuda.empty_cache()
+    return rows
+
+
 EXTRA_ROWS = {
     "batched_M32": lambda t, w, st, k, wu: bench_gemm(t, w, st, 32, 4096, 12800, 128, True, k, wu, 3),
     "prefill_M256": lambda t, w, st, k, wu: bench_gemm(t, w, st, 256, 12800, 4096, 128, True, k, wu, 4),
     "repack_K4096_N12800": lambda t, w, st, k, wu: bench_repack(t, w, st, 4096, 12800, k, wu),
     "decode_step": lambda t, w, st, k, wu: bench_decode(t, w, st, [1, 32], max(5, k // 20), 3),
+    "fp16_dense_context": lambda t, w, st, k, wu: bench_fp16_dense(t, st, min(k, 100), wu),
     "copy_context_27MB": lambda t, w, st, k, wu: bench_copy_context(
         t, st, alg_bytes(1, 4096, 12800, 128, False), k, wu),
 }
