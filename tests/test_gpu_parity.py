@@ -299,6 +299,34 @@ def test_decode_step_small_stack(M):
     assert rel < 1e-2
 
 
+@pytest.mark.parametrize("M", [1, 2, 5])
+@pytest.mark.parametrize("H,NQ,I", [(256, 384, 512), (512, 768, 9216), (512, 512, 17408)])
+def test_decode_step_fused_equals_unfused(M, H, NQ, I):
+    """At M <= 8 the row-norm and SwiGLU glue runs inside the consuming GEMVs'
+    activation loads, and a layer's output row-norm inside the next layer's
+    QKV.  The GEMV computes each row scale in the standalone glue kernels' own
+    summation order, so the step equals the unfused one (separate glue
+    kernels, forced with decode_fuse=0) bit for bit.  Row widths up to 17408
+    cover one, two and four 8-element vectors per virtual thread."""
+    G, nl = 128, 2
+    layers = []
+    for l in range(nl):
+        layers += synth.stack_layer(l, H=H, NQ=NQ, I=I, G=G, seed_base=1700)
+    x = dev(synth.stack_input(M, H, seed=40 + M))
+    dstack = dev_stack(layers)
+    note("decode fused vs unfused M=%d H=%d I=%d" % (M, H, I))
+    fused = host(w4.w4a16_decode_step(dstack, x))
+    try:
+        w4.w4a16_set_tuning("decode_fuse=0")
+        unfused = host(w4.w4a16_decode_step(dstack, x))
+    finally:
+        w4.w4a16_set_tuning(None)
+    assert np.array_equal(fused.view(np.uint16), unfused.view(np.uint16))
+    want = oracle.decode_step(layers[:4], host(x), 1)
+    first = host(w4.w4a16_decode_step(dstack[:4], x))
+    check_close(first, want, "fused layer 0 M=%d I=%d" % (M, I))
+
+
 @pytest.mark.parametrize("M", [1, 16])
 def test_decode_step_one_real_layer(M):
     """One layer at the 8B-class shapes (QKV 4096->6144, O, gate+up

@@ -60,6 +60,7 @@ struct Tune {
     int64_t mfma_splits = 0;           // force the MFMA split count
     int64_t mfma_cfg = 0;  // force (mt, waves, kwaves): 1..5 = (1,2,4) (2,2,4) (4,2,2) (2,1,8) (4,2,4)
     int64_t max_partial_bytes = 64ll << 20;
+    int64_t decode_fuse = 1;           // 0: decode-step glue as separate kernels
 };
 
 // Returns false on an unknown key or a malformed entry (nothing applied).
@@ -88,6 +89,7 @@ bool parse_tune(const char *spec, Tune *out) {
         else if (k == "mfma_splits") v.mfma_splits = val;
         else if (k == "mfma_cfg") v.mfma_cfg = val;
         else if (k == "max_partial_bytes") v.max_partial_bytes = val;
+        else if (k == "decode_fuse") v.decode_fuse = val;
         else return false;
     }
     *out = v;
@@ -295,10 +297,15 @@ int validate_gemm(const uint16_t *a, const int32_t *b, const uint16_t *s, const 
     return W4A16_OK;
 }
 
+// exact_form: the GEMV keeps (q - z) exact per weight (no folded zero
+// correction).  The decode step uses it for every linear, so that its fused
+// and unfused routes compute each linear the same way, bit for bit.
 int run_gemm(const uint16_t *a, const int32_t *b, const uint16_t *s, const int32_t *qz, int64_t M,
-             int64_t K, int64_t N, int64_t G, int32_t zp, uint16_t *out, hipStream_t stream) {
+             int64_t K, int64_t N, int64_t G, int32_t zp, uint16_t *out, hipStream_t stream,
+             bool exact_form = false) {
     if (M == 0) return ok();
-    const GemmPlan plan = plan_gemm(M, K, N, G);
+    GemmPlan plan = plan_gemm(M, K, N, G);
+    if (exact_form) plan.fold = plan.fold_asym = false;
     GemmArgs args{a, b, s, qz, M, K, N, G, zp, out, nullptr, nullptr};
     int rc = get_scratch(stream, plan, &args.partials, &args.counters);
     if (rc != W4A16_OK) return rc;
@@ -322,12 +329,15 @@ int run_gemm_act(int act, const uint16_t *src, int64_t ld, const w4a16_linear &L
 
 // The three glue steps inside a layer fold into the next GEMV when all three
 // of those linears run the default GEMV shape (M <= 8, 8 waves).
+bool fusable(const GemmPlan &p) { return p.path == kPathGemv && p.waves == 8; }
 bool fused_glue(const w4a16_linear *L, int64_t M, int64_t H, int64_t I) {
-    const GemmPlan p1 = plan_gemm(M, H, H, L[1].G), p2 = plan_gemm(M, H, 2 * I, L[2].G),
-                   p3 = plan_gemm(M, I, H, L[3].G);
-    for (const GemmPlan *p : {&p1, &p2, &p3})
-        if (p->path != kPathGemv || p->waves != 8) return false;
-    return true;
+    if (tune().decode_fuse == 0) return false;
+    return fusable(plan_gemm(M, H, H, L[1].G)) && fusable(plan_gemm(M, H, 2 * I, L[2].G)) &&
+           fusable(plan_gemm(M, I, H, L[3].G));
+}
+// The layer-output row-norm folds into the next layer's QKV GEMV.
+bool fused_qkv(const w4a16_linear *L, int64_t M, int64_t H) {
+    return tune().decode_fuse != 0 && fusable(plan_gemm(M, H, L[0].N, L[0].G));
 }
 
 // Decode-step workspace layout: T (GEMM outputs, M x maxN fp16) then Hb
@@ -446,32 +456,44 @@ int w4a16_decode_step(const w4a16_linear *lin, int64_t n_layers, const uint16_t 
         return e == hipSuccess ? W4A16_OK
                                : fail(W4A16_ERR_HIP, std::string("glue launch: ") + hipGetErrorString(e));
     };
+    // `pending`: Hb holds the previous layer's down-projection output whose
+    // row-norm has not been applied yet (the next fused QKV applies it on load,
+    // bit for bit as the row-norm kernel would).
+    bool pending = false;
     for (int64_t l = 0; l < n_layers; ++l) {
         const w4a16_linear *L = lin + 4 * l;
         const int64_t H = d.H, I = L[2].N / 2;
-        if (fused_glue(L, M, H, I)) {
+        const bool fuse = fused_glue(L, M, H, I);
+        if (pending && !(fuse && fused_qkv(L, M, H))) {
+            if ((rc = glue(launch_rownorm(Hb, M, H, H, x_out, stream)))) return rc;
+            x = x_out;
+            pending = false;
+        }
+        if (fuse) {
             // Row-norm and SwiGLU folded into the consuming GEMVs: o and d land
-            // in Hb, q and gu in T; only the layer's output norm is a kernel.
-            if ((rc = run_gemm(x, L[0].b_packed, L[0].scales, L[0].qzeros, M, H, L[0].N, L[0].G, L[0].zp_bias, T, stream)) ||
+            // in Hb, q and gu in T.
+            if ((rc = pending ? run_gemm_act(1, Hb, H, L[0], M, H, L[0].N, T, stream)
+                              : run_gemm(x, L[0].b_packed, L[0].scales, L[0].qzeros, M, H, L[0].N, L[0].G,
+                                         L[0].zp_bias, T, stream, true)) ||
                 (rc = run_gemm_act(1, T, L[0].N, L[1], M, H, H, Hb, stream)) ||
                 (rc = run_gemm_act(1, Hb, H, L[2], M, H, 2 * I, T, stream)) ||
-                (rc = run_gemm_act(2, T, 2 * I, L[3], M, I, H, Hb, stream)) ||
-                (rc = glue(launch_rownorm(Hb, M, H, H, x_out, stream))))
+                (rc = run_gemm_act(2, T, 2 * I, L[3], M, I, H, Hb, stream)))
                 return rc;
-            x = x_out;
+            pending = true;
             continue;
         }
-        if ((rc = run_gemm(x, L[0].b_packed, L[0].scales, L[0].qzeros, M, H, L[0].N, L[0].G, L[0].zp_bias, T, stream)) ||
+        if ((rc = run_gemm(x, L[0].b_packed, L[0].scales, L[0].qzeros, M, H, L[0].N, L[0].G, L[0].zp_bias, T, stream, true)) ||
             (rc = glue(launch_rownorm(T, M, L[0].N, H, Hb, stream))) ||
-            (rc = run_gemm(Hb, L[1].b_packed, L[1].scales, L[1].qzeros, M, H, H, L[1].G, L[1].zp_bias, T, stream)) ||
+            (rc = run_gemm(Hb, L[1].b_packed, L[1].scales, L[1].qzeros, M, H, H, L[1].G, L[1].zp_bias, T, stream, true)) ||
             (rc = glue(launch_rownorm(T, M, H, H, Hb, stream))) ||
-            (rc = run_gemm(Hb, L[2].b_packed, L[2].scales, L[2].qzeros, M, H, 2 * I, L[2].G, L[2].zp_bias, T, stream)) ||
+            (rc = run_gemm(Hb, L[2].b_packed, L[2].scales, L[2].qzeros, M, H, 2 * I, L[2].G, L[2].zp_bias, T, stream, true)) ||
             (rc = glue(launch_swiglu_rownorm(T, M, I, Hb, stream))) ||
-            (rc = run_gemm(Hb, L[3].b_packed, L[3].scales, L[3].qzeros, M, I, H, L[3].G, L[3].zp_bias, T, stream)) ||
+            (rc = run_gemm(Hb, L[3].b_packed, L[3].scales, L[3].qzeros, M, I, H, L[3].G, L[3].zp_bias, T, stream, true)) ||
             (rc = glue(launch_rownorm(T, M, H, H, x_out, stream))))
             return rc;
         x = x_out;
     }
+    if (pending && (rc = glue(launch_rownorm(Hb, M, d.H, d.H, x_out, stream)))) return rc;
     return ok();
 }
 

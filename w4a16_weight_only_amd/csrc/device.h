@@ -148,6 +148,29 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
     return __builtin_bit_cast(uint16_t, (f16)x);  // round-to-nearest-even
 }
 
+// Decode-step glue arithmetic, shared by the standalone glue kernels and the
+// GEMVs that apply the glue as they load activations, so that both round the
+// same way bit for bit.  A value passed through an empty asm is opaque to the
+// optimiser: it is rounded to fp32 on its own and cannot be fused with what
+// follows (left alone, the compiler turned fp16(t * inv) into one
+// mixed-precision multiply that rounds once in one kernel and into a multiply
+// plus a conversion, two roundings, in another).
+__device__ __forceinline__ float opaque(float x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+// fp16(t * inv): the product rounded to fp32, then to fp16 (RNE).
+__device__ __forceinline__ uint32_t scaled_f16(float t, float inv) { return f32_to_f16_bits(opaque(t * inv)); }
+// 1 / sqrt(sum_sq / width + 1e-6).
+__device__ __forceinline__ float row_inv(float sum_sq, int width) {
+    return 1.0f / sqrtf(opaque(sum_sq / (float)width) + 1e-6f);
+}
+// silu(g) * u with silu(g) = g / (1 + exp(-g)).
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    const float d = opaque(1.0f + opaque(expf(-g)));
+    return opaque(g / d) * u;
+}
+
 // Split-K hand-off between workgroups that may sit on different XCDs (each
 // with its own L2).  Partial sums are written with device-scope stores (sc1:
 // coherent at device scope by themselves) and read back with device-scope

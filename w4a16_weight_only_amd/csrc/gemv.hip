@@ -115,8 +115,6 @@ __device__ __forceinline__ int xcd_local_index(int bid, int grid) {
     return (bid & 7) * (grid >> 3) + (bid >> 3);
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
-
 // Activation transform applied as the activations are loaded (the decode
 // step's glue between linears, folded into the consuming GEMV):
 //   ACT 0: a as given
@@ -128,6 +126,46 @@ __device__ __forceinline__ float act_value(const u32x4 &x, const u32x4 &y, int e
     const float v = f16_bits_to_f32((x[e >> 1] >> (16 * (e & 1))) & 0xffffu);
     if constexpr (ACT == 2) return silu_mul(v, f16_bits_to_f32((y[e >> 1] >> (16 * (e & 1))) & 0xffffu));
     else return v;
+}
+
+// Row sums of squares of the transformed activations, in the glue kernels'
+// order (glue.hip): 1024 virtual threads, virtual thread i accumulates vectors
+// i + 1024 j (j = 0, 1, ...) element by element with fma, each wave of 64
+// reduces with an xor-shuffle and the 16 wave sums are added in order.  Thread
+// t of the 512-thread workgroup plays virtual threads t (chain 0) and t + 512
+// (chain 1), so the row scale is bit for bit the standalone glue kernel's and
+// the fused and unfused decode steps agree exactly.
+template <int ACT>
+__device__ __forceinline__ float sq_chain(const u32x4 &x, const u32x4 &y, float ss) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float t = act_value<ACT>(x, y, e);
+        ss = __builtin_fmaf(t, t, ss);
+    }
+    return ss;
+}
+
+template <int M>
+__device__ __forceinline__ void row_scales(const float (&ss)[M][2], int K, float (&s_part)[16][M],
+                                           float (&s_inv)[M]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float v = ss[m][h];
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+            if (lane == 0) s_part[8 * h + wave][m] = v;
+        }
+    __syncthreads();
+    if (threadIdx.x < M) {
+        float t = 0.f;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) t += s_part[w][threadIdx.x];
+        s_inv[threadIdx.x] = row_inv(t, K);
+    }
+    __syncthreads();
 }
 
 template <int M, int WORDS, int NW, bool ASYM, bool FOLD, int ACT>
@@ -166,92 +204,74 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
 #pragma unroll
         for (int j = 0; j < COLS; ++j) acc[m][j] = 0.f;
 
-    // Row scales of the transformed activations: every workgroup sums the
-    // squares of its rows' full K range (16-byte loads, xor-shuffle within
-    // waves, waves through LDS in order).
+    // Activation transform (ACT != 0): the rows' scales come first, before
+    // the weight stream starts.  (Issuing the weights first and summing the
+    // rows while they are in flight measured slower on MI355X: the
+    // workgroup barrier then waits for every wave's back-pressured weight
+    // requests.)
     __shared__ float s_inv[M];
-    if constexpr (ACT != 0) {
-        __shared__ float s_part[NW][M];
-        float ss[M];
-#pragma unroll
-        for (int m = 0; m < M; ++m) ss[m] = 0.f;
-        for (int k = (int)threadIdx.x * 8; k < K; k += 64 * NW * 8) {
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                const uint16_t *row = src + (size_t)m * ld;
-                const u32x4 x = *reinterpret_cast<const u32x4 *>(row + k);
-                u32x4 y = x;
-                if constexpr (ACT == 2) y = *reinterpret_cast<const u32x4 *>(row + K + k);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float t = act_value<ACT>(x, y, e);
-                    ss[m] = __builtin_fmaf(t, t, ss[m]);
-                }
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            float v = ss[m];
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-            if (lane == 0) s_part[wave][m] = v;
-        }
-        __syncthreads();
-        if (threadIdx.x < M) {
-            float t = 0.f;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) t += s_part[w][threadIdx.x];
-            s_inv[threadIdx.x] = 1.0f / sqrtf(t / (float)K + 1e-6f);
-        }
-        __syncthreads();
-    }
+    __shared__ float s_part[16][M];
 
-    for (int c = c_begin + wave * RL + rl; c < c_end; c += NW * RL) {
+    struct Chunk {
+        u32x4 ax[M][2], ay[M][2];  // raw activations (ACT 2: gate in ax, up in ay)
+        uint32_t sw[COLS / 2];     // scale bits, two columns per word
+        Words<WORDS> zw;           // packed zeros (ASYM)
+        Words<WORDS> w[kChunkRows];
+    };
+    // Small loads first, the weight stream last, so that row pairs are
+    // consumed in order as they land.
+    auto load_chunk = [&](int c, Chunk &d) __attribute__((always_inline)) {
         const int k0 = c * kChunkRows;
         const int g = k0 / G;
-
-        // Small loads first, the weight stream last, so that row pairs are
-        // consumed in order as they land.
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const uint16_t *row = ACT == 0 ? a + (size_t)m * K + k0 : src + (size_t)m * ld + k0;
+            d.ax[m][0] = *reinterpret_cast<const u32x4 *>(row);
+            d.ax[m][1] = *reinterpret_cast<const u32x4 *>(row + 8);
+            if constexpr (ACT == 2) {
+                d.ay[m][0] = *reinterpret_cast<const u32x4 *>(row + K);
+                d.ay[m][1] = *reinterpret_cast<const u32x4 *>(row + K + 8);
+            }
+        }
+        const u32x4 *sp = reinterpret_cast<const u32x4 *>(scales + (size_t)g * N + word0 * 8);
+#pragma unroll
+        for (int x = 0; x < WORDS; ++x) {
+            const u32x4 t = sp[x];
+            d.sw[4 * x] = t.x; d.sw[4 * x + 1] = t.y; d.sw[4 * x + 2] = t.z; d.sw[4 * x + 3] = t.w;
+        }
+#pragma unroll
+        for (int x = 0; x < WORDS; ++x) d.zw.v[x] = 0u;
+        if (ASYM) d.zw = load_words<WORDS>(qzeros + (size_t)g * N8 + word0);
+        // keep the scale and zero requests ahead of the weight stream (the
+        // scheduler otherwise sinks them towards their late use)
+        __builtin_amdgcn_sched_barrier(0);
+        const uint32_t voff = ((uint32_t)k0 * (uint32_t)N8 + (uint32_t)word0) * 4u;
+#pragma unroll
+        for (int r = 0; r < kChunkRows; ++r) d.w[r] = buffer_words<WORDS>(brs, voff, (uint32_t)r * row_bytes);
+    };
+    auto compute_chunk = [&](const Chunk &d) __attribute__((always_inline)) {
         uint32_t av[M][8];
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             if constexpr (ACT == 0) {
-                const u32x4 *ap = reinterpret_cast<const u32x4 *>(a + (size_t)m * K + k0);
-                const u32x4 lo = ap[0], hi = ap[1];
-                av[m][0] = lo.x; av[m][1] = lo.y; av[m][2] = lo.z; av[m][3] = lo.w;
-                av[m][4] = hi.x; av[m][5] = hi.y; av[m][6] = hi.z; av[m][7] = hi.w;
-            } else {
-                const uint16_t *row = src + (size_t)m * ld + k0;
-                const float inv = s_inv[m];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const u32x4 x = *reinterpret_cast<const u32x4 *>(row + 8 * h);
-                    u32x4 y = x;
-                    if constexpr (ACT == 2) y = *reinterpret_cast<const u32x4 *>(row + K + 8 * h);
+                    av[m][4 * h] = d.ax[m][h].x; av[m][4 * h + 1] = d.ax[m][h].y;
+                    av[m][4 * h + 2] = d.ax[m][h].z; av[m][4 * h + 3] = d.ax[m][h].w;
+                }
+            } else {
+                const float inv = s_inv[m];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        av[m][4 * h + j] = (uint32_t)f32_to_f16_bits(act_value<ACT>(x, y, 2 * j) * inv) |
-                                           ((uint32_t)f32_to_f16_bits(act_value<ACT>(x, y, 2 * j + 1) * inv) << 16);
-                }
+                        av[m][4 * h + j] = scaled_f16(act_value<ACT>(d.ax[m][h], d.ay[m][h], 2 * j), inv) |
+                                           (scaled_f16(act_value<ACT>(d.ax[m][h], d.ay[m][h], 2 * j + 1), inv) << 16);
             }
         }
-        uint32_t sw[COLS / 2];
-        {
-            const u32x4 *sp = reinterpret_cast<const u32x4 *>(scales + (size_t)g * N + word0 * 8);
-#pragma unroll
-            for (int x = 0; x < WORDS; ++x) {
-                const u32x4 t = sp[x];
-                sw[4 * x] = t.x; sw[4 * x + 1] = t.y; sw[4 * x + 2] = t.z; sw[4 * x + 3] = t.w;
-            }
-        }
-        Words<WORDS> zw;
-#pragma unroll
-        for (int x = 0; x < WORDS; ++x) zw.v[x] = 0u;
-        if (ASYM) zw = load_words<WORDS>(qzeros + (size_t)g * N8 + word0);
-        Words<WORDS> w[kChunkRows];
-        const uint32_t voff = ((uint32_t)k0 * (uint32_t)N8 + (uint32_t)word0) * 4u;
-#pragma unroll
-        for (int r = 0; r < kChunkRows; ++r) w[r] = buffer_words<WORDS>(brs, voff, (uint32_t)r * row_bytes);
+        const uint32_t(&sw)[COLS / 2] = d.sw;
+        const Words<WORDS> &zw = d.zw;
+        const Words<WORDS>(&w)[kChunkRows] = d.w;
 
         f16x2 zc[COLS];
         if (!FOLD) {
@@ -346,6 +366,35 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
                 for (int m = 0; m < M; ++m) acc[m][j] = __builtin_fmaf(s, p[m][j], acc[m][j]);
             }
         }
+    };
+
+    const int c0 = c_begin + wave * RL + rl;
+    constexpr int kStride = NW * RL;
+    if constexpr (ACT != 0) {
+        static_assert(NW == 8, "the row sums map 1024 virtual threads onto 512");
+        float ss[M][2];
+        const int nvec = K / 8;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const uint16_t *row = src + (size_t)m * ld;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                float t = 0.f;
+                for (int i = (int)threadIdx.x + 512 * h; i < nvec; i += 1024) {
+                    const u32x4 x = *reinterpret_cast<const u32x4 *>(row + 8 * i);
+                    u32x4 y = x;
+                    if constexpr (ACT == 2) y = *reinterpret_cast<const u32x4 *>(row + K + 8 * i);
+                    t = sq_chain<ACT>(x, y, t);
+                }
+                ss[m][h] = t;
+            }
+        }
+        row_scales<M>(ss, K, s_part, s_inv);
+    }
+    for (int c = c0; c < c_end; c += kStride) {
+        Chunk d;
+        load_chunk(c, d);
+        compute_chunk(d);
     }
 
     // Transpose-reduce over the row lanes (lane bits 5 .. log2(CL)): after the
@@ -437,26 +486,28 @@ hipError_t launch_k(const GemmArgs &g, const GemmPlan &p, const uint16_t *src, i
     return hipGetLastError();
 }
 
-template <int M, int WORDS, int NW, int ACT>
-hipError_t launch_v(const GemmArgs &g, const GemmPlan &p, const uint16_t *src, int ld, hipStream_t stream) {
-    // With the glue transform in the activation loads the folded form costs
-    // more registers than it saves VALU work (measured on MI355X): exact form.
-    if (ACT != 0)
-        return g.qzeros ? launch_k<M, WORDS, NW, true, false, ACT>(g, p, src, ld, stream)
-                        : launch_k<M, WORDS, NW, false, false, ACT>(g, p, src, ld, stream);
+// Glue-fused variants: exact dequantisation form (the folded one costs these
+// more registers than it saves VALU work, measured on MI355X).
+template <int M, int WORDS, int ACT>
+hipError_t launch_act(const GemmArgs &g, const GemmPlan &p, const uint16_t *src, int ld, hipStream_t stream) {
+    return g.qzeros ? launch_k<M, WORDS, 8, true, false, ACT>(g, p, src, ld, stream)
+                    : launch_k<M, WORDS, 8, false, false, ACT>(g, p, src, ld, stream);
+}
+
+template <int M, int WORDS, int NW>
+hipError_t launch_v(const GemmArgs &g, const GemmPlan &p, hipStream_t stream) {
     if (g.qzeros)
-        return p.fold_asym ? launch_k<M, WORDS, NW, true, true, ACT>(g, p, src, ld, stream)
-                           : launch_k<M, WORDS, NW, true, false, ACT>(g, p, src, ld, stream);
-    return p.fold ? launch_k<M, WORDS, NW, false, true, ACT>(g, p, src, ld, stream)
-                  : launch_k<M, WORDS, NW, false, false, ACT>(g, p, src, ld, stream);
+        return p.fold_asym ? launch_k<M, WORDS, NW, true, true, 0>(g, p, nullptr, 0, stream)
+                           : launch_k<M, WORDS, NW, true, false, 0>(g, p, nullptr, 0, stream);
+    return p.fold ? launch_k<M, WORDS, NW, false, true, 0>(g, p, nullptr, 0, stream)
+                  : launch_k<M, WORDS, NW, false, false, 0>(g, p, nullptr, 0, stream);
 }
 
 template <int M, int WORDS>
 hipError_t launch_m(const GemmArgs &g, const GemmPlan &p, int act, const uint16_t *src, int ld, hipStream_t stream) {
-    if (act == 1) return launch_v<M, WORDS, 8, 1>(g, p, src, ld, stream);
-    if (act == 2) return launch_v<M, WORDS, 8, 2>(g, p, src, ld, stream);
-    return p.waves == 8 ? launch_v<M, WORDS, 8, 0>(g, p, src, ld, stream)
-                        : launch_v<M, WORDS, 4, 0>(g, p, src, ld, stream);
+    if (act == 1) return launch_act<M, WORDS, 1>(g, p, src, ld, stream);
+    if (act == 2) return launch_act<M, WORDS, 2>(g, p, src, ld, stream);
+    return p.waves == 8 ? launch_v<M, WORDS, 8>(g, p, stream) : launch_v<M, WORDS, 4>(g, p, stream);
 }
 
 }  // namespace
@@ -468,7 +519,8 @@ hipError_t launch_gemv(const GemmArgs &g, const GemmPlan &p, hipStream_t stream)
 hipError_t launch_gemv_act(const GemmArgs &g, const GemmPlan &p, int act, const uint16_t *src, int64_t ld,
                            hipStream_t stream) {
     if (p.splits > kMaxSplits) return hipErrorInvalidValue;
-    if (act != 0 && (p.waves != 8 || !src || ld % 8 != 0 || g.K % 8 != 0)) return hipErrorInvalidValue;
+    if (act != 0 && (p.waves != 8 || !src || ld % 8 != 0 || g.K % 8 != 0 || g.K > kGlueMaxWidth))
+        return hipErrorInvalidValue;
     switch (g.M) {
         case 1: return launch_m<1, 4>(g, p, act, src, (int)ld, stream);
         case 2: return launch_m<2, 4>(g, p, act, src, (int)ld, stream);

@@ -42,8 +42,7 @@ __device__ __forceinline__ u32x4 load16(const uint16_t *p) { return *reinterpret
 __device__ __forceinline__ void store_scaled(uint16_t *p, const float (&t)[8], float inv) {
     u32x4 o;
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
-        o[w] = (uint32_t)f32_to_f16_bits(t[2 * w] * inv) | ((uint32_t)f32_to_f16_bits(t[2 * w + 1] * inv) << 16);
+    for (int w = 0; w < 4; ++w) o[w] = scaled_f16(t[2 * w], inv) | (scaled_f16(t[2 * w + 1], inv) << 16);
     *reinterpret_cast<u32x4 *>(p) = o;
 }
 
@@ -71,7 +70,7 @@ __global__ __launch_bounds__(kThreads) void rownorm_kernel(const uint16_t *__res
             ss = __builtin_fmaf(t[j][e], t[j][e], ss);
         }
     const float tot = block_sum(ss, sh);
-    const float inv = 1.0f / sqrtf(tot / (float)width + 1e-6f);
+    const float inv = row_inv(tot, width);
     uint16_t *yr = y + (size_t)blockIdx.x * width;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
@@ -79,8 +78,6 @@ __global__ __launch_bounds__(kThreads) void rownorm_kernel(const uint16_t *__res
         if (i < nvec) store_scaled(yr + 8 * i, t[j], inv);
     }
 }
-
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
 // y[m][i] = rn_row(silu(gu[m][i]) * gu[m][I + i]), gu is [M, 2I]; same
 // vector layout as rownorm_kernel over the I outputs.
@@ -108,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_rownorm_kernel(const uint16_t
             ss = __builtin_fmaf(t[j][e], t[j][e], ss);
         }
     const float tot = block_sum(ss, sh);
-    const float inv = 1.0f / sqrtf(tot / (float)I + 1e-6f);
+    const float inv = row_inv(tot, I);
     uint16_t *yr = y + (size_t)blockIdx.x * I;
 #pragma unroll
     for (int j = 0; j < V; ++j) {

@@ -51,7 +51,9 @@ hipError_t launch_gemv(const GemmArgs &args, const GemmPlan &plan, hipStream_t s
 // glue folded in): act 1: a = fp16(src * inv_row), act 2: a = fp16(silu(g) *
 // u * inv_row) with g = src[:, :K], u = src[:, K:2K]; inv_row =
 // 1/sqrt(mean(v^2) + 1e-6) over the transformed row; src rows ld elements
-// apart (ld and K multiples of 8).  Needs plan.waves == 8.
+// apart (ld and K multiples of 8, K <= kGlueMaxWidth).  Needs plan.waves == 8.
+// The row scale is computed in the same order as launch_rownorm /
+// launch_swiglu_rownorm, so the activations match theirs bit for bit.
 hipError_t launch_gemv_act(const GemmArgs &args, const GemmPlan &plan, int act, const uint16_t *src,
                            int64_t ld, hipStream_t stream);
 hipError_t launch_mfma(const GemmArgs &args, const GemmPlan &plan, hipStream_t stream);
