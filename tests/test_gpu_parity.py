@@ -87,7 +87,8 @@ def small_cases():
     cases += [(1, 256, 264, 64, True), (7, 384, 8, 128, False),  # N % 32 != 0 at small M
               (40, 2048, 1024, 2048, True), (256, 1280, 512, 128, True),
               (96, 96, 256, 32, True),     # large-M kernel: K-groups with no steps
-              (72, 160, 136, 32, False)]   # large-M kernel: ragged rows and columns
+              (72, 160, 136, 32, False),   # large-M kernel: ragged rows and columns
+              (128, 2048, 1024, 128, True), (200, 1024, 392, 64, False)]  # 64-row tiles, 128-column shape
     return cases
 
 
@@ -102,7 +103,8 @@ def test_gemm_matches_oracle(M, K, N, G, asym):
 
 
 TUNED_FORMS = ["gemv_fold=0", "gemv_fold=1", "gemv_waves=4", "gemv_waves=4,gemv_fold=1",
-               "gemv_splits=1", "gemv_splits=7", "gemv_max_m=0", "mfma_cfg=4", "mfma_cfg=5,mfma_splits=3"]
+               "gemv_splits=1", "gemv_splits=7", "gemv_max_m=0", "mfma_cfg=4", "mfma_cfg=5,mfma_splits=3",
+               "mfma_cfg=3", "mfma_cfg=6", "mfma_cfg=6,mfma_splits=3"]
 
 
 @pytest.mark.parametrize("spec", TUNED_FORMS)

@@ -58,7 +58,7 @@ struct Tune {
     int64_t gemv_max_m = 8;            // largest M sent to the GEMV path (at most 8)
     int64_t mfma_target_waves = 2048;  // aim for about this many MFMA-path waves
     int64_t mfma_splits = 0;           // force the MFMA split count
-    int64_t mfma_cfg = 0;  // force (mt, waves, kwaves): 1..5 = (1,2,4) (2,2,4) (4,2,2) (2,1,8) (4,2,4)
+    int64_t mfma_cfg = 0;  // force (mt, waves, kwaves): 1..6 = (1,2,4) (2,2,4) (4,2,2) (2,1,8) (4,2,4) (4,1,8)
     int64_t max_partial_bytes = 64ll << 20;
     int64_t decode_fuse = 1;           // 0: decode-step glue as separate kernels
 };
@@ -171,9 +171,7 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G) {
         // (the last workgroup of a tile sums the splits' fp32 partials).
         // Measured on MI355X: at M = 32 the 128-column, 8-K-wave shape beats
         // 256-column tiles on the 8B-class decode shapes (fewer splits, less
-        // partial traffic).  Above M = 32, 64-row wave tiles with 2 or 4
-        // K-waves per workgroup: 4 (two waves per SIMD) wherever that needs
-        // fewer K-splits, since partial traffic is what the split count costs.
+        // partial traffic).  Above M = 32, 64-row wave tiles (below).
         p.path = kPathMfma;
         auto fill = [&](int mt, int waves, int kwaves) {
             p.mt = mt;
@@ -196,18 +194,41 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G) {
             p.split_len = cdiv(nsteps, splits);
             p.splits = (int)cdiv(nsteps, p.split_len);
         };
-        static const int kCfg[5][3] = {{1, 2, 4}, {2, 2, 4}, {4, 2, 2}, {2, 1, 8}, {4, 2, 4}};
-        if (t.mfma_cfg >= 1 && t.mfma_cfg <= 5) {
+        static const int kCfg[6][3] = {{1, 2, 4}, {2, 2, 4}, {4, 2, 2}, {2, 1, 8}, {4, 2, 4}, {4, 1, 8}};
+        if (t.mfma_cfg >= 1 && t.mfma_cfg <= 6) {
             fill(kCfg[t.mfma_cfg - 1][0], kCfg[t.mfma_cfg - 1][1], kCfg[t.mfma_cfg - 1][2]);
         } else if (M <= 16) {
             fill(1, 2, 4);
         } else if (M <= 32) {
             fill(2, 1, 8);
         } else {
-            fill(4, 2, 4);
-            const int s4 = p.splits;
-            fill(4, 2, 2);
-            if (s4 < p.splits) fill(4, 2, 4);
+            // 64-row wave tiles: 256 columns with 2 or 4 K-waves, or 128 columns
+            // with 8 K-waves (twice the tiles, so half the K-splits, or a full
+            // chip where 256-column tiles leave CUs idle).  Measured on MI355X:
+            // prefer the shape that keeps the most CUs busy per round of
+            // workgroups, then the fewest K-splits (split partials go through
+            // memory), then the fewest workgroups.
+            static const int kBig[3][3] = {{4, 2, 2}, {4, 2, 4}, {4, 1, 8}};
+            int best = -1;
+            double best_eff = -1;
+            int best_splits = 0;
+            int64_t best_grid = 0;
+            for (int c = 0; c < 3; ++c) {
+                fill(kBig[c][0], kBig[c][1], kBig[c][2]);
+                const int64_t grid = p.tiles_n * p.tiles_m * p.splits;
+                const int64_t rounds = cdiv(grid, 256);
+                const double eff = (double)grid / (double)(rounds * 256);
+                const bool better = best < 0 || eff > best_eff + 1e-9 ||
+                                    (eff > best_eff - 1e-9 && (p.splits < best_splits ||
+                                                               (p.splits == best_splits && grid < best_grid)));
+                if (better) {
+                    best = c;
+                    best_eff = eff;
+                    best_splits = p.splits;
+                    best_grid = grid;
+                }
+            }
+            fill(kBig[best][0], kBig[best][1], kBig[best][2]);
         }
     }
     p.grid = p.tiles_n * p.tiles_m * p.splits;

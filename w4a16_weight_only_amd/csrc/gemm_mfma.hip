@@ -93,7 +93,7 @@ struct Gcd<A, 0> : std::integral_constant<int, A> {};
 // flight.  (A third A slot measured no faster at MT = 4.)
 // Two B slots where eight waves of 64-row tiles share a CU (256 VGPRs each).
 template <int MT, int NWK>
-struct RingW : std::integral_constant<int, (MT == 4 && NWK == 4) ? 2 : 4> {};
+struct RingW : std::integral_constant<int, (MT == 4 && NWK >= 4) ? 2 : 4> {};
 template <int MT>
 struct RingA : std::integral_constant<int, 2> {};
 
@@ -492,6 +492,7 @@ int mfma_max_splits(int mt, int waves, int kwaves) {
     if (mt == 4 && waves == 2 && kwaves == 2) return Cfg<4, 2, 2>::kMaxSplits;
     if (mt == 2 && waves == 1 && kwaves == 8) return Cfg<2, 1, 8>::kMaxSplits;
     if (mt == 4 && waves == 2 && kwaves == 4) return Cfg<4, 2, 4>::kMaxSplits;
+    if (mt == 4 && waves == 1 && kwaves == 8) return Cfg<4, 1, 8>::kMaxSplits;
     return 1;
 }
 
@@ -502,6 +503,7 @@ hipError_t launch_mfma(const GemmArgs &g, const GemmPlan &p, hipStream_t stream)
     if (p.mt == 4 && p.waves == 2 && p.kwaves == 2) return launch_cfg<4, 2, 2>(g, p, stream);
     if (p.mt == 2 && p.waves == 1 && p.kwaves == 8) return launch_cfg<2, 1, 8>(g, p, stream);
     if (p.mt == 4 && p.waves == 2 && p.kwaves == 4) return launch_cfg<4, 2, 4>(g, p, stream);
+    if (p.mt == 4 && p.waves == 1 && p.kwaves == 8) return launch_cfg<4, 1, 8>(g, p, stream);
     return hipErrorInvalidValue;
 }
 
