@@ -277,10 +277,11 @@ def dev_stack(layers):
 def test_decode_step_small_stack(M):
     """Teacher-forced per layer: the oracle's layer l is fed the GPU's own input
     to layer l, so each comparison covers one layer (four chained linears) at
-    the per-element bound.  The multi-layer call must equal the chained
-    single-layer calls bit for bit, and the end-to-end drift against the
-    oracle's own chain (fp16 rounding differences compound) is reported and
-    bounded by relative L2 <= 1e-2."""
+    the per-element bound.  The multi-layer call matches the chained
+    single-layer calls to relative L2 <= 1e-2 (at M <= 8 it applies each
+    layer's output row-norm inside the next layer's QKV, one fp16 rounding
+    fewer, and rounding differences compound over layers), and so does the
+    end-to-end drift against the oracle's own chain."""
     H, NQ, I, G, nl = 256, 384, 512, 64, 3
     layers = []
     for l in range(nl):
@@ -294,7 +295,10 @@ def test_decode_step_small_stack(M):
         want = oracle.decode_step(layers[4 * l: 4 * l + 4], host(cur), 1)
         check_close(host(y), want, "decode small M=%d layer %d" % (M, l))
         cur = y
-    assert np.array_equal(host(cur).view(np.uint16), full.view(np.uint16))
+    chained = host(cur).astype(np.float64)
+    rel = np.linalg.norm(full.astype(np.float64) - chained) / np.linalg.norm(chained)
+    note("decode small M=%d n-layer vs chained relative L2 %.3g" % (M, rel))
+    assert rel < 1e-2
     e2e = oracle.decode_step(layers, x, nl).astype(np.float64)
     rel = np.linalg.norm(full.astype(np.float64) - e2e) / np.linalg.norm(e2e)
     note("decode small M=%d end-to-end relative L2 drift %.3g" % (M, rel))
@@ -303,13 +307,14 @@ def test_decode_step_small_stack(M):
 
 @pytest.mark.parametrize("M", [1, 2, 5])
 @pytest.mark.parametrize("H,NQ,I", [(256, 384, 512), (512, 768, 9216), (512, 512, 17408)])
-def test_decode_step_fused_equals_unfused(M, H, NQ, I):
-    """At M <= 8 the row-norm and SwiGLU glue runs inside the consuming GEMVs'
-    activation loads, and a layer's output row-norm inside the next layer's
-    QKV.  The GEMV computes each row scale in the standalone glue kernels' own
-    summation order, so the step equals the unfused one (separate glue
-    kernels, forced with decode_fuse=0) bit for bit.  Row widths up to 17408
-    cover one, two and four 8-element vectors per virtual thread."""
+def test_decode_step_fused_matches_unfused(M, H, NQ, I):
+    """At M <= 8 the row-norm and SwiGLU glue runs inside the consuming GEMVs
+    (the row scale applied to the products) and a layer's output row-norm
+    inside the next layer's QKV.  One layer matches the unfused step
+    (separate glue kernels, forced with decode_fuse=0) and the oracle at the
+    per-element bound; two layers (the cross-layer fold) match the unfused
+    step to relative L2 <= 1e-2.  Row widths up to 17408 cover one, two and
+    four 8-element vectors per virtual thread of the row sums."""
     G, nl = 128, 2
     layers = []
     for l in range(nl):
@@ -323,9 +328,17 @@ def test_decode_step_fused_equals_unfused(M, H, NQ, I):
         unfused = host(w4.w4a16_decode_step(dstack, x))
     finally:
         w4.w4a16_set_tuning(None)
-    assert np.array_equal(fused.view(np.uint16), unfused.view(np.uint16))
-    want = oracle.decode_step(layers[:4], host(x), 1)
+    rel = np.linalg.norm(fused.astype(np.float64) - unfused) / np.linalg.norm(unfused.astype(np.float64))
+    note("decode fused vs unfused M=%d I=%d two layers relative L2 %.3g" % (M, I, rel))
+    assert rel < 1e-2
     first = host(w4.w4a16_decode_step(dstack[:4], x))
+    try:
+        w4.w4a16_set_tuning("decode_fuse=0")
+        first_unfused = host(w4.w4a16_decode_step(dstack[:4], x))
+    finally:
+        w4.w4a16_set_tuning(None)
+    check_close(first, first_unfused, "fused vs unfused layer 0 M=%d I=%d" % (M, I))
+    want = oracle.decode_step(layers[:4], host(x), 1)
     check_close(first, want, "fused layer 0 M=%d I=%d" % (M, I))
 
 

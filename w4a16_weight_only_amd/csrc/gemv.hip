@@ -145,30 +145,7 @@ __device__ __forceinline__ float sq_chain(const u32x4 &x, const u32x4 &y, float 
     return ss;
 }
 
-template <int M>
-__device__ __forceinline__ void row_scales(const float (&ss)[M][2], int K, float (&s_part)[16][M],
-                                           float (&s_inv)[M]) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            float v = ss[m][h];
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-            if (lane == 0) s_part[8 * h + wave][m] = v;
-        }
-    __syncthreads();
-    if (threadIdx.x < M) {
-        float t = 0.f;
-#pragma unroll
-        for (int w = 0; w < 16; ++w) t += s_part[w][threadIdx.x];
-        s_inv[threadIdx.x] = row_inv(t, K);
-    }
-    __syncthreads();
-}
-
-template <int M, int WORDS, int NW, bool ASYM, bool FOLD, int ACT>
+template <int M, int WORDS, int NW, bool ASYM, bool FOLD, int ACT, int RV>
 __global__ __launch_bounds__(64 * NW) void gemv_kernel(
     const uint16_t *__restrict__ a, const uint16_t *__restrict__ src, int ld, const uint32_t *__restrict__ b,
     const uint16_t *__restrict__ scales, const uint32_t *__restrict__ qzeros, int K, int N, int G,
@@ -204,13 +181,37 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
 #pragma unroll
         for (int j = 0; j < COLS; ++j) acc[m][j] = 0.f;
 
-    // Activation transform (ACT != 0): the rows' scales come first, before
-    // the weight stream starts.  (Issuing the weights first and summing the
-    // rows while they are in flight measured slower on MI355X: the
-    // workgroup barrier then waits for every wave's back-pressured weight
-    // requests.)
-    __shared__ float s_inv[M];
+    // Glue transform (ACT != 0).  The row-norm is a per-row scalar, so it is
+    // applied to the products in the epilogue: the GEMV takes the raw row
+    // (ACT 1) or fp16(silu(g) * u) (ACT 2) and each output is multiplied by
+    // its row's 1/sqrt(mean(t^2) + 1e-6).  The row sums run off the weight
+    // stream's critical path: at M <= 2 the row's vectors are requested
+    // before the weights (loads complete in issue order, so they never wait
+    // for the weight stream), are summed while the first weights are in
+    // flight, and meet at the epilogue's barrier.  (Summing the rows before the weight stream
+    // starts costs an L2 round trip and two barriers per launch.)
     __shared__ float s_part[16][M];
+    constexpr bool kEarlyRows = ACT != 0 && M <= 2;
+    constexpr int kRM = kEarlyRows ? M : 1, kRV = kEarlyRows ? RV : 1;
+    u32x4 rx[kRM][2][kRV], ry[kRM][2][kRV];
+    if constexpr (kEarlyRows) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const __amdgpu_buffer_rsrc_t gr = buffer_rsrc(src + (size_t)m * ld, (uint32_t)K * 2u);
+            const __amdgpu_buffer_rsrc_t ur = buffer_rsrc(src + (size_t)m * ld + K, ACT == 2 ? (uint32_t)K * 2u : 0u);
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int j = 0; j < RV; ++j) {
+                    // a vector past the row reads zeros (adds exactly 0)
+                    const uint32_t off = ((uint32_t)threadIdx.x + 512u * h + 1024u * j) * 16u;
+                    rx[m][h][j] = buffer_load_x4(gr, off, 0);
+                    ry[m][h][j] = rx[m][h][j];
+                    if constexpr (ACT == 2) ry[m][h][j] = buffer_load_x4(ur, off, 0);
+                }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
 
     struct Chunk {
         u32x4 ax[M][2], ay[M][2];  // raw activations (ACT 2: gate in ax, up in ay)
@@ -253,20 +254,20 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
         uint32_t av[M][8];
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            if constexpr (ACT == 0) {
+            if constexpr (ACT != 2) {
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     av[m][4 * h] = d.ax[m][h].x; av[m][4 * h + 1] = d.ax[m][h].y;
                     av[m][4 * h + 2] = d.ax[m][h].z; av[m][4 * h + 3] = d.ax[m][h].w;
                 }
             } else {
-                const float inv = s_inv[m];
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        av[m][4 * h + j] = scaled_f16(act_value<ACT>(d.ax[m][h], d.ay[m][h], 2 * j), inv) |
-                                           (scaled_f16(act_value<ACT>(d.ax[m][h], d.ay[m][h], 2 * j + 1), inv) << 16);
+                        av[m][4 * h + j] =
+                            (uint32_t)f32_to_f16_bits(act_value<2>(d.ax[m][h], d.ay[m][h], 2 * j)) |
+                            ((uint32_t)f32_to_f16_bits(act_value<2>(d.ax[m][h], d.ay[m][h], 2 * j + 1)) << 16);
             }
         }
         const uint32_t(&sw)[COLS / 2] = d.sw;
@@ -370,31 +371,70 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
 
     const int c0 = c_begin + wave * RL + rl;
     constexpr int kStride = NW * RL;
-    if constexpr (ACT != 0) {
-        static_assert(NW == 8, "the row sums map 1024 virtual threads onto 512");
-        float ss[M][2];
-        const int nvec = K / 8;
+    // Row sums of squares of the transformed rows (the glue kernels' order:
+    // 1024 virtual threads, two chains per thread of the 512), reduced per
+    // wave here and across waves in the epilogue.  With the row held in
+    // registers (M <= 2) they are computed while the first chunk's weights
+    // are in flight; otherwise after the chunk loop.
+    auto row_sums = [&]() __attribute__((always_inline)) {
+        if constexpr (ACT != 0) {
+            static_assert(NW == 8, "the row sums map 1024 virtual threads onto 512");
+            float ss[M][2];
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const uint16_t *row = src + (size_t)m * ld;
+            for (int m = 0; m < M; ++m)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                float t = 0.f;
-                for (int i = (int)threadIdx.x + 512 * h; i < nvec; i += 1024) {
-                    const u32x4 x = *reinterpret_cast<const u32x4 *>(row + 8 * i);
-                    u32x4 y = x;
-                    if constexpr (ACT == 2) y = *reinterpret_cast<const u32x4 *>(row + K + 8 * i);
-                    t = sq_chain<ACT>(x, y, t);
+                for (int h = 0; h < 2; ++h) {
+                    float t = 0.f;
+                    if constexpr (kEarlyRows) {
+#pragma unroll
+                        for (int j = 0; j < RV; ++j) t = sq_chain<ACT>(rx[m][h][j], ry[m][h][j], t);
+                    } else {
+                        const uint16_t *row = src + (size_t)m * ld;
+                        for (int i = (int)threadIdx.x + 512 * h; i < K / 8; i += 1024) {
+                            const u32x4 x = *reinterpret_cast<const u32x4 *>(row + 8 * i);
+                            u32x4 y = x;
+                            if constexpr (ACT == 2) y = *reinterpret_cast<const u32x4 *>(row + K + 8 * i);
+                            t = sq_chain<ACT>(x, y, t);
+                        }
+                    }
+                    ss[m][h] = t;
                 }
-                ss[m][h] = t;
-            }
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    float v = ss[m][h];
+#pragma unroll
+                    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+                    if (lane == 0) s_part[8 * h + wave][m] = v;
+                }
         }
-        row_scales<M>(ss, K, s_part, s_inv);
-    }
-    for (int c = c0; c < c_end; c += kStride) {
-        Chunk d;
-        load_chunk(c, d);
-        compute_chunk(d);
+    };
+
+    if constexpr (kEarlyRows) {
+        // first chunk peeled: its weights are requested, then the row sums
+        // run on the row vectors (requested earlier, so already waited for
+        // without waiting for the weights)
+        if (c0 < c_end) {
+            Chunk d;
+            load_chunk(c0, d);
+            row_sums();
+            compute_chunk(d);
+        } else {
+            row_sums();
+        }
+        for (int c = c0 + kStride; c < c_end; c += kStride) {
+            Chunk d;
+            load_chunk(c, d);
+            compute_chunk(d);
+        }
+    } else {
+        for (int c = c0; c < c_end; c += kStride) {
+            Chunk d;
+            load_chunk(c, d);
+            compute_chunk(d);
+        }
+        row_sums();
     }
 
     // Transpose-reduce over the row lanes (lane bits 5 .. log2(CL)): after the
@@ -440,6 +480,12 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
         if (t < M * kTileCols) {
 #pragma unroll
             for (int wv = 0; wv < NW; ++wv) s += red[wv][t / kTileCols][t % kTileCols];
+            if constexpr (ACT != 0) {
+                float q = 0.f;
+#pragma unroll
+                for (int w = 0; w < 16; ++w) q += s_part[w][t / kTileCols];
+                s *= row_inv(q, K);
+            }
         }
         sums[i] = s;
     }
@@ -477,21 +523,29 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
     }
 }
 
-template <int M, int WORDS, int NW, bool ASYM, bool FOLD, int ACT>
+template <int M, int WORDS, int NW, bool ASYM, bool FOLD, int ACT, int RV = 1>
 hipError_t launch_k(const GemmArgs &g, const GemmPlan &p, const uint16_t *src, int ld, hipStream_t stream) {
-    hipLaunchKernelGGL((gemv_kernel<M, WORDS, NW, ASYM, FOLD, ACT>), dim3((unsigned)p.grid), dim3(64 * NW), 0, stream,
-                       g.a, src, ld, reinterpret_cast<const uint32_t *>(g.b), g.scales,
+    hipLaunchKernelGGL((gemv_kernel<M, WORDS, NW, ASYM, FOLD, ACT, RV>), dim3((unsigned)p.grid), dim3(64 * NW), 0,
+                       stream, g.a, src, ld, reinterpret_cast<const uint32_t *>(g.b), g.scales,
                        reinterpret_cast<const uint32_t *>(g.qzeros), (int)g.K, (int)g.N, (int)g.G, (uint32_t)g.zp,
                        (int)p.tiles_n, (int)p.split_len, p.splits, g.out, g.counters);
     return hipGetLastError();
 }
 
-// Glue-fused variants: exact dequantisation form (the folded one costs these
-// more registers than it saves VALU work, measured on MI355X).
+// Glue-fused variants: exact dequantisation form.  At M <= 2 the row's
+// vectors are held in registers from the start: RV per virtual thread, the
+// glue kernels' own count for a row of K values.
 template <int M, int WORDS, int ACT>
 hipError_t launch_act(const GemmArgs &g, const GemmPlan &p, const uint16_t *src, int ld, hipStream_t stream) {
-    return g.qzeros ? launch_k<M, WORDS, 8, true, false, ACT>(g, p, src, ld, stream)
-                    : launch_k<M, WORDS, 8, false, false, ACT>(g, p, src, ld, stream);
+    const int64_t per = (g.K / 8 + 1023) / 1024;
+    if (M <= 2 && per > 2)
+        return g.qzeros ? launch_k<M, WORDS, 8, true, false, ACT, 4>(g, p, src, ld, stream)
+                        : launch_k<M, WORDS, 8, false, false, ACT, 4>(g, p, src, ld, stream);
+    if (M <= 2 && per > 1)
+        return g.qzeros ? launch_k<M, WORDS, 8, true, false, ACT, 2>(g, p, src, ld, stream)
+                        : launch_k<M, WORDS, 8, false, false, ACT, 2>(g, p, src, ld, stream);
+    return g.qzeros ? launch_k<M, WORDS, 8, true, false, ACT, 1>(g, p, src, ld, stream)
+                    : launch_k<M, WORDS, 8, false, false, ACT, 1>(g, p, src, ld, stream);
 }
 
 template <int M, int WORDS, int NW>

@@ -47,13 +47,14 @@ struct GemmArgs {
 GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G);
 
 hipError_t launch_gemv(const GemmArgs &args, const GemmPlan &plan, hipStream_t stream);
-// GEMV whose activations are transformed as they are loaded (decode-step
-// glue folded in): act 1: a = fp16(src * inv_row), act 2: a = fp16(silu(g) *
-// u * inv_row) with g = src[:, :K], u = src[:, K:2K]; inv_row =
-// 1/sqrt(mean(v^2) + 1e-6) over the transformed row; src rows ld elements
-// apart (ld and K multiples of 8, K <= kGlueMaxWidth).  Needs plan.waves == 8.
-// The row scale is computed in the same order as launch_rownorm /
-// launch_swiglu_rownorm, so the activations match theirs bit for bit.
+// GEMV with the decode step's glue folded in: act 1: out = (src . W) * inv_row,
+// act 2: out = (fp16(silu(g) * u) . W) * inv_row with g = src[:, :K],
+// u = src[:, K:2K]; inv_row = 1/sqrt(mean(t^2) + 1e-6) over the row's
+// transformed values t (summed in the glue kernels' order).  The row scale is
+// applied to the products, so the normalised activations are not rounded to
+// fp16 on their own (one rounding fewer than the separate glue kernels).
+// src rows ld elements apart (ld and K multiples of 8, K <= kGlueMaxWidth).
+// Needs plan.waves == 8.
 hipError_t launch_gemv_act(const GemmArgs &args, const GemmPlan &plan, int act, const uint16_t *src,
                            int64_t ld, hipStream_t stream);
 hipError_t launch_mfma(const GemmArgs &args, const GemmPlan &plan, hipStream_t stream);
