@@ -43,11 +43,11 @@ def host(t):
     return t.cpu().numpy()
 
 
-def check_close(got, want, what=""):
+def check_close(got, want, what="", tol=TOL):
     g = got.astype(np.float64)
     r = want.astype(np.float64)
     err = np.abs(g - r)
-    bound = TOL * np.maximum(1.0, np.abs(r))
+    bound = tol * np.maximum(1.0, np.abs(r))
     worst = np.unravel_index(np.argmax(err / bound), err.shape) if err.size else None
     ulp = np.abs(got.view(np.uint16).astype(np.int64) - want.view(np.uint16).astype(np.int64))
     note("%s max|err|=%.3g max ulp=%d" % (what, err.max() if err.size else 0, ulp.max() if ulp.size else 0))
@@ -293,7 +293,7 @@ def test_decode_step_small_stack(M):
     for l in range(nl):
         y = w4.w4a16_decode_step(dstack[4 * l: 4 * l + 4], cur)
         want = oracle.decode_step(layers[4 * l: 4 * l + 4], host(cur), 1)
-        check_close(host(y), want, "decode small M=%d layer %d" % (M, l))
+        check_close(host(y), want, "decode small M=%d layer %d" % (M, l), tol=FUSED_LAYER_TOL)
         cur = y
     chained = host(cur).astype(np.float64)
     rel = np.linalg.norm(full.astype(np.float64) - chained) / np.linalg.norm(chained)
@@ -305,12 +305,13 @@ def test_decode_step_small_stack(M):
     assert rel < 1e-2
 
 
-@pytest.mark.parametrize("M", [1, 2, 5])
+@pytest.mark.parametrize("M", [1, 2, 5, 12, 24])
 @pytest.mark.parametrize("H,NQ,I", [(256, 384, 512), (512, 768, 9216), (512, 512, 17408)])
 def test_decode_step_fused_matches_unfused(M, H, NQ, I):
     """At M <= 8 the row-norm and SwiGLU glue runs inside the consuming GEMVs
     (the row scale applied to the products) and a layer's output row-norm
-    inside the next layer's QKV.  One layer matches the unfused step
+    inside the next layer's QKV; at M >= 9 the row-norms run inside the
+    consuming MFMA GEMMs the same way (SwiGLU stays a kernel).  One layer matches the unfused step
     (separate glue kernels, forced with decode_fuse=0) and the oracle at the
     per-element bound; two layers (the cross-layer fold) match the unfused
     step to relative L2 <= 1e-2.  Row widths up to 17408 cover one, two and
@@ -337,21 +338,40 @@ def test_decode_step_fused_matches_unfused(M, H, NQ, I):
         first_unfused = host(w4.w4a16_decode_step(dstack[:4], x))
     finally:
         w4.w4a16_set_tuning(None)
-    check_close(first, first_unfused, "fused vs unfused layer 0 M=%d I=%d" % (M, I))
+    check_close(first, first_unfused, "fused vs unfused layer 0 M=%d I=%d" % (M, I), tol=FUSED_LAYER_TOL)
     want = oracle.decode_step(layers[:4], host(x), 1)
-    check_close(first, want, "fused layer 0 M=%d I=%d" % (M, I))
+    check_close(first, want, "fused layer 0 M=%d I=%d" % (M, I), tol=FUSED_LAYER_TOL)
 
 
-@pytest.mark.parametrize("M", [1, 16])
+# A decode layer chains four linears and the glue.  With every glue step a
+# kernel of its own, the GPU takes the oracle's roundings (fp16 after each GEMM
+# and each glue step) and one layer stays within the single-GEMM bound.  The
+# fused routes apply each row-norm to the products and so skip the fp16
+# rounding of the normalised activations that the oracle takes; that adds up
+# to about 0.004 per element on the 8B-class layer (measured), where the MFMA
+# path's fp16 weight operands already use about 0.007 of the 0.01.  The bound
+# for a fused layer is twice the single-GEMM bound.
+FUSED_LAYER_TOL = 2 * TOL
+
+
+@pytest.mark.parametrize("M", [1, 16, 32])
 def test_decode_step_one_real_layer(M):
     """One layer at the 8B-class shapes (QKV 4096->6144, O, gate+up
-    4096->25600, down 12800->4096), same launch plans as the full stack."""
+    4096->25600, down 12800->4096), same launch plans as the full stack: the
+    separate-kernel route within the single-GEMM bound, the fused route (the
+    default) within the fused-layer bound."""
     layers = synth.stack_layer(0)
     x = synth.stack_input(M)
     note("decode real layer M=%d" % M)
-    got = host(w4.w4a16_decode_step(dev_stack(layers), dev(x)))
     want = oracle.decode_step(layers, x, 1)
-    check_close(got, want, "decode real M=%d" % M)
+    got = host(w4.w4a16_decode_step(dev_stack(layers), dev(x)))
+    check_close(got, want, "decode real fused M=%d" % M, tol=FUSED_LAYER_TOL)
+    try:
+        w4.w4a16_set_tuning("decode_fuse=0")
+        sep = host(w4.w4a16_decode_step(dev_stack(layers), dev(x)))
+    finally:
+        w4.w4a16_set_tuning(None)
+    check_close(sep, want, "decode real separate M=%d" % M)
 
 
 def test_decode_step_in_place_and_rms():

@@ -339,30 +339,26 @@ int run_gemm(const uint16_t *a, const int32_t *b, const uint16_t *s, const int32
 // SwiGLU + row-norm) of `src` (row stride ld), for the decode step.
 int run_gemm_act(int act, const uint16_t *src, int64_t ld, const w4a16_linear &L, int64_t M, int64_t K, int64_t N,
                  uint16_t *out, hipStream_t stream) {
-    const GemmPlan plan = plan_gemm(M, K, N, L.G);
+    GemmPlan plan = plan_gemm(M, K, N, L.G);
+    if (plan.path == kPathMfma) {
+        if (act != 1) return fail(W4A16_ERR_UNSUPPORTED, "the MFMA path folds the row-norm only");
+        plan.partial_floats += mfma_rn_extra_floats(plan);
+    }
     GemmArgs args{nullptr, L.b_packed, L.scales, L.qzeros, M, K, N, L.G, L.zp_bias, out, nullptr, nullptr};
     int rc = get_scratch(stream, plan, &args.partials, &args.counters);
     if (rc != W4A16_OK) return rc;
-    hipError_t e = launch_gemv_act(args, plan, act, src, ld, stream);
+    hipError_t e = plan.path == kPathMfma ? launch_mfma_rn(args, plan, true, src, ld, stream)
+                                          : launch_gemv_act(args, plan, act, src, ld, stream);
     if (e != hipSuccess) return fail(W4A16_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
     return ok();
 }
 
-// The three glue steps inside a layer fold into the next GEMV when all three
-// of those linears run the default GEMV shape (M <= 8, 8 waves).
+// A glue step folds into the GEMV that consumes it when that GEMV runs the
+// default shape (M <= 8, 8 waves).
 bool fusable(const GemmPlan &p) { return p.path == kPathGemv && p.waves == 8; }
-bool fused_glue(const w4a16_linear *L, int64_t M, int64_t H, int64_t I) {
-    if (tune().decode_fuse == 0) return false;
-    return fusable(plan_gemm(M, H, H, L[1].G)) && fusable(plan_gemm(M, H, 2 * I, L[2].G)) &&
-           fusable(plan_gemm(M, I, H, L[3].G));
-}
-// The layer-output row-norm folds into the next layer's QKV GEMV.
-bool fused_qkv(const w4a16_linear *L, int64_t M, int64_t H) {
-    return tune().decode_fuse != 0 && fusable(plan_gemm(M, H, L[0].N, L[0].G));
-}
 
-// Decode-step workspace layout: T (GEMM outputs, M x maxN fp16) then Hb
-// (re-normalised inputs, M x max(H, I) fp16), each 256-byte aligned.
+// Decode-step workspace layout: two buffers of M x maxN fp16 (maxN = the
+// widest linear output), each 256-byte aligned.
 struct DecodeShape {
     int64_t H = 0, NQ = 0, I = 0, maxN = 0, maxK = 0;
 };
@@ -452,7 +448,7 @@ int w4a16_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t G, int32_t *path, i
 size_t w4a16_decode_workspace_bytes(int64_t M, const w4a16_linear *lin, int64_t n_layers) {
     DecodeShape d;
     if (M <= 0 || check_stack(lin, n_layers, &d) != W4A16_OK) return 0;
-    return align256((size_t)M * d.maxN * 2) + align256((size_t)M * d.maxK * 2);
+    return 2 * align256((size_t)M * d.maxN * 2);
 }
 
 int w4a16_decode_step(const w4a16_linear *lin, int64_t n_layers, const uint16_t *x_in, uint16_t *x_out,
@@ -462,59 +458,78 @@ int w4a16_decode_step(const w4a16_linear *lin, int64_t n_layers, const uint16_t 
     DecodeShape d;
     int rc = check_stack(lin, n_layers, &d);
     if (rc != W4A16_OK) return rc;
-    const size_t t_bytes = align256((size_t)M * d.maxN * 2);
-    const size_t need = t_bytes + align256((size_t)M * d.maxK * 2);
+    const size_t buf_bytes = align256((size_t)M * d.maxN * 2);
+    const size_t need = 2 * buf_bytes;
     if (workspace_bytes < need) return fail(W4A16_ERR_INVALID_ARG, "workspace smaller than w4a16_decode_workspace_bytes()");
+    if (M * d.maxN >= (1ll << 31)) return fail(W4A16_ERR_UNSUPPORTED, "decode step too large for 32-bit kernel indexing");
     if (!aligned16(x_in) || !aligned16(x_out) || !aligned16(workspace))
         return fail(W4A16_ERR_UNSUPPORTED, "x_in, x_out and workspace must be 16-byte aligned");
     const size_t x_b = (size_t)M * d.H * 2;
     if (overlaps(workspace, need, x_in, x_b) || overlaps(workspace, need, x_out, x_b))
         return fail(W4A16_ERR_INVALID_ARG, "workspace overlaps x_in or x_out");
-    uint16_t *T = static_cast<uint16_t *>(workspace);
-    uint16_t *Hb = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + t_bytes);
-    const uint16_t *x = x_in;
+    // Two buffers, each M x maxN: every kernel reads one and writes the other.
+    uint16_t *A = static_cast<uint16_t *>(workspace);
+    uint16_t *B = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + buf_bytes);
+    auto other = [&](const uint16_t *p) { return p == A ? B : A; };
     auto glue = [](hipError_t e) {
         return e == hipSuccess ? W4A16_OK
                                : fail(W4A16_ERR_HIP, std::string("glue launch: ") + hipGetErrorString(e));
     };
-    // `pending`: Hb holds the previous layer's down-projection output whose
-    // row-norm has not been applied yet (the next fused QKV applies it on load,
-    // bit for bit as the row-norm kernel would).
-    bool pending = false;
+    const bool fuse = tune().decode_fuse != 0;
+    const uint16_t *x = x_in;  // the layer input, row-normed (when pend is null)
+    uint16_t *pend = nullptr;  // or: the previous layer's down output, its row-norm not yet applied
     for (int64_t l = 0; l < n_layers; ++l) {
         const w4a16_linear *L = lin + 4 * l;
-        const int64_t H = d.H, I = L[2].N / 2;
-        const bool fuse = fused_glue(L, M, H, I);
-        if (pending && !(fuse && fused_qkv(L, M, H))) {
-            if ((rc = glue(launch_rownorm(Hb, M, H, H, x_out, stream)))) return rc;
+        const int64_t H = d.H, NQ = L[0].N, I = L[2].N / 2;
+        const GemmPlan pq = plan_gemm(M, H, NQ, L[0].G), po = plan_gemm(M, H, H, L[1].G),
+                       pg = plan_gemm(M, H, 2 * I, L[2].G), pd = plan_gemm(M, I, H, L[3].G);
+        // GEMV route (M <= 8): every glue step runs inside the GEMV that consumes
+        // it.  MFMA route: the row-norms run inside the MFMA GEMMs that consume
+        // them; SwiGLU + row-norm stays a kernel of its own.
+        const bool gemv_route = fuse && fusable(po) && fusable(pg) && fusable(pd);
+        const bool mfma_route = fuse && !gemv_route && po.path == kPathMfma && pg.path == kPathMfma;
+        const bool qkv_rn = pend && ((gemv_route && fusable(pq)) || (mfma_route && pq.path == kPathMfma));
+        if (pend && !qkv_rn) {
+            if ((rc = glue(launch_rownorm(pend, M, H, H, x_out, stream)))) return rc;
             x = x_out;
-            pending = false;
+            pend = nullptr;
         }
-        if (fuse) {
-            // Row-norm and SwiGLU folded into the consuming GEMVs: o and d land
-            // in Hb, q and gu in T.
-            if ((rc = pending ? run_gemm_act(1, Hb, H, L[0], M, H, L[0].N, T, stream)
-                              : run_gemm(x, L[0].b_packed, L[0].scales, L[0].qzeros, M, H, L[0].N, L[0].G,
-                                         L[0].zp_bias, T, stream, true)) ||
-                (rc = run_gemm_act(1, T, L[0].N, L[1], M, H, H, Hb, stream)) ||
-                (rc = run_gemm_act(1, Hb, H, L[2], M, H, 2 * I, T, stream)) ||
-                (rc = run_gemm_act(2, T, 2 * I, L[3], M, I, H, Hb, stream)))
-                return rc;
-            pending = true;
-            continue;
-        }
-        if ((rc = run_gemm(x, L[0].b_packed, L[0].scales, L[0].qzeros, M, H, L[0].N, L[0].G, L[0].zp_bias, T, stream, true)) ||
-            (rc = glue(launch_rownorm(T, M, L[0].N, H, Hb, stream))) ||
-            (rc = run_gemm(Hb, L[1].b_packed, L[1].scales, L[1].qzeros, M, H, H, L[1].G, L[1].zp_bias, T, stream, true)) ||
-            (rc = glue(launch_rownorm(T, M, H, H, Hb, stream))) ||
-            (rc = run_gemm(Hb, L[2].b_packed, L[2].scales, L[2].qzeros, M, H, 2 * I, L[2].G, L[2].zp_bias, T, stream, true)) ||
-            (rc = glue(launch_swiglu_rownorm(T, M, I, Hb, stream))) ||
-            (rc = run_gemm(Hb, L[3].b_packed, L[3].scales, L[3].qzeros, M, I, H, L[3].G, L[3].zp_bias, T, stream, true)) ||
-            (rc = glue(launch_rownorm(T, M, H, H, x_out, stream))))
+        uint16_t *q = pend ? other(pend) : A;
+        uint16_t *o = other(q);
+        if ((rc = qkv_rn ? run_gemm_act(1, pend, H, L[0], M, H, NQ, q, stream)
+                         : run_gemm(x, L[0].b_packed, L[0].scales, L[0].qzeros, M, H, NQ, L[0].G, L[0].zp_bias,
+                                    q, stream, true)))
             return rc;
-        x = x_out;
+        if (gemv_route) {
+            // q -> o (O), o -> q (gate+up), q -> o (down)
+            if ((rc = run_gemm_act(1, q, NQ, L[1], M, H, H, o, stream)) ||
+                (rc = run_gemm_act(1, o, H, L[2], M, H, 2 * I, q, stream)) ||
+                (rc = run_gemm_act(2, q, 2 * I, L[3], M, I, H, o, stream)))
+                return rc;
+            pend = o;
+        } else if (mfma_route) {
+            // q -> o (O), o -> q (gate+up), q -> o (SwiGLU + row-norm), o -> q (down)
+            if ((rc = run_gemm_act(1, q, NQ, L[1], M, H, H, o, stream)) ||
+                (rc = run_gemm_act(1, o, H, L[2], M, H, 2 * I, q, stream)) ||
+                (rc = glue(launch_swiglu_rownorm(q, M, I, o, stream))) ||
+                (rc = run_gemm(o, L[3].b_packed, L[3].scales, L[3].qzeros, M, I, H, L[3].G, L[3].zp_bias, q,
+                               stream, true)))
+                return rc;
+            pend = q;
+        } else {
+            // every glue step a kernel of its own
+            if ((rc = glue(launch_rownorm(q, M, NQ, H, o, stream))) ||
+                (rc = run_gemm(o, L[1].b_packed, L[1].scales, L[1].qzeros, M, H, H, L[1].G, L[1].zp_bias, q, stream, true)) ||
+                (rc = glue(launch_rownorm(q, M, H, H, o, stream))) ||
+                (rc = run_gemm(o, L[2].b_packed, L[2].scales, L[2].qzeros, M, H, 2 * I, L[2].G, L[2].zp_bias, q, stream, true)) ||
+                (rc = glue(launch_swiglu_rownorm(q, M, I, o, stream))) ||
+                (rc = run_gemm(o, L[3].b_packed, L[3].scales, L[3].qzeros, M, I, H, L[3].G, L[3].zp_bias, q, stream, true)) ||
+                (rc = glue(launch_rownorm(q, M, H, H, x_out, stream))))
+                return rc;
+            x = x_out;
+        }
     }
-    if (pending && (rc = glue(launch_rownorm(Hb, M, d.H, d.H, x_out, stream)))) return rc;
+    if (pend && (rc = glue(launch_rownorm(pend, M, d.H, d.H, x_out, stream)))) return rc;
     return ok();
 }
 

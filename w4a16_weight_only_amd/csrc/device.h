@@ -104,6 +104,12 @@ __device__ __forceinline__ f32x4 buffer_load_f32x4_sc1(__amdgpu_buffer_rsrc_t r,
 __device__ __forceinline__ void buffer_store_f32x4_sc1(f32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)voff, (int)soff, kCpolSc1);
 }
+__device__ __forceinline__ float buffer_load_f32_sc1(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, kCpolSc1));
+}
+__device__ __forceinline__ void buffer_store_f32_sc1(float v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)voff, (int)soff, kCpolSc1);
+}
 
 // dot(x, y) + 0 into a fresh register (VOP3P form: no zeroing move first).
 __device__ __forceinline__ float dot2_first(f16x2 x, f16x2 y) {

@@ -148,12 +148,19 @@ __device__ __forceinline__ void dequant_byte(const uint32_t (&wd)[8], const f16x
 }
 
 
-template <int MT, int NWN, int NWK, bool ASYM>
+// RN: the decode step's row-norm folded in.  A is the raw row (row stride
+// lda); each output is multiplied by its row's 1/sqrt(mean(a^2) + 1e-6) over
+// the K values, a per-row scalar, so it is applied to the products: each wave
+// sums the squares of the A operands it already holds, the K-waves meet in
+// the LDS reduction, and with K-splits the per-row partial sums travel with
+// the fp32 partials (after the output planes) to the last workgroup.
+template <int MT, int NWN, int NWK, bool ASYM, bool RN>
 __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
-    const uint16_t *__restrict__ a, const uint32_t *__restrict__ b,
+    const uint16_t *__restrict__ a, int lda, const uint32_t *__restrict__ b,
     const uint16_t *__restrict__ scales, const uint32_t *__restrict__ qzeros, int M, int K, int N,
     int G, uint32_t zp, int tiles_n, int tiles_m, int split_len, int splits,
     uint16_t *__restrict__ out, float *__restrict__ partials, uint32_t *__restrict__ counters) {
+    static_assert(!RN || NWK > 1, "the row sums meet in the K-wave reduction");
     using C = Cfg<MT, NWN, NWK>;
     // Logical workgroup: XCD-contiguous runs (grid is a multiple of 8).
     const int logical = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
@@ -182,7 +189,7 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
 
     const uint32_t row_bytes = (uint32_t)N8 * 4u;
     const __amdgpu_buffer_rsrc_t brs = buffer_rsrc(b, (uint32_t)((uint64_t)K * N8 * 4));
-    const __amdgpu_buffer_rsrc_t ars = buffer_rsrc(a, (uint32_t)((uint64_t)M * K * 2));
+    const __amdgpu_buffer_rsrc_t ars = buffer_rsrc(a, (uint32_t)(((uint64_t)(M - 1) * lda + K) * 2));
     const __amdgpu_buffer_rsrc_t srs = buffer_rsrc(scales, (uint32_t)((uint64_t)(K / G) * N * 2));
     const __amdgpu_buffer_rsrc_t zrs = buffer_rsrc(qzeros, ASYM ? (uint32_t)((uint64_t)(K / G) * row_bytes) : 0u);
     const uint32_t b_voff = ((uint32_t)(8 * kq) * (uint32_t)N8 + (uint32_t)wordc) * 4u;
@@ -192,13 +199,13 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
     // wave-uniform byte offset, so one lane offset serves every tile.  Rows
     // past M read row M-1 instead (valid memory; results never stored), which
     // only happens in a workgroup's last row tiles when 16*MT does not divide M.
-    const uint32_t a_row_bytes = (uint32_t)K * 2u;
+    const uint32_t a_row_bytes = (uint32_t)lda * 2u;
     const bool a_full = m0 + C::kTileRows <= M;
-    const uint32_t a_voff0 = ((uint32_t)(m0 + j16) * (uint32_t)K + 8u * kq) * 2u;
+    const uint32_t a_voff0 = ((uint32_t)(m0 + j16) * (uint32_t)lda + 8u * kq) * 2u;
     uint32_t a_voff_tail[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-        a_voff_tail[mt] = ((uint32_t)min(m0 + 16 * mt + j16, M - 1) * (uint32_t)K + 8u * kq) * 2u;
+        a_voff_tail[mt] = ((uint32_t)min(m0 + 16 * mt + j16, M - 1) * (uint32_t)lda + 8u * kq) * 2u;
 
     // Accumulators start from distinct (opaque) zeros: with one shared zero
     // constant the register allocator gave MFMA results and their srcC
@@ -282,13 +289,22 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
     // the next step's scale and zero pairs), so that the matrix core and the
     // VALU stay busy together; left alone the scheduler clusters them.
     constexpr int kValuPair = (28 + 2 * MT - 1) / (2 * MT);
-    constexpr int kValuFirst = (28 + 8 + (ASYM ? 16 : 0) + 2 * MT - 1) / (2 * MT);
+    constexpr int kValuFirst = (28 + 8 + (ASYM ? 16 : 0) + (RN ? 8 * MT : 0) + 2 * MT - 1) / (2 * MT);
+    float sq[MT];  // RN: this lane's sum of squares of its A values (row m0 + 16 mt + j16)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) sq[mt] = 0.f;
     auto step = [&](int s, auto uc) __attribute__((always_inline)) {
         constexpr int U = decltype(uc)::value;
         constexpr int AC = U % kRingA, AN = (U + kRingA - 1) % kRingA, WC = U % kRing, WN = (U + 1) % kRing;
         load_a(stc(s + kRingA - 1), av[AN]);
         f16x2 spn[8], zcn[8];
         mfma_pair(av[AC], bop, I0{});
+        if constexpr (RN) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sq[mt] = __builtin_fmaf((float)av[AC][mt][e], (float)av[AC][mt][e], sq[mt]);
+        }
         dequant_byte<3>(w[WC], zc, sp, nk, bop);
         scale_pairs(sv[WN], spn);
         zero_pairs<ASYM>(zw[WN], zp, nk, zcn);
@@ -354,8 +370,12 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
     // those rows itself: fp16 when the grid does not split K, else fp32 with
     // device-coherent stores into partials[split].
     typedef f16 f16x8_t __attribute__((ext_vector_type(8)));
-    const __amdgpu_buffer_rsrc_t prs =
-        buffer_rsrc(partials, splits > 1 ? (uint32_t)((uint64_t)splits * M * N * 4) : 0u);
+    const int tile = tile_m * tiles_n + tile_n;
+    // RN with K-splits: per (split, tile) the kTileRows row sums of squares,
+    // after the splits' output planes.
+    const uint32_t sq_base = (uint32_t)splits * (uint32_t)M * (uint32_t)N * 4u;
+    const uint32_t sq_bytes = RN ? (uint32_t)splits * (uint32_t)(tiles_n * tiles_m) * C::kTileRows * 4u : 0u;
+    const __amdgpu_buffer_rsrc_t prs = buffer_rsrc(partials, splits > 1 ? sq_base + sq_bytes : 0u);
     const uint32_t plane = (uint32_t)M * (uint32_t)N * 4u;
     auto store_slot = [&](int mt, int v, const f32x4 &lo, const f32x4 &hi) __attribute__((always_inline)) {
         const int row = m0 + 16 * mt + 4 * kq + v;
@@ -390,6 +410,16 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
         constexpr int PER = (SLOTS + NWK - 1) / NWK;    // slots per reducing wave
         static_assert(MT % MTC == 0, "whole rounds");
         __shared__ f32x4 red[NWN][NWK][SLOTS][2][64];
+        __shared__ float sq_red[NWN][NWK][MT][16];  // RN: per K-wave row sums of squares
+        if constexpr (RN) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                float v = sq[mt];
+                v += __shfl_xor(v, 16);
+                v += __shfl_xor(v, 32);
+                if (kq == 0) sq_red[wn][wk][mt][j16] = v;
+            }
+        }
 #pragma unroll
         for (int r0 = 0; r0 < MT; r0 += MTC) {
             if (r0 > 0) __syncthreads();  // previous round's reads are done
@@ -409,6 +439,22 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
                         lo += red[wn][src][q][0][lane];
                         hi += red[wn][src][q][1][lane];
                     }
+                    if constexpr (RN) {
+                        const int mt = r0 + q / 4, rl = 4 * kq + q % 4;  // row m0 + 16 mt + rl
+                        float rs = sq_red[wn][0][mt][rl];
+#pragma unroll
+                        for (int src = 1; src < NWK; ++src) rs += sq_red[wn][src][mt][rl];
+                        if (splits == 1) {
+                            const float inv = row_inv(rs, K);
+                            lo *= inv;
+                            hi *= inv;
+                        } else if (wn == 0 && j16 == 0 && m0 + 16 * mt + rl < M) {
+                            buffer_store_f32_sc1(rs, prs,
+                                                 sq_base + (((uint32_t)split * (uint32_t)(tiles_n * tiles_m) +
+                                                             (uint32_t)tile) * C::kTileRows + 16u * mt + rl) * 4u,
+                                                 0u);
+                        }
+                    }
                     store_slot(r0 + q / 4, q % 4, lo, hi);
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -420,7 +466,6 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
     wait_vm_zero();
     __syncthreads();
     __shared__ uint32_t last;
-    const int tile = tile_m * tiles_n + tile_n;
     if (threadIdx.x == 0) last = (arrive_agent(&counters[tile]) == (uint32_t)(splits - 1)) ? 1u : 0u;
     __syncthreads();
     if (!last) return;
@@ -434,6 +479,7 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
 #pragma unroll
     for (int u0 = 0; u0 < C::kUnits; u0 += C::kChunk) {
         f32x4 v[C::kChunk][C::kMaxSplits];
+        float rq[C::kChunk][C::kMaxSplits];  // RN: the splits' row sums of squares
 #pragma unroll
         for (int u = 0; u < C::kChunk; ++u) {
             const int idx = threadIdx.x + (u0 + u) * C::kThreads;
@@ -441,10 +487,17 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
             const int col = col0 + 4 * (idx % kRowUnits);
             const bool ok = row < M && col < N;
             const uint32_t off = ok ? ((uint32_t)row * (uint32_t)N + (uint32_t)col) * 4u : 0u;
+            const uint32_t roff = ((uint32_t)tile * C::kTileRows + (uint32_t)(idx / kRowUnits)) * 4u;
 #pragma unroll
-            for (int sp = 0; sp < C::kMaxSplits; ++sp)
+            for (int sp = 0; sp < C::kMaxSplits; ++sp) {
                 v[u][sp] = (ok && sp < splits) ? buffer_load_f32x4_sc1(prs, off, (uint32_t)sp * plane)
                                                : f32x4{0.f, 0.f, 0.f, 0.f};
+                rq[u][sp] = 0.f;
+                if constexpr (RN)
+                    if (ok && sp < splits)
+                        rq[u][sp] = buffer_load_f32_sc1(
+                            prs, sq_base + (uint32_t)sp * (uint32_t)(tiles_n * tiles_m) * C::kTileRows * 4u + roff, 0u);
+            }
         }
 #pragma unroll
         for (int u = 0; u < C::kChunk; ++u) {
@@ -455,6 +508,12 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
             f32x4 s = v[u][0];
 #pragma unroll
             for (int sp = 1; sp < C::kMaxSplits; ++sp) s += v[u][sp];
+            if constexpr (RN) {
+                float rs = rq[u][0];
+#pragma unroll
+                for (int sp = 1; sp < C::kMaxSplits; ++sp) rs += rq[u][sp];  // zero past `splits`
+                s *= row_inv(rs, K);
+            }
             const u16x4 o = {f32_to_f16_bits(s.x), f32_to_f16_bits(s.y), f32_to_f16_bits(s.z),
                              f32_to_f16_bits(s.w)};
             *reinterpret_cast<u16x4 *>(out + (size_t)row * N + col) = o;
@@ -464,23 +523,26 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
     if (threadIdx.x == 0) reset_counter_agent(&counters[tile]);
 }
 
+template <int MT, int NWN, int NWK, bool ASYM, bool RN>
+hipError_t launch_k(const GemmArgs &g, const GemmPlan &p, const uint16_t *a, int64_t lda, hipStream_t stream) {
+    hipLaunchKernelGGL((mfma_kernel<MT, NWN, NWK, ASYM, RN>), dim3((unsigned)p.grid), dim3(64 * NWN * NWK), 0, stream,
+                       a, (int)lda, reinterpret_cast<const uint32_t *>(g.b), g.scales,
+                       reinterpret_cast<const uint32_t *>(g.qzeros), (int)g.M, (int)g.K, (int)g.N, (int)g.G,
+                       (uint32_t)g.zp, (int)p.tiles_n, (int)p.tiles_m, (int)p.split_len, p.splits, g.out,
+                       g.partials, g.counters);
+    return hipGetLastError();
+}
+
 template <int MT, int NWN, int NWK>
-hipError_t launch_cfg(const GemmArgs &g, const GemmPlan &p, hipStream_t stream) {
+hipError_t launch_cfg(const GemmArgs &g, const GemmPlan &p, bool rn, const uint16_t *a, int64_t lda,
+                      hipStream_t stream) {
     if (p.splits > Cfg<MT, NWN, NWK>::kMaxSplits) return hipErrorInvalidValue;
     if (p.splits > 1 && (!g.partials || !g.counters)) return hipErrorInvalidValue;
-    dim3 grid((unsigned)p.grid, 1, 1);
-    dim3 block(64 * NWN * NWK, 1, 1);
-    const uint32_t *b = reinterpret_cast<const uint32_t *>(g.b);
-    const uint32_t *qz = reinterpret_cast<const uint32_t *>(g.qzeros);
-    if (g.qzeros)
-        hipLaunchKernelGGL((mfma_kernel<MT, NWN, NWK, true>), grid, block, 0, stream, g.a, b, g.scales, qz,
-                           (int)g.M, (int)g.K, (int)g.N, (int)g.G, (uint32_t)g.zp, (int)p.tiles_n,
-                           (int)p.tiles_m, (int)p.split_len, p.splits, g.out, g.partials, g.counters);
-    else
-        hipLaunchKernelGGL((mfma_kernel<MT, NWN, NWK, false>), grid, block, 0, stream, g.a, b, g.scales, qz,
-                           (int)g.M, (int)g.K, (int)g.N, (int)g.G, (uint32_t)g.zp, (int)p.tiles_n,
-                           (int)p.tiles_m, (int)p.split_len, p.splits, g.out, g.partials, g.counters);
-    return hipGetLastError();
+    if (rn)
+        return g.qzeros ? launch_k<MT, NWN, NWK, true, true>(g, p, a, lda, stream)
+                        : launch_k<MT, NWN, NWK, false, true>(g, p, a, lda, stream);
+    return g.qzeros ? launch_k<MT, NWN, NWK, true, false>(g, p, a, lda, stream)
+                    : launch_k<MT, NWN, NWK, false, false>(g, p, a, lda, stream);
 }
 
 
@@ -496,15 +558,24 @@ int mfma_max_splits(int mt, int waves, int kwaves) {
     return 1;
 }
 
-hipError_t launch_mfma(const GemmArgs &g, const GemmPlan &p, hipStream_t stream) {
+hipError_t launch_mfma_rn(const GemmArgs &g, const GemmPlan &p, bool rn, const uint16_t *a, int64_t lda,
+                          hipStream_t stream) {
     // (MT, NWN, NWK) combinations the planner emits.
-    if (p.mt == 1 && p.waves == 2 && p.kwaves == 4) return launch_cfg<1, 2, 4>(g, p, stream);
-    if (p.mt == 2 && p.waves == 2 && p.kwaves == 4) return launch_cfg<2, 2, 4>(g, p, stream);
-    if (p.mt == 4 && p.waves == 2 && p.kwaves == 2) return launch_cfg<4, 2, 2>(g, p, stream);
-    if (p.mt == 2 && p.waves == 1 && p.kwaves == 8) return launch_cfg<2, 1, 8>(g, p, stream);
-    if (p.mt == 4 && p.waves == 2 && p.kwaves == 4) return launch_cfg<4, 2, 4>(g, p, stream);
-    if (p.mt == 4 && p.waves == 1 && p.kwaves == 8) return launch_cfg<4, 1, 8>(g, p, stream);
+    if (p.mt == 1 && p.waves == 2 && p.kwaves == 4) return launch_cfg<1, 2, 4>(g, p, rn, a, lda, stream);
+    if (p.mt == 2 && p.waves == 2 && p.kwaves == 4) return launch_cfg<2, 2, 4>(g, p, rn, a, lda, stream);
+    if (p.mt == 4 && p.waves == 2 && p.kwaves == 2) return launch_cfg<4, 2, 2>(g, p, rn, a, lda, stream);
+    if (p.mt == 2 && p.waves == 1 && p.kwaves == 8) return launch_cfg<2, 1, 8>(g, p, rn, a, lda, stream);
+    if (p.mt == 4 && p.waves == 2 && p.kwaves == 4) return launch_cfg<4, 2, 4>(g, p, rn, a, lda, stream);
+    if (p.mt == 4 && p.waves == 1 && p.kwaves == 8) return launch_cfg<4, 1, 8>(g, p, rn, a, lda, stream);
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_mfma(const GemmArgs &g, const GemmPlan &p, hipStream_t stream) {
+    return launch_mfma_rn(g, p, false, g.a, g.K, stream);
+}
+
+size_t mfma_rn_extra_floats(const GemmPlan &p) {
+    return p.splits > 1 ? (size_t)p.splits * (size_t)(p.tiles_n * p.tiles_m) * (size_t)(16 * p.mt) : 0;
 }
 
 }  // namespace w4a16

@@ -58,6 +58,13 @@ hipError_t launch_gemv(const GemmArgs &args, const GemmPlan &plan, hipStream_t s
 hipError_t launch_gemv_act(const GemmArgs &args, const GemmPlan &plan, int act, const uint16_t *src,
                            int64_t ld, hipStream_t stream);
 hipError_t launch_mfma(const GemmArgs &args, const GemmPlan &plan, hipStream_t stream);
+// MFMA GEMM on A = `a` with row stride lda (>= K); with rn, the decode step's
+// row-norm folded in: out = (a . W) * inv_row, inv_row = 1/sqrt(mean(a_row^2)
+// + 1e-6) over the row's K values, applied to the products (the partials
+// buffer then needs mfma_rn_extra_floats(plan) more floats).
+hipError_t launch_mfma_rn(const GemmArgs &args, const GemmPlan &plan, bool rn, const uint16_t *a, int64_t lda,
+                          hipStream_t stream);
+size_t mfma_rn_extra_floats(const GemmPlan &plan);
 // Largest K-split count the MFMA kernel's in-kernel reduction takes for a
 // (mt, waves, kwaves) configuration.
 int mfma_max_splits(int mt, int waves, int kwaves);
