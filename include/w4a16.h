@@ -164,10 +164,12 @@ int w4a16_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t G, int32_t *path,
 
 /* Replace the planner's tuning overrides (the same "key=value,..." form the
  * environment variable W4A16_TUNE gives at first use; NULL or "" restores the
- * defaults).  Keys: gemv_target_waves, gemv_waves (4 or 8), gemv_splits,
+ * defaults).  Keys: gemv_target_waves (the M <= 2 GEMV wave target),
+ * gemv_waves (4 or 8), gemv_splits,
  * gemv_fold (1 folded form, 0 exact form, -1 folded for symmetric zero
  * point at M <= 2), gemv_max_m,
- * mfma_target_waves, mfma_splits, mfma_cfg (1..6), max_partial_bytes,
+ * mfma_target_waves, mfma_splits, mfma_cfg (1..6), mfma_mgroup (row tiles
+ * walked per column tile by consecutive workgroups), max_partial_bytes,
  * decode_fuse (0: the decode step runs its glue as separate kernels).  Every
  * choice computes the same product; they differ in speed and in fp32
  * rounding.  Unknown keys or malformed values: W4A16_ERR_INVALID_ARG and the

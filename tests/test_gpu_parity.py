@@ -104,18 +104,21 @@ def test_gemm_matches_oracle(M, K, N, G, asym):
 
 TUNED_FORMS = ["gemv_fold=0", "gemv_fold=1", "gemv_waves=4", "gemv_waves=4,gemv_fold=1",
                "gemv_splits=1", "gemv_splits=7", "gemv_max_m=0", "mfma_cfg=4", "mfma_cfg=5,mfma_splits=3",
-               "mfma_cfg=3", "mfma_cfg=6", "mfma_cfg=6,mfma_splits=3"]
+               "mfma_cfg=3", "mfma_cfg=6", "mfma_cfg=6,mfma_splits=3", "mfma_mgroup=1", "mfma_mgroup=2",
+               "mfma_cfg=4,mfma_mgroup=3", "mfma_cfg=1,mfma_mgroup=4,mfma_splits=2"]
 
 
 @pytest.mark.parametrize("spec", TUNED_FORMS)
 def test_gemm_tuned_forms_match_oracle(spec):
     """Every planner override computes the same product (the exact and folded
     GEMV forms, 4- and 8-wave workgroups, forced split counts, the MFMA path
-    at small M, the alternative MFMA tile shapes)."""
+    at small M, the alternative MFMA tile shapes, the workgroup orders over
+    row tiles, including a ragged last band)."""
     try:
         w4.w4a16_set_tuning(spec)
         for M, K, N, G, asym in [(1, 1024, 544, 128, False), (2, 2048, 1024, 64, True), (3, 512, 800, 128, True),
-                                 (5, 1024, 288, 256, False), (8, 1024, 544, 128, True), (20, 1024, 520, 128, True)]:
+                                 (5, 1024, 288, 256, False), (8, 1024, 544, 128, True), (20, 1024, 520, 128, True),
+                                 (150, 512, 800, 128, True)]:
             path, splits, grid = w4.w4a16_gemm_plan(M, K, N, G)
             note("tuned %s M=%d K=%d N=%d path=%d splits=%d grid=%d" % (spec, M, K, N, path, splits, grid))
             p = synth.problem(M, K, N, G, asym, seed=300 + M)

@@ -51,7 +51,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Plan knobs, overridable for tuning sweeps: "key=value,..." from the
 // environment variable W4A16_TUNE at first use, or from w4a16_set_tuning().
 struct Tune {
-    int64_t gemv_target_waves = 1600;  // aim for about this many GEMV waves
+    int64_t gemv_target_waves = 1600;  // M <= 2: aim for about this many GEMV waves (see plan_gemm)
     int64_t gemv_waves = 8;            // waves per GEMV workgroup (4 or 8)
     int64_t gemv_splits = 0;           // force the GEMV K-split count
     int64_t gemv_fold = -1;            // bias/zero removed per chunk: 1 always, 0 never, -1 symmetric M <= 2
@@ -59,6 +59,7 @@ struct Tune {
     int64_t mfma_target_waves = 2048;  // aim for about this many MFMA-path waves
     int64_t mfma_splits = 0;           // force the MFMA split count
     int64_t mfma_cfg = 0;  // force (mt, waves, kwaves): 1..6 = (1,2,4) (2,2,4) (4,2,2) (2,1,8) (4,2,4) (4,1,8)
+    int64_t mfma_mgroup = 0;           // force the MFMA row-tile group (0: by estimated L2 traffic)
     int64_t max_partial_bytes = 64ll << 20;
     int64_t decode_fuse = 1;           // 0: decode-step glue as separate kernels
 };
@@ -88,6 +89,7 @@ bool parse_tune(const char *spec, Tune *out) {
         else if (k == "mfma_target_waves") v.mfma_target_waves = val;
         else if (k == "mfma_splits") v.mfma_splits = val;
         else if (k == "mfma_cfg") v.mfma_cfg = val;
+        else if (k == "mfma_mgroup") v.mfma_mgroup = val;
         else if (k == "max_partial_bytes") v.max_partial_bytes = val;
         else if (k == "decode_fuse") v.decode_fuse = val;
         else return false;
@@ -139,7 +141,7 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G) {
     const int64_t N8 = N / 8;
     if (M <= std::min<int64_t>(8, t.gemv_max_m) && N % 32 == 0) {
         // 256-column tiles (one 128-byte line of every weight row per
-        // workgroup); K-splits to give about gemv_target_waves waves.
+        // workgroup); K-splits to fill one round of the 256 CUs (below).
         p.path = kPathGemv;
         p.words = gemv_words_for_m(M);
         // The folded form drops one packed subtract per weight pair; measured
@@ -156,9 +158,21 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G) {
         if (t.gemv_splits > 0) {
             splits = t.gemv_splits;
         } else {
-            splits = cdiv(t.gemv_target_waves, p.tiles_n * p.waves);
-            // keep at least half of each workgroup's row lanes busy
-            splits = std::min<int64_t>(splits, std::max<int64_t>(1, nchunks / (p.waves * RL / 2)));
+            // Measured on MI355X: as many splits as one round of workgroups
+            // holds (one 8-wave workgroup per CU) is fastest, except at M <= 2,
+            // where the stream is purely bandwidth-bound and fewer splits (less
+            // fixed-point slot traffic, longer per-wave streams) win as long as
+            // they still give 3/4 of the CUs a workgroup: about
+            // gemv_target_waves waves, each workgroup's row lanes kept at
+            // least half busy.  Splits keep at least 8 chunks each.
+            const int64_t per_cu = 8 / p.waves;
+            splits = std::max<int64_t>(1, 256 * per_cu / p.tiles_n);
+            splits = std::min<int64_t>(splits, std::max<int64_t>(1, nchunks / 8));  // >= 128 rows per split
+            if (M <= 2) {
+                int64_t fewer = cdiv(t.gemv_target_waves, p.tiles_n * p.waves);
+                fewer = std::min<int64_t>(fewer, std::max<int64_t>(1, nchunks / (p.waves * RL / 2)));
+                if (fewer < splits && 4 * fewer * p.tiles_n >= 3 * 256 * per_cu) splits = fewer;
+            }
         }
         splits = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(splits, 32), nchunks));
         p.split_len = cdiv(nchunks, splits);
@@ -230,6 +244,28 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G) {
             }
             fill(kBig[best][0], kBig[best][1], kBig[best][2]);
         }
+        // Row-tile group: the 32 workgroups an XCD holds at once (one per CU)
+        // are consecutive logical indices; walking g row tiles per column tile
+        // makes them read about ceil(32/g) column tiles of weights and g row
+        // tiles of activations through that XCD's L2.  Pick the g with the
+        // fewest such bytes (the smallest g on ties).
+        const int64_t krows = p.split_len * 32;
+        const int64_t cols = 16 * 8 * (int64_t)p.waves;
+        const double wcol = (double)krows * (double)cols * 0.5 + (double)(krows / G) * (double)cols * 2.5;
+        const double arow = (double)(16 * p.mt) * (double)krows * 2.0;
+        const int64_t resident = std::max<int64_t>(1, std::min<int64_t>(32, cdiv(p.tiles_n * p.tiles_m * p.splits, 8)));
+        int64_t gbest = 1;
+        double cbest = -1;
+        for (int64_t g = 1; g <= std::min<int64_t>(p.tiles_m, resident); ++g) {
+            const double cost = (double)std::min<int64_t>(cdiv(resident, g), p.tiles_n) * wcol +
+                                (double)std::min<int64_t>(g, resident) * arow;
+            if (cbest < 0 || cost < cbest - 1e-6 * cbest) {
+                cbest = cost;
+                gbest = g;
+            }
+        }
+        if (t.mfma_mgroup > 0) gbest = std::min<int64_t>(t.mfma_mgroup, p.tiles_m);
+        p.m_group = (int)gbest;
     }
     p.grid = p.tiles_n * p.tiles_m * p.splits;
     p.grid = cdiv(p.grid, 8) * 8;  // XCD-aware index mapping needs a multiple of 8

@@ -158,16 +158,24 @@ template <int MT, int NWN, int NWK, bool ASYM, bool RN>
 __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
     const uint16_t *__restrict__ a, int lda, const uint32_t *__restrict__ b,
     const uint16_t *__restrict__ scales, const uint32_t *__restrict__ qzeros, int M, int K, int N,
-    int G, uint32_t zp, int tiles_n, int tiles_m, int split_len, int splits,
+    int G, uint32_t zp, int tiles_n, int tiles_m, int m_group, int split_len, int splits,
     uint16_t *__restrict__ out, float *__restrict__ partials, uint32_t *__restrict__ counters) {
     static_assert(!RN || NWK > 1, "the row sums meet in the K-wave reduction");
     using C = Cfg<MT, NWN, NWK>;
-    // Logical workgroup: XCD-contiguous runs (grid is a multiple of 8).
+    // Logical workgroup: XCD-contiguous runs (grid is a multiple of 8), so the
+    // workgroups one XCD runs together are consecutive logical indices.
     const int logical = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
     if (logical >= tiles_n * tiles_m * splits) return;  // whole workgroup
-    const int tile_n = logical % tiles_n;
-    const int tile_m = (logical / tiles_n) % tiles_m;
+    // Within a split: bands of m_group row tiles; inside a band the row tiles
+    // of one column tile are consecutive (they read the same weights), the
+    // last band possibly shorter.
     const int split = logical / (tiles_n * tiles_m);
+    const int in_split = logical - split * (tiles_n * tiles_m);
+    const int band = in_split / (m_group * tiles_n);
+    const int in_band = in_split - band * (m_group * tiles_n);
+    const int band_rows = min(m_group, tiles_m - band * m_group);
+    const int tile_n = in_band / band_rows;
+    const int tile_m = band * m_group + (in_band - tile_n * band_rows);
 
     const int lane = threadIdx.x & 63;
     // Wave-uniform (the compiler cannot prove threadIdx.x >> 6 is): keeps the
@@ -528,7 +536,7 @@ hipError_t launch_k(const GemmArgs &g, const GemmPlan &p, const uint16_t *a, int
     hipLaunchKernelGGL((mfma_kernel<MT, NWN, NWK, ASYM, RN>), dim3((unsigned)p.grid), dim3(64 * NWN * NWK), 0, stream,
                        a, (int)lda, reinterpret_cast<const uint32_t *>(g.b), g.scales,
                        reinterpret_cast<const uint32_t *>(g.qzeros), (int)g.M, (int)g.K, (int)g.N, (int)g.G,
-                       (uint32_t)g.zp, (int)p.tiles_n, (int)p.tiles_m, (int)p.split_len, p.splits, g.out,
+                       (uint32_t)g.zp, (int)p.tiles_n, (int)p.tiles_m, p.m_group, (int)p.split_len, p.splits, g.out,
                        g.partials, g.counters);
     return hipGetLastError();
 }

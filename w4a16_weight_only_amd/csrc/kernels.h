@@ -24,6 +24,8 @@ struct GemmPlan {
     bool fold_asym = false;   // the same with packed zeros
     int64_t tiles_n = 0;      // workgroup tiles along N
     int64_t tiles_m = 1;      // workgroup tiles along M (MFMA)
+    int m_group = 1;          // MFMA: consecutive workgroups walk this many row tiles of one
+                              // column tile before the next column tile (shared weights in L2)
     int splits = 1;           // K-splits across workgroups
     int64_t split_len = 0;    // K-units per split (GEMV: 16-row chunks; MFMA: 32-row steps)
     int64_t grid = 0;         // workgroups launched
