@@ -387,3 +387,29 @@ def test_decode_step_in_place_and_rms():
     assert np.array_equal(got.view(np.uint16), ref.view(np.uint16))
     rms = np.sqrt((got.astype(np.float64) ** 2).mean(1))
     assert np.allclose(rms, 1.0, atol=5e-3)
+
+
+@pytest.mark.parametrize("M", [1, 2, 5])
+@pytest.mark.parametrize("I", [9216, 12800])
+def test_decode_step_down_projection_intermediate(M, I):
+    """White box: the step's output is row-normed, which hides a wrong row
+    scale in the down projection (its SwiGLU row-norm runs inside the GEMV).
+    After a one-layer step at M <= 8 the workspace's first buffer holds the
+    gate+up output and the second the down projection's; the latter must be
+    the oracle's down projection of the former, element by element.  MLP
+    widths 9216 and 12800 give K-splits with fewer 16-row chunks than row
+    lanes, where a row-sum reduction run on only the lanes that hold a chunk
+    lost part of a wave's sum."""
+    H, NQ, G = 512, 640, 128
+    layers = synth.stack_layer(0, H=H, NQ=NQ, I=I, G=G, seed_base=2300)
+    x = dev(synth.stack_input(M, H, seed=90 + M))
+    buf = (M * max(L["N"] for L in layers) * 2 + 255) // 256 * 256
+    ws = torch.zeros(2 * buf, dtype=torch.uint8, device="cuda")
+    note("decode down intermediate M=%d I=%d" % (M, I))
+    w4.w4a16_decode_step(dev_stack(layers), x, workspace=ws)
+    w = host(ws)
+    gu = w[:buf].view(np.float16)[:M * 2 * I].reshape(M, 2 * I)
+    down = w[buf:].view(np.float16)[:M * H].reshape(M, H)
+    D = layers[3]
+    want = oracle.gemm(oracle.swiglu_rownorm(gu), D["b_packed"], D["scales"], None, G, 8)
+    check_close(down, want, "down projection M=%d I=%d" % (M, I), tol=FUSED_LAYER_TOL)

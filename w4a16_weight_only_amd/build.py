@@ -7,6 +7,7 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -24,23 +25,41 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + ["-o", tmp] + srcs
+# hipcc's host pass warns that it does not know the packed-fp32 feature: harmless
+_NOISE = "not a recognized feature for this target"
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    # hipcc's host pass warns that it does not know the packed-fp32 feature: harmless
-    noise = "not a recognized feature for this target"
-    out = "\n".join(l for l in res.stdout.splitlines() if noise not in l)
-    if res.returncode != 0:
-        if os.path.exists(tmp):
-            os.remove(tmp)
-        raise RuntimeError("hipcc failed:\n" + out)
+    out = "\n".join(l for l in res.stdout.splitlines() if _NOISE not in l)
     if verbose and out.strip():
         print(out)
-    os.replace(tmp, LIB)
+    return res.returncode, out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link the library."""
+    tag = ".tmp%d" % os.getpid()
+    objs = [os.path.join(CSRC, s + tag + ".o") for s in SOURCES]
+    cmds = [[HIPCC] + [f for f in FLAGS if f != "-shared"] + ["-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(SOURCES, objs)]
+    tmp = LIB + tag
+    try:
+        with ThreadPoolExecutor(max_workers=min(len(cmds), max(1, (os.cpu_count() or 1)))) as ex:
+            results = list(ex.map(lambda c: _run(c, verbose), cmds))
+        for (rc, out), src in zip(results, SOURCES):
+            if rc != 0:
+                raise RuntimeError("hipcc failed on %s:\n%s" % (src, out))
+        rc, out = _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
+        if rc != 0:
+            raise RuntimeError("hipcc link failed:\n" + out)
+        os.replace(tmp, LIB)
+    finally:
+        for f in objs + [tmp]:
+            if os.path.exists(f):
+                os.remove(f)
     return LIB
 
 

@@ -372,14 +372,15 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
     const int c0 = c_begin + wave * RL + rl;
     constexpr int kStride = NW * RL;
     // Row sums of squares of the transformed rows (the glue kernels' order:
-    // 1024 virtual threads, two chains per thread of the 512), reduced per
-    // wave here and across waves in the epilogue.  With the row held in
-    // registers (M <= 2) they are computed while the first chunk's weights
-    // are in flight; otherwise after the chunk loop.
-    auto row_sums = [&]() __attribute__((always_inline)) {
+    // 1024 virtual threads, two chains per thread of the 512): a per-lane part
+    // (row_partials), reduced across the wave (row_reduce, where every lane of
+    // the wave is active) and across waves in the epilogue.  With the row held
+    // in registers (M <= 2) the per-lane part runs while the first chunk's
+    // weights are in flight; otherwise after the chunk loop.
+    float ss[M][2];
+    auto row_partials = [&]() __attribute__((always_inline)) {
         if constexpr (ACT != 0) {
             static_assert(NW == 8, "the row sums map 1024 virtual threads onto 512");
-            float ss[M][2];
 #pragma unroll
             for (int m = 0; m < M; ++m)
 #pragma unroll
@@ -399,6 +400,10 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
                     }
                     ss[m][h] = t;
                 }
+        }
+    };
+    auto row_reduce = [&]() __attribute__((always_inline)) {
+        if constexpr (ACT != 0) {
 #pragma unroll
             for (int m = 0; m < M; ++m)
 #pragma unroll
@@ -412,17 +417,21 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
     };
 
     if constexpr (kEarlyRows) {
-        // first chunk peeled: its weights are requested, then the row sums
-        // run on the row vectors (requested earlier, so already waited for
-        // without waiting for the weights)
+        // first chunk peeled: its weights are requested, then the per-lane row
+        // sums run on the row vectors (requested earlier, so already waited
+        // for without waiting for the weights).  Whether a lane holds a chunk
+        // differs between the lanes of a wave when a split holds fewer chunks
+        // than row lanes, so the cross-lane reduction waits until after the
+        // branch, where every lane takes part.
         if (c0 < c_end) {
             Chunk d;
             load_chunk(c0, d);
-            row_sums();
+            row_partials();
             compute_chunk(d);
         } else {
-            row_sums();
+            row_partials();
         }
+        row_reduce();
         for (int c = c0 + kStride; c < c_end; c += kStride) {
             Chunk d;
             load_chunk(c, d);
@@ -434,7 +443,8 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
             load_chunk(c, d);
             compute_chunk(d);
         }
-        row_sums();
+        row_partials();
+        row_reduce();
     }
 
     // Transpose-reduce over the row lanes (lane bits 5 .. log2(CL)): after the
