@@ -9,7 +9,7 @@
 //    line with WORDS-word loads (16 bytes when WORDS = 4) and RL = 64/CL row
 //    lanes take different 16-row chunks, so each load instruction reads whole
 //    lines (narrower tiles that split lines between workgroups cost up to 60%
-//    more time on MI355X).  Loads are unconditional -- lanes past N read a
+//    more time on MI355X), with the non-temporal cache policy (read once).  Loads are unconditional -- lanes past N read a
 //    clamped, valid address and their columns are never stored -- so the
 //    compiler can wait for each row pair as it lands.
 //  * Each lane converts nibbles two rows at a time (device.h) and accumulates
@@ -48,17 +48,17 @@ template <int W>
 __device__ __forceinline__ Words<W> buffer_words(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff);
 template <>
 __device__ __forceinline__ Words<4> buffer_words<4>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    const u32x4 t = buffer_load_x4(r, voff, soff);
+    const u32x4 t = buffer_load_x4_nt(r, voff, soff);
     return Words<4>{{t.x, t.y, t.z, t.w}};
 }
 template <>
 __device__ __forceinline__ Words<2> buffer_words<2>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    const u32x2 t = buffer_load_x2(r, voff, soff);
+    const u32x2 t = buffer_load_x2_nt(r, voff, soff);
     return Words<2>{{t.x, t.y}};
 }
 template <>
 __device__ __forceinline__ Words<1> buffer_words<1>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return Words<1>{{buffer_load_x1(r, voff, soff)}};
+    return Words<1>{{buffer_load_x1_nt(r, voff, soff)}};
 }
 
 template <int W>

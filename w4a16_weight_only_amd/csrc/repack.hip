@@ -16,6 +16,8 @@
 // whole 128-byte source row segments.  Results go through LDS with an XOR
 // swizzle (column nb ^ kb) that keeps both the scattered block writes and the
 // row-wise read-back conflict-free, and leave as 128-byte destination rows.
+// Every word is read once and written once: both use the non-temporal cache
+// policy (measured on MI355X: 15.6 -> 13.0 us at K = 4096, N = 12800).
 #include "device.h"
 #include "kernels.h"
 
@@ -58,7 +60,7 @@ __global__ __launch_bounds__(256) void repack_kernel(const uint32_t *__restrict_
         uint32_t w[8];
         if (kb < K8 && nb < N8) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) w[i] = src[(size_t)(8 * nb + i) * K8 + kb];
+            for (int i = 0; i < 8; ++i) w[i] = __builtin_nontemporal_load(&src[(size_t)(8 * nb + i) * K8 + kb]);
         } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i) w[i] = 0u;
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(256) void repack_kernel(const uint32_t *__restrict_
         const int nb_local = phys ^ (row >> 3);
         const int k = 8 * kb0 + row;
         const int nb = nb0 + nb_local;
-        if (k < 8 * K8 && nb < N8) dst[(size_t)k * N8 + nb] = tile[row][phys];
+        if (k < 8 * K8 && nb < N8) __builtin_nontemporal_store(tile[row][phys], &dst[(size_t)k * N8 + nb]);
     }
 }
 
