@@ -81,7 +81,8 @@ def small_cases():
     cases = []
     for M in range(1, 9):  # GEMV path: tiles of 256 columns, ragged last tile
         cases.append((M, 512, 544, 128, M % 2 == 0))
-    cases += [(1, 256, 256, 64, False), (2, 1024, 256, 1024, True), (3, 4096, 1024, 128, False)]
+    cases += [(1, 256, 256, 64, False), (2, 1024, 256, 1024, True), (3, 4096, 1024, 128, False),
+              (1, 512, 544, 32, False), (6, 256, 288, 32, True)]  # smallest group size on the GEMV path
     for M in (9, 15, 16, 17, 32, 33, 64, 65, 100, 128, 200, 256):  # MFMA path, ragged words/rows
         cases.append((M, 512, 520, 64, M % 2 == 1))
     cases += [(1, 256, 264, 64, True), (7, 384, 8, 128, False),  # N % 32 != 0 at small M
@@ -389,17 +390,20 @@ def test_decode_step_in_place_and_rms():
     assert np.allclose(rms, 1.0, atol=5e-3)
 
 
-@pytest.mark.parametrize("M", [1, 2, 5])
+@pytest.mark.parametrize("M", [1, 2, 5, 12, 24])
 @pytest.mark.parametrize("I", [9216, 12800])
 def test_decode_step_down_projection_intermediate(M, I):
     """White box: the step's output is row-normed, which hides a wrong row
-    scale in the down projection (its SwiGLU row-norm runs inside the GEMV).
-    After a one-layer step at M <= 8 the workspace's first buffer holds the
-    gate+up output and the second the down projection's; the latter must be
-    the oracle's down projection of the former, element by element.  MLP
-    widths 9216 and 12800 give K-splits with fewer 16-row chunks than row
-    lanes, where a row-sum reduction run on only the lanes that hold a chunk
-    lost part of a wave's sum."""
+    scale in any linear before it.  After a one-layer step the workspace holds
+    the down projection's output and its input: at M <= 8 (SwiGLU + row-norm
+    inside the down GEMV) the first buffer holds the gate+up output and the
+    second the down output, which must be the oracle's down projection of
+    fp16(rn(silu(g) * u)); at M >= 9 the second buffer holds the SwiGLU +
+    row-norm kernel's output (rows of unit rms) and the first the down GEMM's,
+    which must be the oracle's product of the two.  MLP widths 9216 and 12800
+    give GEMV K-splits with fewer 16-row chunks than row lanes, where a row-sum
+    reduction run on only the lanes that hold a chunk lost part of a wave's
+    sum."""
     H, NQ, G = 512, 640, 128
     layers = synth.stack_layer(0, H=H, NQ=NQ, I=I, G=G, seed_base=2300)
     x = dev(synth.stack_input(M, H, seed=90 + M))
@@ -408,8 +412,15 @@ def test_decode_step_down_projection_intermediate(M, I):
     note("decode down intermediate M=%d I=%d" % (M, I))
     w4.w4a16_decode_step(dev_stack(layers), x, workspace=ws)
     w = host(ws)
-    gu = w[:buf].view(np.float16)[:M * 2 * I].reshape(M, 2 * I)
-    down = w[buf:].view(np.float16)[:M * H].reshape(M, H)
     D = layers[3]
-    want = oracle.gemm(oracle.swiglu_rownorm(gu), D["b_packed"], D["scales"], None, G, 8)
+    if M <= 8:
+        gu = w[:buf].view(np.float16)[:M * 2 * I].reshape(M, 2 * I)
+        down = w[buf:].view(np.float16)[:M * H].reshape(M, H)
+        h3 = oracle.swiglu_rownorm(gu)
+    else:
+        h3 = w[buf:].view(np.float16)[:M * I].reshape(M, I)
+        down = w[:buf].view(np.float16)[:M * H].reshape(M, H)
+        rms = np.sqrt((h3.astype(np.float64) ** 2).mean(1))
+        assert np.allclose(rms, 1.0, atol=5e-3), rms
+    want = oracle.gemm(h3, D["b_packed"], D["scales"], None, G, 8)
     check_close(down, want, "down projection M=%d I=%d" % (M, I), tol=FUSED_LAYER_TOL)
