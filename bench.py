@@ -160,12 +160,15 @@ def bench_gemm(torch, w4, stream, M, K, N, G, asym, steps, warmup, seed):
     path, splits, grid = w4.w4a16_gemm_plan(M, K, N, G)
     del P
     torch.cuda.empty_cache()
+    # floor at the binding roof: max(bytes at peak HBM, 2MNK at peak fp16 MFMA)
+    floor_us = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (FP16_PEAK_TFLOPS * 1e12)) * 1e6
     return dict(M=M, K=K, N=N, G=G, asym=asym, path="gemv" if path == 1 else "mfma", splits=splits,
                 grid=grid, rotated_copies=copies, us_per_call=ms * 1e3, host_us_per_call=host_ms * 1e3,
                 eager_us_per_call=eager_ms * 1e3, alg_bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9,
                 tflops=flops / (ms * 1e-3) / 1e12,
                 hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                mfma_frac=flops / (ms * 1e-3) / 1e12 / FP16_PEAK_TFLOPS)
+                mfma_frac=flops / (ms * 1e-3) / 1e12 / FP16_PEAK_TFLOPS,
+                floor_us=floor_us, residual=ms * 1e3 / floor_us)
 
 
 def bench_repack(torch, w4, stream, K, N, steps, warmup):
@@ -234,6 +237,8 @@ def bench_decode(torch, w4, stream, Ms, steps, warmup):
                               tok_per_s=M / (ms * 1e-3), eager_tok_per_s=M / (eager_ms * 1e-3),
                               weight_bytes=wbytes, gbs=(wbytes + act) / (ms * 1e-3) / 1e9,
                               hbm_frac=(wbytes + act) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                              floor_us=(wbytes + act) / (HBM_PEAK_GBS * 1e9) * 1e6,
+                              residual=ms * 1e3 / ((wbytes + act) / (HBM_PEAK_GBS * 1e9) * 1e6),
                               output_row_rms=rms)
     del stack
     torch.cuda.empty_cache()
