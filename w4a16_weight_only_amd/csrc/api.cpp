@@ -355,8 +355,8 @@ int validate_gemm(const uint16_t *a, const int32_t *b, const uint16_t *s, const 
 }
 
 // exact_form: the GEMV keeps (q - z) exact per weight (no folded zero
-// correction).  The decode step uses it for every linear, so that its fused
-// and unfused routes compute each linear the same way, bit for bit.
+// correction).  The decode step's separate-kernel route uses it for every
+// linear (the oracle's roundings), and the fused route for layer 0's QKV.
 int run_gemm(const uint16_t *a, const int32_t *b, const uint16_t *s, const int32_t *qz, int64_t M,
              int64_t K, int64_t N, int64_t G, int32_t zp, uint16_t *out, hipStream_t stream,
              bool exact_form = false) {
