@@ -162,7 +162,7 @@ def bench_gemm(torch, w4, stream, M, K, N, G, asym, steps, warmup, seed):
     torch.cuda.empty_cache()
     # floor at the binding roof: max(bytes at peak HBM, 2MNK at peak fp16 MFMA)
     floor_us = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (FP16_PEAK_TFLOPS * 1e12)) * 1e6
-    return dict(M=M, K=K, N=N, G=G, asym=asym, path="gemv" if path == 1 else "mfma", splits=splits,
+    return dict(M=M, K=K, N=N, G=G, asym=asym, path={1: "gemv", 2: "mfma", 3: "gemv_mma"}[path], splits=splits,
                 grid=grid, rotated_copies=copies, us_per_call=ms * 1e3, host_us_per_call=host_ms * 1e3,
                 eager_us_per_call=eager_ms * 1e3, alg_bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9,
                 tflops=flops / (ms * 1e-3) / 1e12,
@@ -400,7 +400,8 @@ def main():
     traffic = measured_traffic()
     roofline = dict(bound="hbm", achieved=round(head["gbs"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(head["gbs"] / HBM_PEAK_GBS, 4), traffic=traffic,
-                    kernel="gemv_kernel<M=1>", alg_bytes_per_launch=head["alg_bytes"],
+                    kernel=("gemv_mma_kernel<M=1>" if head["path"] == "gemv_mma" else "gemv_kernel<M=1>"),
+                    alg_bytes_per_launch=head["alg_bytes"],
                     us_per_launch=round(head["us_per_call"], 3), kernel_source_sha256_16=kernel_hash())
     line = {
         "metric": "W4A16 linear: HBM GB/s at M=1, TFLOP/s at M=32/256, % of roofline",

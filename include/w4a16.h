@@ -155,7 +155,9 @@ int w4a16_decode_step(const w4a16_linear *lin, int64_t n_layers, const uint16_t 
 
 /*
  * Describe the plan w4a16_gemm would run for a shape (host-only, no HIP calls):
- * path 1 = GEMV (vector ALUs), 2 = MFMA; splits = K-splits across workgroups;
+ * path 1 = GEMV on the vector ALUs (dot2), 3 = GEMV with its k-reduction on
+ * the matrix cores (M <= 8), 2 = MFMA GEMM (tiles of 16+ rows); splits =
+ * K-splits across workgroups;
  * grid = workgroups launched.  Returns the status w4a16_gemm would return from
  * validation of the sizes alone (pointers are not examined).
  */
@@ -164,10 +166,11 @@ int w4a16_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t G, int32_t *path,
 
 /* Replace the planner's tuning overrides (the same "key=value,..." form the
  * environment variable W4A16_TUNE gives at first use; NULL or "" restores the
- * defaults).  Keys: gemv_target_waves (the M <= 2 GEMV wave target),
- * gemv_waves (4 or 8), gemv_splits,
- * gemv_fold (1 folded form, 0 exact form, -1 folded for symmetric zero
- * point at M <= 2), gemv_max_m,
+ * defaults).  Keys: gemv_mma (1 default: the matrix-core GEMV at M <= 8;
+ * 0: the dot2 GEMV), gemv_target_waves (the dot2 GEMV's M <= 2 wave target),
+ * gemv_waves (4 or 8; 4 selects the dot2 GEMV), gemv_splits,
+ * gemv_fold (dot2 GEMV: 1 folded form, 0 exact form, -1 folded for symmetric
+ * zero point at M <= 2), gemv_max_m,
  * mfma_target_waves, mfma_splits, mfma_cfg (1..6), mfma_mgroup (row tiles
  * walked per column tile by consecutive workgroups), max_partial_bytes,
  * decode_fuse (0: the decode step runs its glue as separate kernels).  Every

@@ -56,6 +56,12 @@ def test_set_tuning_changes_the_plan_and_rejects_bad_specs(lib):
     try:
         w4.w4a16_set_tuning("gemv_splits=2")
         assert w4.w4a16_gemm_plan(1, 4096, 12800, 128)[1] == 2
+        w4.w4a16_set_tuning("gemv_mma=0")
+        assert w4.w4a16_gemm_plan(1, 4096, 12800, 128)[0] == 1
+        w4.w4a16_set_tuning("gemv_mma=0")
+        assert w4.w4a16_gemm_plan(4, 4096, 12800, 128)[0] == 1
+        w4.w4a16_set_tuning("gemv_waves=4")  # the matrix-core GEMV runs 8-wave workgroups only
+        assert w4.w4a16_gemm_plan(4, 4096, 12800, 128)[0] == 1
         w4.w4a16_set_tuning("gemv_max_m=0")
         assert w4.w4a16_gemm_plan(1, 4096, 12800, 128)[0] == 2
         for bad in ("bogus=1", "gemv_splits", "gemv_splits=x", "gemv_splits=3q"):
@@ -125,9 +131,10 @@ def test_repack_rejects_null_and_overlap(lib):
 
 
 def test_gemm_plan_paths(lib):
-    # decode GEMV, batched and prefill shapes
-    assert w4.w4a16_gemm_plan(1, 4096, 12800, 128)[0] == 1
-    assert w4.w4a16_gemm_plan(8, 4096, 12800, 128)[0] == 1
+    # decode GEMV (matrix cores; the dot2 form on request), batched and prefill shapes
+    for M in range(1, 9):
+        assert w4.w4a16_gemm_plan(M, 4096, 12800, 128)[0] == 3
+    assert w4.w4a16_gemm_plan(1, 4096, 12800, 128)[1] == 5  # one round: 50 tiles x 5 splits
     assert w4.w4a16_gemm_plan(9, 4096, 12800, 128)[0] == 2
     assert w4.w4a16_gemm_plan(32, 4096, 12800, 128)[0] == 2
     assert w4.w4a16_gemm_plan(256, 12800, 4096, 128)[0] == 2

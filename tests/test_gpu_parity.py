@@ -103,16 +103,34 @@ def test_gemm_matches_oracle(M, K, N, G, asym):
     check_close(got, want, "M=%d K=%d N=%d" % (M, K, N))
 
 
-TUNED_FORMS = ["gemv_fold=0", "gemv_fold=1", "gemv_waves=4", "gemv_waves=4,gemv_fold=1",
-               "gemv_splits=1", "gemv_splits=7", "gemv_max_m=0", "mfma_cfg=4", "mfma_cfg=5,mfma_splits=3",
+@pytest.mark.parametrize("M,K,N,G,asym", [c for c in small_cases() if c[0] <= 8 and c[2] % 32 == 0])
+def test_gemm_dot2_gemv_matches_oracle(M, K, N, G, asym):
+    """The dot2 GEMV (vector ALUs; the planner's default is the matrix-core
+    GEMV) on the small GEMV cases."""
+    p = synth.problem(M, K, N, G, asym, seed=1000 + M * 7 + K + N)
+    try:
+        w4.w4a16_set_tuning("gemv_mma=0")
+        assert w4.w4a16_gemm_plan(M, K, N, G)[0] == 1
+        got = run_gemm(p)
+    finally:
+        w4.w4a16_set_tuning(None)
+    want = oracle.gemm(p["a"], p["b_packed"], p["scales"], p["qzeros"], G, 8)
+    check_close(got, want, "dot2 M=%d K=%d N=%d" % (M, K, N))
+
+
+TUNED_FORMS = ["gemv_mma=0", "gemv_mma=0,gemv_fold=0", "gemv_mma=0,gemv_fold=1", "gemv_waves=4",
+               "gemv_waves=4,gemv_fold=1", "gemv_mma=0,gemv_splits=1", "gemv_mma=0,gemv_splits=7",
+               "gemv_mma=1", "gemv_mma=1,gemv_splits=1", "gemv_mma=1,gemv_splits=7",
+               "gemv_max_m=0", "mfma_cfg=4", "mfma_cfg=5,mfma_splits=3",
                "mfma_cfg=3", "mfma_cfg=6", "mfma_cfg=6,mfma_splits=3", "mfma_mgroup=1", "mfma_mgroup=2",
                "mfma_cfg=4,mfma_mgroup=3", "mfma_cfg=1,mfma_mgroup=4,mfma_splits=2"]
 
 
 @pytest.mark.parametrize("spec", TUNED_FORMS)
 def test_gemm_tuned_forms_match_oracle(spec):
-    """Every planner override computes the same product (the exact and folded
-    GEMV forms, 4- and 8-wave workgroups, forced split counts, the MFMA path
+    """Every planner override computes the same product (the dot2 GEMV's exact
+    and folded forms, the matrix-core GEMV at every M, 4- and 8-wave
+    workgroups, forced split counts (uneven per wave included), the MFMA path
     at small M, the alternative MFMA tile shapes, the workgroup orders over
     row tiles, including a ragged last band)."""
     try:
@@ -147,13 +165,15 @@ def f16_ulp(x):
 
 @pytest.mark.parametrize("M", [1, 2, 5, 8, 12, 32, 256])
 def test_gemm_identities(M):
-    """All-8 nibbles with zero point 8 give exactly 0 (also in the folded GEMV
-    form, whose zero correction runs the same dot chain); qzeros all 8 equal
+    """All-8 nibbles with zero point 8 give exactly 0 on the dot2 GEMV (also
+    in its folded form, whose zero correction runs the same dot chain) and the
+    MFMA GEMM, and 0 within the tolerance on the matrix-core GEMV (its zero
+    correction runs on separately rounded activation sums); qzeros all 8 equal
     the symmetric call bit for bit where both take the same arithmetic form
-    (the default folds only symmetric GEMVs at M <= 2: there, within the
+    (the default folds only symmetric dot2 GEMVs at M <= 2: there, within the
     tolerance, and bit for bit with the exact form forced); doubling every
     scale doubles the output -- exactly where the K-splits meet in fp32, and
-    to within one fp16 step where the GEMV's K-splits meet in 2^-26 fixed point
+    to within one fp16 step where the GEMVs' K-splits meet in 2^-26 fixed point
     (each split's partial is rounded to that grid, which does not commute with
     doubling)."""
     K, N, G = 1024, 512, 128
@@ -162,7 +182,10 @@ def test_gemm_identities(M):
     a, b, s = dev(p["a"]), dev(p["b_packed"]), dev(p["scales"])
     eights = torch.full_like(b, np.uint32(0x88888888).view(np.int32).item())
     zero = host(w4.w4a16_gemm(a, eights, s, None, G, 8))
-    assert np.all(zero == 0)
+    if path == 3:
+        check_close(zero, np.zeros_like(zero), "all-zp columns, matrix-core GEMV")
+    else:
+        assert np.all(zero == 0)
     qz8 = torch.full((K // G, N // 8), np.uint32(0x88888888).view(np.int32).item(), dtype=torch.int32, device="cuda")
     sym = host(w4.w4a16_gemm(a, b, s, None, G, 8))
     asym = host(w4.w4a16_gemm(a, b, s, qz8, G, 3))
@@ -179,7 +202,7 @@ def test_gemm_identities(M):
         assert np.array_equal(sym.view(np.uint16), asym.view(np.uint16))
     dbl = host(w4.w4a16_gemm(a, b, s * 2, None, G, 8)).astype(np.float64)
     two = 2 * sym.astype(np.float64)
-    if path == 1 and splits > 1:
+    if path in (1, 3) and splits > 1:
         assert np.all(np.abs(dbl - two) <= f16_ulp(two))
     else:
         assert np.array_equal(dbl, two)

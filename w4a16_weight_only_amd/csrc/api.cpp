@@ -56,6 +56,7 @@ struct Tune {
     int64_t gemv_splits = 0;           // force the GEMV K-split count
     int64_t gemv_fold = -1;            // bias/zero removed per chunk: 1 always, 0 never, -1 symmetric M <= 2
     int64_t gemv_max_m = 8;            // largest M sent to the GEMV path (at most 8)
+    int64_t gemv_mma = 1;              // GEMV k-reduction on the matrix cores (0: the dot2 GEMV)
     int64_t mfma_target_waves = 2048;  // aim for about this many MFMA-path waves
     int64_t mfma_splits = 0;           // force the MFMA split count
     int64_t mfma_cfg = 0;  // force (mt, waves, kwaves): 1..6 = (1,2,4) (2,2,4) (4,2,2) (2,1,8) (4,2,4) (4,1,8)
@@ -86,6 +87,8 @@ bool parse_tune(const char *spec, Tune *out) {
         else if (k == "gemv_splits") v.gemv_splits = val;
         else if (k == "gemv_fold") v.gemv_fold = val;
         else if (k == "gemv_max_m") v.gemv_max_m = val;
+        else if (k == "gemv_mma") v.gemv_mma = val;
+
         else if (k == "mfma_target_waves") v.mfma_target_waves = val;
         else if (k == "mfma_splits") v.mfma_splits = val;
         else if (k == "mfma_cfg") v.mfma_cfg = val;
@@ -134,8 +137,7 @@ int validate_sizes(int64_t M, int64_t K, int64_t N, int64_t G) {
 
 namespace w4a16 {
 
-GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G) {
-    (void)G;
+GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma) {
     const Tune &t = tune();
     GemmPlan p;
     const int64_t N8 = N / 8;
@@ -178,6 +180,26 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G) {
         p.split_len = cdiv(nchunks, splits);
         p.splits = (int)cdiv(nchunks, p.split_len);
         p.tiles_m = 1;
+        // The matrix-core GEMV (gemv_mma_kernel) needs far fewer vector-ALU
+        // instructions per weight than the dot2 form; its products are summed
+        // less finely (about 1e-4 of the output: subnormal-encoded weights on
+        // the matrix core) but far inside the tolerance.  Measured on MI355X,
+        // with one round of workgroups (256 / tiles splits, waves of a split
+        // taking unequal chunk counts where they do not divide): the headline
+        // M = 1 K = 4096 N = 12800 8.57 -> 7.94 us, K = 12800 N = 4096
+        // 9.50 -> 7.88 us, K = 8192 N = 8192 11.9 -> 9.0 us, and 40-53% less
+        // time at M = 8.  Rounding the splits down to equal chunk counts per
+        // wave (one round fewer workgroups) was slower at M <= 2 (headline
+        // 8.56 us).
+        if (allow_mma && p.waves == 8 && t.gemv_mma != 0) {
+            const int64_t mchunks = K / kMmaChunkRows;
+            int64_t ms = t.gemv_splits > 0 ? t.gemv_splits : std::max<int64_t>(1, 256 / p.tiles_n);
+            ms = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(ms, 32), mchunks));
+            p.split_len = cdiv(mchunks, ms);
+            p.splits = (int)cdiv(mchunks, p.split_len);
+            p.mma = true;
+            p.fold = p.fold_asym = false;
+        }
     } else {
         // MFMA: wave tile (16*mt rows) x 128 columns; `waves` along N and
         // `kwaves` along K per workgroup (one workgroup per CU); K-splits
@@ -361,7 +383,7 @@ int run_gemm(const uint16_t *a, const int32_t *b, const uint16_t *s, const int32
              int64_t K, int64_t N, int64_t G, int32_t zp, uint16_t *out, hipStream_t stream,
              bool exact_form = false) {
     if (M == 0) return ok();
-    GemmPlan plan = plan_gemm(M, K, N, G);
+    GemmPlan plan = plan_gemm(M, K, N, G, !exact_form);
     if (exact_form) plan.fold = plan.fold_asym = false;
     GemmArgs args{a, b, s, qz, M, K, N, G, zp, out, nullptr, nullptr};
     int rc = get_scratch(stream, plan, &args.partials, &args.counters);
@@ -375,7 +397,7 @@ int run_gemm(const uint16_t *a, const int32_t *b, const uint16_t *s, const int32
 // SwiGLU + row-norm) of `src` (row stride ld), for the decode step.
 int run_gemm_act(int act, const uint16_t *src, int64_t ld, const w4a16_linear &L, int64_t M, int64_t K, int64_t N,
                  uint16_t *out, hipStream_t stream) {
-    GemmPlan plan = plan_gemm(M, K, N, L.G);
+    GemmPlan plan = plan_gemm(M, K, N, L.G, false);
     if (plan.path == kPathMfma) {
         if (act != 1) return fail(W4A16_ERR_UNSUPPORTED, "the MFMA path folds the row-norm only");
         plan.partial_floats += mfma_rn_extra_floats(plan);
@@ -475,7 +497,7 @@ int w4a16_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t G, int32_t *path, i
     int rc = validate_sizes(M, K, N, G);
     if (rc != W4A16_OK) return rc;
     const GemmPlan p = plan_gemm(std::max<int64_t>(M, 1), K, N, G);
-    if (path) *path = p.path;
+    if (path) *path = p.mma ? 3 : p.path;
     if (splits) *splits = p.splits;
     if (grid) *grid = p.grid;
     return ok();

@@ -145,6 +145,60 @@ __device__ __forceinline__ float sq_chain(const u32x4 &x, const u32x4 &y, float 
     return ss;
 }
 
+// Sums the workgroup's per-wave partials of a 256-column tile (red) in wave
+// order, multiplies row m by row_scale(m), and writes the tile: directly with
+// one K-split, else through one fixed-point slot per output (device.h), every
+// atomic issued before the first result is looked at.
+template <int M, int NW, typename RowScale>
+__device__ __forceinline__ void finish_tile(const float (&red)[NW][M][kTileCols], RowScale row_scale, int tile,
+                                            int N, int splits, uint16_t *__restrict__ out,
+                                            uint32_t *__restrict__ counters) {
+    // One (row, column) per thread and pass.
+    constexpr int PASSES = (M * kTileCols + 64 * NW - 1) / (64 * NW);
+    const int col_base = tile * kTileCols;
+    float sums[PASSES];
+#pragma unroll
+    for (int i = 0; i < PASSES; ++i) {
+        const int t = threadIdx.x + i * 64 * NW;
+        float s = 0.f;
+        if (t < M * kTileCols) {
+#pragma unroll
+            for (int wv = 0; wv < NW; ++wv) s += red[wv][t / kTileCols][t % kTileCols];
+            s *= row_scale(t / kTileCols);
+        }
+        sums[i] = s;
+    }
+    if (splits == 1) {
+#pragma unroll
+        for (int i = 0; i < PASSES; ++i) {
+            const int t = threadIdx.x + i * 64 * NW;
+            const int col = col_base + t % kTileCols;
+            if (t < M * kTileCols && col < N) out[(size_t)(t / kTileCols) * N + col] = f32_to_f16_bits(sums[i]);
+        }
+        return;
+    }
+    uint64_t *slots = reinterpret_cast<uint64_t *>(counters);
+    uint64_t add[PASSES], old[PASSES];
+#pragma unroll
+    for (int i = 0; i < PASSES; ++i) {
+        const int t = threadIdx.x + i * 64 * NW;
+        const int col = col_base + t % kTileCols;
+        add[i] = slot_contribution(sums[i]);
+        old[i] = 0;
+        if (t < M * kTileCols && col < N) old[i] = slot_add(&slots[(size_t)(t / kTileCols) * N + col], add[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < PASSES; ++i) {
+        const int t = threadIdx.x + i * 64 * NW;
+        const int col = col_base + t % kTileCols;
+        if (t < M * kTileCols && col < N && slot_last(old[i], splits)) {
+            const size_t o = (size_t)(t / kTileCols) * N + col;
+            out[o] = slot_result_f16(old[i] + add[i], splits);
+            slot_reset(&slots[o]);
+        }
+    }
+}
+
 template <int M, int WORDS, int NW, bool ASYM, bool FOLD, int ACT, int RV>
 __global__ __launch_bounds__(64 * NW) void gemv_kernel(
     const uint16_t *__restrict__ a, const uint16_t *__restrict__ src, int ld, const uint32_t *__restrict__ b,
@@ -478,59 +532,201 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
         *reinterpret_cast<f32x4 *>(&red[wave][m][cl * COLS + 4 * rl]) = v;
     }
     __syncthreads();
-
-    // Epilogue: one (row, column) per thread and pass.
-    constexpr int PASSES = (M * kTileCols + 64 * NW - 1) / (64 * NW);
-    const int col_base = tile * kTileCols;
-    float sums[PASSES];
-#pragma unroll
-    for (int i = 0; i < PASSES; ++i) {
-        const int t = threadIdx.x + i * 64 * NW;
-        float s = 0.f;
-        if (t < M * kTileCols) {
-#pragma unroll
-            for (int wv = 0; wv < NW; ++wv) s += red[wv][t / kTileCols][t % kTileCols];
+    finish_tile<M, NW>(
+        red,
+        [&](int m) __attribute__((always_inline)) {
             if constexpr (ACT != 0) {
                 float q = 0.f;
 #pragma unroll
-                for (int w = 0; w < 16; ++w) q += s_part[w][t / kTileCols];
-                s *= row_inv(q, K);
+                for (int w = 0; w < 16; ++w) q += s_part[w][m];
+                return row_inv(q, K);
+            } else {
+                return 1.0f;
             }
-        }
-        sums[i] = s;
-    }
-    if (splits == 1) {
+        },
+        tile, N, splits, out, counters);
+}
+
+// ------------------------------------------------------------- MFMA form ---
+// The same tiles, K-splits and hand-off with the k-reduction on the matrix
+// cores: per 16-row set one v_mfma_f32_16x16x32_f16 takes the weights of 16
+// lanes' columns as B and the activations as A.  Measured against the dot2
+// form above, the vector ALUs then do about 0.8 instructions per weight
+// instead of 1.4 (M = 1) to 4.75 (M = 8):
+//
+//  * Weights as fp16 subnormals.  AND-ing a packed word with 0x000F000F gives
+//    nibbles 0 and 4 in the two fp16 halves, each worth q * 2^-24 exactly
+//    (binary16 subnormals are integers times 2^-24); 0x00F000F0 gives nibbles
+//    1 and 5 worth 16 q * 2^-24; the word shifted right by 8 gives nibbles
+//    2, 6 and 3, 7 the same way.  One AND per two weights, no bias to remove.
+//  * Two columns per register.  A register of the B operand holds (column c,
+//    column c + 4) of one weight row: its two k-slots.  Activation row mu
+//    occupies A rows 2 mu and 2 mu + 1, which hold the row's activations in
+//    the even and in the odd k-slots only, so D row 2 mu + e collects column
+//    c + 4e.  Up to 8 activation rows fill the 16 A rows.
+//  * Zero point folded per chunk.  A ninth MFMA per set multiplies the same A
+//    by 2^-24 in every slot, giving sum(a) * 2^-24 in the layout of the
+//    products; the chunk's (q - z) sums are D - z' * that (z' = z or 16 z),
+//    scaled by the group scale into an fp32 total, and the 2^24 (2^20) is
+//    applied once at the end.  A zero point that is a power of two cancels
+//    all-z columns exactly (a scaling by a power of two commutes with the
+//    matrix core's rounding).
+//
+// Lane (j, g) = (lane % 16, lane / 16) loads words 2j, 2j+1 of the tile (8
+// bytes of each row) for rows 16 s + 4 g + i (i < 4) of set s, and the
+// activations of row mu = j / 2 at those rows.  A wave takes chunks of CH rows
+// (CH divides G, so a chunk lies in one group) and issues all of a chunk's
+// loads before its first wait.
+template <int M, bool ASYM>
+__global__ __launch_bounds__(512) void gemv_mma_kernel(
+    const uint16_t *__restrict__ a, const uint32_t *__restrict__ b, const uint16_t *__restrict__ scales,
+    const uint32_t *__restrict__ qzeros, int K, int N, int G, uint32_t zp, int tiles, int split_len, int splits,
+    uint16_t *__restrict__ out, uint32_t *__restrict__ counters) {
+    static_assert(M >= 1 && M <= 8, "two A rows per activation row");
+    constexpr int NW = 8;
+    constexpr int CH = kMmaChunkRows;
+    constexpr int SETS = CH / 16;
+    constexpr int RV = M >= 2 ? 4 : 2;  // D elements that can hold rows < M (D row 4 g + v)
+    const int logical = xcd_local_index(blockIdx.x, gridDim.x);
+    if (logical >= tiles * splits) return;
+    const int tile = logical % tiles;
+    const int split = logical / tiles;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int j = lane & 15;
+    const int g = lane >> 4;
+    const int N8 = N >> 3;
+    // Lanes past N read a valid (clamped) address; their columns are never stored.
+    const int word = min(tile * kTileWords + 2 * j, N8 - 2);
+    const int nchunks = K / CH;
+    const int c_begin = split * split_len;
+    const int c_end = min(c_begin + split_len, nchunks);
+    const uint32_t row_bytes = (uint32_t)N8 * 4u;
+    const __amdgpu_buffer_rsrc_t brs = buffer_rsrc(b, (uint32_t)((uint64_t)K * N8 * 4));
+    const __amdgpu_buffer_rsrc_t srs = buffer_rsrc(scales, (uint32_t)((uint64_t)(K / G) * N * 2));
+    const __amdgpu_buffer_rsrc_t zrs = buffer_rsrc(qzeros, ASYM ? (uint32_t)((uint64_t)(K / G) * row_bytes) : 0u);
+    const __amdgpu_buffer_rsrc_t ars = buffer_rsrc(a, (uint32_t)((uint64_t)M * K * 2));
+    const uint32_t b_voff = ((uint32_t)(4 * g) * (uint32_t)N8 + (uint32_t)word) * 4u;
+    const int mu = j >> 1;
+    const uint32_t a_voff = ((uint32_t)min(mu, M - 1) * (uint32_t)K + 4u * (uint32_t)g) * 2u;
+    // v_perm selectors placing activation 2r (sel0) or 2r + 1 (sel1) of a
+    // loaded pair in fp16 half (j & 1) of an A register, the other half zero;
+    // lanes of rows mu >= M give zeros.
+    uint32_t sel0 = (j & 1) ? 0x01000c0cu : 0x0c0c0100u;
+    uint32_t sel1 = (j & 1) ? 0x03020c0cu : 0x0c0c0302u;
+    if (mu >= M) sel0 = sel1 = 0x0c0c0c0cu;
+
+    f32x4 tot[2][4];
 #pragma unroll
-        for (int i = 0; i < PASSES; ++i) {
-            const int t = threadIdx.x + i * 64 * NW;
-            const int col = col_base + t % kTileCols;
-            if (t < M * kTileCols && col < N) out[(size_t)(t / kTileCols) * N + col] = f32_to_f16_bits(sums[i]);
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tot[x][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    struct Chunk {
+        u32x4 sv[2];     // scales of the lane's 16 columns
+        u32x2 zw;        // packed zeros of its two words (ASYM)
+        u32x2 av[SETS];  // activations of row mu at the lane's 4 rows of each set
+        u32x2 w[SETS][4];
+    };
+    auto load_chunk = [&](int c, Chunk &d) __attribute__((always_inline)) {
+        const uint32_t k0 = (uint32_t)c * CH;
+        const uint32_t grp = k0 / (uint32_t)G;
+        d.sv[0] = buffer_load_x4(srs, (uint32_t)word * 16u, grp * (uint32_t)N * 2u);
+        d.sv[1] = buffer_load_x4(srs, (uint32_t)word * 16u + 16u, grp * (uint32_t)N * 2u);
+        d.zw = u32x2{0u, 0u};
+        if constexpr (ASYM) d.zw = buffer_load_x2(zrs, (uint32_t)word * 4u, grp * row_bytes);
+#pragma unroll
+        for (int s = 0; s < SETS; ++s) d.av[s] = buffer_load_x2(ars, a_voff, (k0 + 16u * s) * 2u);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < SETS; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) d.w[s][i] = buffer_load_x2_nt(brs, b_voff, (k0 + 16u * s + i) * row_bytes);
+    };
+    // Products of one chunk into acc (per word x and nibble pair q) and the
+    // activation sums into asum.
+    f32x4 acc[2][4], asum;
+    auto zero_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[x][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        asum = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    auto mma_chunk = [&](const Chunk &d) __attribute__((always_inline)) {
+        const f16x8 unit = __builtin_bit_cast(f16x8, u32x4{0x00010001u, 0x00010001u, 0x00010001u, 0x00010001u});
+#pragma unroll
+        for (int s = 0; s < SETS; ++s) {
+            const uint32_t lo = d.av[s].x, hi = d.av[s].y;
+            const f16x8 av = __builtin_bit_cast(
+                f16x8, u32x4{__builtin_amdgcn_perm(0u, lo, sel0), __builtin_amdgcn_perm(0u, lo, sel1),
+                             __builtin_amdgcn_perm(0u, hi, sel0), __builtin_amdgcn_perm(0u, hi, sel1)});
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                uint32_t p[4][4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t w = x ? d.w[s][i].y : d.w[s][i].x;
+                    const uint32_t sh = w >> 8;
+                    p[0][i] = w & kMaskLo;
+                    p[1][i] = w & kMaskHi;
+                    p[2][i] = sh & kMaskLo;
+                    p[3][i] = sh & kMaskHi;
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    acc[x][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        av, __builtin_bit_cast(f16x8, u32x4{p[q][0], p[q][1], p[q][2], p[q][3]}), acc[x][q], 0, 0, 0);
+            }
+            asum = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, unit, asum, 0, 0, 0);
         }
-        return;
+    };
+    // End of a group: (q - z) sums times the group scale into tot.  acc[x][q]
+    // element v is D row 4 g + v = (row 2 g + v / 2, half e = v & 1), column
+    // 8 (word + x) + q + 4 e of the lane's words.
+    auto flush = [&](const u32x4 (&sv)[2], const u32x2 &zw) __attribute__((always_inline)) {
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            const uint32_t zword = x ? zw.y : zw.x;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int v = 0; v < RV; ++v) {
+                    const int c = q + 4 * (v & 1);  // column within the word
+                    const float s = f16_bits_to_f32((sv[x][c >> 1] >> (16 * (c & 1))) & 0xffffu);
+                    const uint32_t z = ASYM ? (zword >> (4 * c)) & 0xfu : zp;
+                    const float zs = (float)((q & 1) ? 16u * z : z);
+                    tot[x][q][v] = __builtin_fmaf(s, __builtin_fmaf(-zs, asum[v], acc[x][q][v]), tot[x][q][v]);
+                }
+        }
+    };
+
+    // chunks c_begin + wave, + 8, ...: the workgroup's waves read consecutive rows
+    for (int c = c_begin + wave; c < c_end; c += NW) {
+        Chunk d;
+        load_chunk(c, d);
+        zero_acc();
+        mma_chunk(d);
+        flush(d.sv, d.zw);
     }
 
-    // Split-K: one fixed-point atomic per output and split (device.h); every
-    // atomic is issued before the first result is looked at.
-    uint64_t *slots = reinterpret_cast<uint64_t *>(counters);
-    uint64_t add[PASSES], old[PASSES];
+    __shared__ float red[NW][M][kTileCols];
 #pragma unroll
-    for (int i = 0; i < PASSES; ++i) {
-        const int t = threadIdx.x + i * 64 * NW;
-        const int col = col_base + t % kTileCols;
-        add[i] = slot_contribution(sums[i]);
-        old[i] = 0;
-        if (t < M * kTileCols && col < N) old[i] = slot_add(&slots[(size_t)(t / kTileCols) * N + col], add[i]);
-    }
+    for (int v = 0; v < RV; ++v) {
+        const int m = 2 * g + (v >> 1);
+        if (m < M) {
 #pragma unroll
-    for (int i = 0; i < PASSES; ++i) {
-        const int t = threadIdx.x + i * 64 * NW;
-        const int col = col_base + t % kTileCols;
-        if (t < M * kTileCols && col < N && slot_last(old[i], splits)) {
-            const size_t o = (size_t)(t / kTileCols) * N + col;
-            out[o] = slot_result_f16(old[i] + add[i], splits);
-            slot_reset(&slots[o]);
+            for (int x = 0; x < 2; ++x) {
+                // undo the subnormal encoding: 2^24 for nibbles 0, 2 (q = 0, 2), 2^20 for 1, 3
+                const f32x4 o = {tot[x][0][v] * 16777216.f, tot[x][1][v] * 1048576.f, tot[x][2][v] * 16777216.f,
+                                 tot[x][3][v] * 1048576.f};
+                *reinterpret_cast<f32x4 *>(&red[wave][m][16 * j + 8 * x + 4 * (v & 1)]) = o;
+            }
         }
     }
+    __syncthreads();
+    finish_tile<M, NW>(red, [](int) { return 1.0f; }, tile, N, splits, out, counters);
 }
 
 template <int M, int WORDS, int NW, bool ASYM, bool FOLD, int ACT, int RV = 1>
@@ -579,15 +775,42 @@ hipError_t launch_m(const GemmArgs &g, const GemmPlan &p, int act, const uint16_
     return p.waves == 8 ? launch_v<M, WORDS, 8>(g, p, stream) : launch_v<M, WORDS, 4>(g, p, stream);
 }
 
+template <int M, bool ASYM>
+hipError_t launch_mma_z(const GemmArgs &g, const GemmPlan &p, hipStream_t stream) {
+    hipLaunchKernelGGL((gemv_mma_kernel<M, ASYM>), dim3((unsigned)p.grid), dim3(512), 0, stream, g.a,
+                       reinterpret_cast<const uint32_t *>(g.b), g.scales, reinterpret_cast<const uint32_t *>(g.qzeros),
+                       (int)g.K, (int)g.N, (int)g.G, (uint32_t)g.zp, (int)p.tiles_n, (int)p.split_len, p.splits,
+                       g.out, g.counters);
+    return hipGetLastError();
+}
+
+template <int M>
+hipError_t launch_mma(const GemmArgs &g, const GemmPlan &p, hipStream_t stream) {
+    return g.qzeros ? launch_mma_z<M, true>(g, p, stream) : launch_mma_z<M, false>(g, p, stream);
+}
+
 }  // namespace
 
 hipError_t launch_gemv(const GemmArgs &g, const GemmPlan &p, hipStream_t stream) {
-    return launch_gemv_act(g, p, 0, nullptr, 0, stream);
+    if (!p.mma) return launch_gemv_act(g, p, 0, nullptr, 0, stream);
+    if (p.splits > kMaxSplits || p.waves != 8 || g.N % 32 != 0 || g.G % kMmaChunkRows != 0)
+        return hipErrorInvalidValue;
+    switch (g.M) {
+        case 1: return launch_mma<1>(g, p, stream);
+        case 2: return launch_mma<2>(g, p, stream);
+        case 3: return launch_mma<3>(g, p, stream);
+        case 4: return launch_mma<4>(g, p, stream);
+        case 5: return launch_mma<5>(g, p, stream);
+        case 6: return launch_mma<6>(g, p, stream);
+        case 7: return launch_mma<7>(g, p, stream);
+        case 8: return launch_mma<8>(g, p, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_gemv_act(const GemmArgs &g, const GemmPlan &p, int act, const uint16_t *src, int64_t ld,
                            hipStream_t stream) {
-    if (p.splits > kMaxSplits) return hipErrorInvalidValue;
+    if (p.splits > kMaxSplits || p.mma) return hipErrorInvalidValue;
     if (act != 0 && (p.waves != 8 || !src || ld % 8 != 0 || g.K % 8 != 0 || g.K > kGlueMaxWidth))
         return hipErrorInvalidValue;
     switch (g.M) {

@@ -9,6 +9,9 @@
 namespace w4a16 {
 
 enum GemmPath { kPathGemv = 1, kPathMfma = 2 };
+// Rows per chunk of the matrix-core GEMV (a multiple of 16 dividing every G,
+// which is a multiple of 32).
+constexpr int kMmaChunkRows = 32;
 
 // Everything a GEMM launch needs besides the tensors; computed on the host
 // from (M, K, N, G) alone so that it can be inspected without a GPU.
@@ -20,6 +23,8 @@ struct GemmPlan {
     int waves = 4;
     int mt = 1;
     int kwaves = 1;           // MFMA: waves dividing a workgroup's K range (LDS-reduced)
+    bool mma = false;         // GEMV with the k-reduction on the matrix cores (split_len in
+                              // kMmaChunkRows-row chunks); false: the dot2 GEMV
     bool fold = false;        // GEMV, symmetric zero point: remove bias and zero per chunk, not per pair
     bool fold_asym = false;   // the same with packed zeros
     int64_t tiles_n = 0;      // workgroup tiles along N
@@ -27,7 +32,8 @@ struct GemmPlan {
     int m_group = 1;          // MFMA: consecutive workgroups walk this many row tiles of one
                               // column tile before the next column tile (shared weights in L2)
     int splits = 1;           // K-splits across workgroups
-    int64_t split_len = 0;    // K-units per split (GEMV: 16-row chunks; MFMA: 32-row steps)
+    int64_t split_len = 0;    // K-units per split (GEMV: 16-row chunks, 32 with mma; MFMA:
+                              // 32-row steps)
     int64_t grid = 0;         // workgroups launched
     size_t partial_floats = 0;  // fp32 split-K partials needed (0 when splits == 1)
     size_t counters = 0;        // zero-initialised words needed: MFMA arrival counters,
@@ -46,7 +52,9 @@ struct GemmArgs {
     uint32_t *counters;  // plan.counters zero-initialised words (or null)
 };
 
-GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G);
+// allow_mma = false keeps a GEMV plan on the dot2 kernel (the glue-fused
+// variants exist only there).
+GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma = true);
 
 hipError_t launch_gemv(const GemmArgs &args, const GemmPlan &plan, hipStream_t stream);
 // GEMV with the decode step's glue folded in: act 1: out = (src . W) * inv_row,
