@@ -332,39 +332,43 @@ def test_decode_step_small_stack(M):
     assert rel < 1e-2
 
 
+def tuned(spec, fn):
+    try:
+        w4.w4a16_set_tuning(spec)
+        return fn()
+    finally:
+        w4.w4a16_set_tuning(None)
+
+
+@pytest.mark.parametrize("gemv", ["", "gemv_mma=0"])
 @pytest.mark.parametrize("M", [1, 2, 5, 12, 24])
 @pytest.mark.parametrize("H,NQ,I", [(256, 384, 512), (512, 768, 9216), (512, 512, 17408)])
-def test_decode_step_fused_matches_unfused(M, H, NQ, I):
+def test_decode_step_fused_matches_unfused(M, H, NQ, I, gemv):
     """At M <= 8 the row-norm and SwiGLU glue runs inside the consuming GEMVs
-    (the row scale applied to the products) and a layer's output row-norm
-    inside the next layer's QKV; at M >= 9 the row-norms run inside the
-    consuming MFMA GEMMs the same way (SwiGLU stays a kernel).  One layer matches the unfused step
-    (separate glue kernels, forced with decode_fuse=0) and the oracle at the
-    per-element bound; two layers (the cross-layer fold) match the unfused
+    (the row scale applied to the products; the matrix-core GEMV by default,
+    the dot2 GEMV with gemv_mma=0) and a layer's output row-norm inside the
+    next layer's QKV; at M >= 9 the row-norms run inside the consuming MFMA
+    GEMMs the same way (SwiGLU stays a kernel).  One layer matches the unfused
+    step (separate glue kernels, forced with decode_fuse=0) and the oracle at
+    the per-element bound; two layers (the cross-layer fold) match the unfused
     step to relative L2 <= 1e-2.  Row widths up to 17408 cover one, two and
     four 8-element vectors per virtual thread of the row sums."""
+    if gemv and M > 8:
+        pytest.skip("the GEMV forms apply at M <= 8 only")
     G, nl = 128, 2
     layers = []
     for l in range(nl):
         layers += synth.stack_layer(l, H=H, NQ=NQ, I=I, G=G, seed_base=1700)
     x = dev(synth.stack_input(M, H, seed=40 + M))
     dstack = dev_stack(layers)
-    note("decode fused vs unfused M=%d H=%d I=%d" % (M, H, I))
-    fused = host(w4.w4a16_decode_step(dstack, x))
-    try:
-        w4.w4a16_set_tuning("decode_fuse=0")
-        unfused = host(w4.w4a16_decode_step(dstack, x))
-    finally:
-        w4.w4a16_set_tuning(None)
+    note("decode fused vs unfused M=%d H=%d I=%d %s" % (M, H, I, gemv))
+    fused = tuned(gemv, lambda: host(w4.w4a16_decode_step(dstack, x)))
+    unfused = tuned("decode_fuse=0", lambda: host(w4.w4a16_decode_step(dstack, x)))
     rel = np.linalg.norm(fused.astype(np.float64) - unfused) / np.linalg.norm(unfused.astype(np.float64))
     note("decode fused vs unfused M=%d I=%d two layers relative L2 %.3g" % (M, I, rel))
     assert rel < 1e-2
-    first = host(w4.w4a16_decode_step(dstack[:4], x))
-    try:
-        w4.w4a16_set_tuning("decode_fuse=0")
-        first_unfused = host(w4.w4a16_decode_step(dstack[:4], x))
-    finally:
-        w4.w4a16_set_tuning(None)
+    first = tuned(gemv, lambda: host(w4.w4a16_decode_step(dstack[:4], x)))
+    first_unfused = tuned("decode_fuse=0", lambda: host(w4.w4a16_decode_step(dstack[:4], x)))
     check_close(first, first_unfused, "fused vs unfused layer 0 M=%d I=%d" % (M, I), tol=FUSED_LAYER_TOL)
     want = oracle.decode_step(layers[:4], host(x), 1)
     check_close(first, want, "fused layer 0 M=%d I=%d" % (M, I), tol=FUSED_LAYER_TOL)
@@ -413,9 +417,10 @@ def test_decode_step_in_place_and_rms():
     assert np.allclose(rms, 1.0, atol=5e-3)
 
 
+@pytest.mark.parametrize("gemv", ["", "gemv_mma=0"])
 @pytest.mark.parametrize("M", [1, 2, 5, 12, 24])
 @pytest.mark.parametrize("I", [9216, 12800])
-def test_decode_step_down_projection_intermediate(M, I):
+def test_decode_step_down_projection_intermediate(M, I, gemv):
     """White box: the step's output is row-normed, which hides a wrong row
     scale in any linear before it.  After a one-layer step the workspace holds
     the down projection's output and its input: at M <= 8 (SwiGLU + row-norm
@@ -432,8 +437,10 @@ def test_decode_step_down_projection_intermediate(M, I):
     x = dev(synth.stack_input(M, H, seed=90 + M))
     buf = (M * max(L["N"] for L in layers) * 2 + 255) // 256 * 256
     ws = torch.zeros(2 * buf, dtype=torch.uint8, device="cuda")
-    note("decode down intermediate M=%d I=%d" % (M, I))
-    w4.w4a16_decode_step(dev_stack(layers), x, workspace=ws)
+    if gemv and M > 8:
+        pytest.skip("the GEMV forms apply at M <= 8 only")
+    note("decode down intermediate M=%d I=%d %s" % (M, I, gemv))
+    tuned(gemv, lambda: w4.w4a16_decode_step(dev_stack(layers), x, workspace=ws))
     w = host(ws)
     D = layers[3]
     if M <= 8:

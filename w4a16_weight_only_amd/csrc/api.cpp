@@ -376,9 +376,9 @@ int validate_gemm(const uint16_t *a, const int32_t *b, const uint16_t *s, const 
     return W4A16_OK;
 }
 
-// exact_form: the GEMV keeps (q - z) exact per weight (no folded zero
-// correction).  The decode step's separate-kernel route uses it for every
-// linear (the oracle's roundings), and the fused route for layer 0's QKV.
+// exact_form: the dot2 GEMV keeping (q - z) exact per weight (no folded zero
+// correction, no matrix cores).  The decode step's separate-kernel route uses
+// it for every linear (the oracle's roundings).
 int run_gemm(const uint16_t *a, const int32_t *b, const uint16_t *s, const int32_t *qz, int64_t M,
              int64_t K, int64_t N, int64_t G, int32_t zp, uint16_t *out, hipStream_t stream,
              bool exact_form = false) {
@@ -397,7 +397,7 @@ int run_gemm(const uint16_t *a, const int32_t *b, const uint16_t *s, const int32
 // SwiGLU + row-norm) of `src` (row stride ld), for the decode step.
 int run_gemm_act(int act, const uint16_t *src, int64_t ld, const w4a16_linear &L, int64_t M, int64_t K, int64_t N,
                  uint16_t *out, hipStream_t stream) {
-    GemmPlan plan = plan_gemm(M, K, N, L.G, false);
+    GemmPlan plan = plan_gemm(M, K, N, L.G);
     if (plan.path == kPathMfma) {
         if (act != 1) return fail(W4A16_ERR_UNSUPPORTED, "the MFMA path folds the row-norm only");
         plan.partial_floats += mfma_rn_extra_floats(plan);
@@ -556,7 +556,7 @@ int w4a16_decode_step(const w4a16_linear *lin, int64_t n_layers, const uint16_t 
         uint16_t *o = other(q);
         if ((rc = qkv_rn ? run_gemm_act(1, pend, H, L[0], M, H, NQ, q, stream)
                          : run_gemm(x, L[0].b_packed, L[0].scales, L[0].qzeros, M, H, NQ, L[0].G, L[0].zp_bias,
-                                    q, stream, true)))
+                                    q, stream, !fuse)))
             return rc;
         if (gemv_route) {
             // q -> o (O), o -> q (gate+up), q -> o (down)

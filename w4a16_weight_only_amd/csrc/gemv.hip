@@ -145,6 +145,79 @@ __device__ __forceinline__ float sq_chain(const u32x4 &x, const u32x4 &y, float 
     return ss;
 }
 
+// Row sums of squares of the glue-transformed rows (ACT 1, 2) for a
+// 512-thread workgroup, in the glue kernels' order (sq_chain).  With EARLY
+// (M <= 2) load() requests the row's vectors before the weight stream and
+// holds them in registers (RV 16-byte vectors per virtual thread); otherwise
+// partials() streams them.  partials() is the per-lane part; reduce() the
+// cross-lane part, to be called where every lane of the wave is active; the
+// 16 per-wave sums of each row meet in s_part, which inv() reads.
+template <int M, int ACT, int RV, bool EARLY>
+struct RowSums {
+    static constexpr int kRM = EARLY ? M : 1, kRV = EARLY ? RV : 1;
+    u32x4 rx[kRM][2][kRV], ry[kRM][2][kRV];
+    float ss[M][2];
+
+    __device__ __forceinline__ void load(const uint16_t *src, int ld, int K) {
+        if constexpr (EARLY) {
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const __amdgpu_buffer_rsrc_t gr = buffer_rsrc(src + (size_t)m * ld, (uint32_t)K * 2u);
+                const __amdgpu_buffer_rsrc_t ur =
+                    buffer_rsrc(src + (size_t)m * ld + K, ACT == 2 ? (uint32_t)K * 2u : 0u);
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int j = 0; j < RV; ++j) {
+                        // a vector past the row reads zeros (adds exactly 0)
+                        const uint32_t off = ((uint32_t)threadIdx.x + 512u * h + 1024u * j) * 16u;
+                        rx[m][h][j] = buffer_load_x4(gr, off, 0);
+                        ry[m][h][j] = rx[m][h][j];
+                        if constexpr (ACT == 2) ry[m][h][j] = buffer_load_x4(ur, off, 0);
+                    }
+            }
+        }
+    }
+    __device__ __forceinline__ void partials(const uint16_t *src, int ld, int K) {
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                float t = 0.f;
+                if constexpr (EARLY) {
+#pragma unroll
+                    for (int j = 0; j < RV; ++j) t = sq_chain<ACT>(rx[m][h][j], ry[m][h][j], t);
+                } else {
+                    const uint16_t *row = src + (size_t)m * ld;
+                    for (int i = (int)threadIdx.x + 512 * h; i < K / 8; i += 1024) {
+                        const u32x4 x = *reinterpret_cast<const u32x4 *>(row + 8 * i);
+                        u32x4 y = x;
+                        if constexpr (ACT == 2) y = *reinterpret_cast<const u32x4 *>(row + K + 8 * i);
+                        t = sq_chain<ACT>(x, y, t);
+                    }
+                }
+                ss[m][h] = t;
+            }
+    }
+    __device__ __forceinline__ void reduce(float (&s_part)[16][M], int lane, int wave) {
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                float v = ss[m][h];
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+                if (lane == 0) s_part[8 * h + wave][m] = v;
+            }
+    }
+    static __device__ __forceinline__ float inv(const float (&s_part)[16][M], int m, int K) {
+        float q = 0.f;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) q += s_part[w][m];
+        return row_inv(q, K);
+    }
+};
+
 // Sums the workgroup's per-wave partials of a 256-column tile (red) in wave
 // order, multiplies row m by row_scale(m), and writes the tile: directly with
 // one K-split, else through one fixed-point slot per output (device.h), every
@@ -246,24 +319,9 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
     // starts costs an L2 round trip and two barriers per launch.)
     __shared__ float s_part[16][M];
     constexpr bool kEarlyRows = ACT != 0 && M <= 2;
-    constexpr int kRM = kEarlyRows ? M : 1, kRV = kEarlyRows ? RV : 1;
-    u32x4 rx[kRM][2][kRV], ry[kRM][2][kRV];
+    RowSums<M, ACT, RV, kEarlyRows> rows;
     if constexpr (kEarlyRows) {
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const __amdgpu_buffer_rsrc_t gr = buffer_rsrc(src + (size_t)m * ld, (uint32_t)K * 2u);
-            const __amdgpu_buffer_rsrc_t ur = buffer_rsrc(src + (size_t)m * ld + K, ACT == 2 ? (uint32_t)K * 2u : 0u);
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int j = 0; j < RV; ++j) {
-                    // a vector past the row reads zeros (adds exactly 0)
-                    const uint32_t off = ((uint32_t)threadIdx.x + 512u * h + 1024u * j) * 16u;
-                    rx[m][h][j] = buffer_load_x4(gr, off, 0);
-                    ry[m][h][j] = rx[m][h][j];
-                    if constexpr (ACT == 2) ry[m][h][j] = buffer_load_x4(ur, off, 0);
-                }
-        }
+        rows.load(src, ld, K);
         __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -425,49 +483,19 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
 
     const int c0 = c_begin + wave * RL + rl;
     constexpr int kStride = NW * RL;
-    // Row sums of squares of the transformed rows (the glue kernels' order:
-    // 1024 virtual threads, two chains per thread of the 512): a per-lane part
-    // (row_partials), reduced across the wave (row_reduce, where every lane of
-    // the wave is active) and across waves in the epilogue.  With the row held
-    // in registers (M <= 2) the per-lane part runs while the first chunk's
-    // weights are in flight; otherwise after the chunk loop.
-    float ss[M][2];
+    // Row sums: the per-lane part (row_partials) and the cross-lane part
+    // (row_reduce, where every lane of the wave is active), then across waves
+    // in the epilogue.  With the row held in registers (M <= 2) the per-lane
+    // part runs while the first chunk's weights are in flight; otherwise
+    // after the chunk loop.
     auto row_partials = [&]() __attribute__((always_inline)) {
         if constexpr (ACT != 0) {
             static_assert(NW == 8, "the row sums map 1024 virtual threads onto 512");
-#pragma unroll
-            for (int m = 0; m < M; ++m)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    float t = 0.f;
-                    if constexpr (kEarlyRows) {
-#pragma unroll
-                        for (int j = 0; j < RV; ++j) t = sq_chain<ACT>(rx[m][h][j], ry[m][h][j], t);
-                    } else {
-                        const uint16_t *row = src + (size_t)m * ld;
-                        for (int i = (int)threadIdx.x + 512 * h; i < K / 8; i += 1024) {
-                            const u32x4 x = *reinterpret_cast<const u32x4 *>(row + 8 * i);
-                            u32x4 y = x;
-                            if constexpr (ACT == 2) y = *reinterpret_cast<const u32x4 *>(row + K + 8 * i);
-                            t = sq_chain<ACT>(x, y, t);
-                        }
-                    }
-                    ss[m][h] = t;
-                }
+            rows.partials(src, ld, K);
         }
     };
     auto row_reduce = [&]() __attribute__((always_inline)) {
-        if constexpr (ACT != 0) {
-#pragma unroll
-            for (int m = 0; m < M; ++m)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    float v = ss[m][h];
-#pragma unroll
-                    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-                    if (lane == 0) s_part[8 * h + wave][m] = v;
-                }
-        }
+        if constexpr (ACT != 0) rows.reduce(s_part, lane, wave);
     };
 
     if constexpr (kEarlyRows) {
@@ -535,14 +563,8 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
     finish_tile<M, NW>(
         red,
         [&](int m) __attribute__((always_inline)) {
-            if constexpr (ACT != 0) {
-                float q = 0.f;
-#pragma unroll
-                for (int w = 0; w < 16; ++w) q += s_part[w][m];
-                return row_inv(q, K);
-            } else {
-                return 1.0f;
-            }
+            if constexpr (ACT != 0) return RowSums<M, ACT, RV, kEarlyRows>::inv(s_part, m, K);
+            else return 1.0f;
         },
         tile, N, splits, out, counters);
 }
@@ -577,16 +599,16 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
 // activations of row mu = j / 2 at those rows.  A wave takes chunks of CH rows
 // (CH divides G, so a chunk lies in one group) and issues all of a chunk's
 // loads before its first wait.
-template <int M, bool ASYM>
+template <int M, bool ASYM, int ACT, int RV>
 __global__ __launch_bounds__(512) void gemv_mma_kernel(
-    const uint16_t *__restrict__ a, const uint32_t *__restrict__ b, const uint16_t *__restrict__ scales,
-    const uint32_t *__restrict__ qzeros, int K, int N, int G, uint32_t zp, int tiles, int split_len, int splits,
-    uint16_t *__restrict__ out, uint32_t *__restrict__ counters) {
+    const uint16_t *__restrict__ a, const uint16_t *__restrict__ src, int ld, const uint32_t *__restrict__ b,
+    const uint16_t *__restrict__ scales, const uint32_t *__restrict__ qzeros, int K, int N, int G, uint32_t zp,
+    int tiles, int split_len, int splits, uint16_t *__restrict__ out, uint32_t *__restrict__ counters) {
     static_assert(M >= 1 && M <= 8, "two A rows per activation row");
     constexpr int NW = 8;
     constexpr int CH = kMmaChunkRows;
     constexpr int SETS = CH / 16;
-    constexpr int RV = M >= 2 ? 4 : 2;  // D elements that can hold rows < M (D row 4 g + v)
+    constexpr int DV = M >= 2 ? 4 : 2;  // D elements that can hold rows < M (D row 4 g + v)
     const int logical = xcd_local_index(blockIdx.x, gridDim.x);
     if (logical >= tiles * splits) return;
     const int tile = logical % tiles;
@@ -606,13 +628,18 @@ __global__ __launch_bounds__(512) void gemv_mma_kernel(
     const __amdgpu_buffer_rsrc_t brs = buffer_rsrc(b, (uint32_t)((uint64_t)K * N8 * 4));
     const __amdgpu_buffer_rsrc_t srs = buffer_rsrc(scales, (uint32_t)((uint64_t)(K / G) * N * 2));
     const __amdgpu_buffer_rsrc_t zrs = buffer_rsrc(qzeros, ASYM ? (uint32_t)((uint64_t)(K / G) * row_bytes) : 0u);
-    const __amdgpu_buffer_rsrc_t ars = buffer_rsrc(a, (uint32_t)((uint64_t)M * K * 2));
+    // Activations: `a` (row stride K), or with the glue folded in (ACT 1, 2)
+    // the raw rows of `src` (row stride ld; ACT 2: gate then up, K each).
+    const int lda = ACT == 0 ? K : ld;
+    const __amdgpu_buffer_rsrc_t ars =
+        buffer_rsrc(ACT == 0 ? a : src, (uint32_t)(((uint64_t)(M - 1) * lda + (ACT == 2 ? 2 : 1) * K) * 2));
     const uint32_t b_voff = ((uint32_t)(4 * g) * (uint32_t)N8 + (uint32_t)word) * 4u;
     const int mu = j >> 1;
-    const uint32_t a_voff = ((uint32_t)min(mu, M - 1) * (uint32_t)K + 4u * (uint32_t)g) * 2u;
+    const uint32_t a_voff = ((uint32_t)min(mu, M - 1) * (uint32_t)lda + 4u * (uint32_t)g) * 2u;
     // v_perm selectors placing activation 2r (sel0) or 2r + 1 (sel1) of a
     // loaded pair in fp16 half (j & 1) of an A register, the other half zero;
     // lanes of rows mu >= M give zeros.
+    const NibbleConsts nk = nibble_consts();
     uint32_t sel0 = (j & 1) ? 0x01000c0cu : 0x0c0c0100u;
     uint32_t sel1 = (j & 1) ? 0x03020c0cu : 0x0c0c0302u;
     if (mu >= M) sel0 = sel1 = 0x0c0c0c0cu;
@@ -623,10 +650,22 @@ __global__ __launch_bounds__(512) void gemv_mma_kernel(
 #pragma unroll
         for (int q = 0; q < 4; ++q) tot[x][q] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // Glue folded in: the row scale 1/sqrt(mean(t^2) + 1e-6) multiplies the
+    // products in the epilogue, as in the dot2 form (row sums in the glue
+    // kernels' order; at M <= 2 the row's vectors requested first).
+    __shared__ float s_part[16][M];
+    constexpr bool kEarlyRows = ACT != 0 && M <= 2;
+    RowSums<M, ACT, RV, kEarlyRows> rows;
+    if constexpr (kEarlyRows) {
+        rows.load(src, ld, K);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
     struct Chunk {
         u32x4 sv[2];     // scales of the lane's 16 columns
         u32x2 zw;        // packed zeros of its two words (ASYM)
-        u32x2 av[SETS];  // activations of row mu at the lane's 4 rows of each set
+        u32x2 av[SETS];  // activations of row mu at the lane's 4 rows of each set (ACT 2: gate)
+        u32x2 au[SETS];  // ACT 2: up
         u32x2 w[SETS][4];
     };
     auto load_chunk = [&](int c, Chunk &d) __attribute__((always_inline)) {
@@ -637,12 +676,20 @@ __global__ __launch_bounds__(512) void gemv_mma_kernel(
         d.zw = u32x2{0u, 0u};
         if constexpr (ASYM) d.zw = buffer_load_x2(zrs, (uint32_t)word * 4u, grp * row_bytes);
 #pragma unroll
-        for (int s = 0; s < SETS; ++s) d.av[s] = buffer_load_x2(ars, a_voff, (k0 + 16u * s) * 2u);
+        for (int s = 0; s < SETS; ++s) {
+            d.av[s] = buffer_load_x2(ars, a_voff, (k0 + 16u * s) * 2u);
+            if constexpr (ACT == 2) d.au[s] = buffer_load_x2(ars, a_voff + (uint32_t)K * 2u, (k0 + 16u * s) * 2u);
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < SETS; ++s)
 #pragma unroll
             for (int i = 0; i < 4; ++i) d.w[s][i] = buffer_load_x2_nt(brs, b_voff, (k0 + 16u * s + i) * row_bytes);
+        // every load of the chunk is issued before its first use: left free,
+        // the scheduler placed the A operand's perms (and with them a wait for
+        // the activations) ahead of the weight requests in the glue-fused
+        // variants, one memory round trip per chunk
+        __builtin_amdgcn_sched_barrier(0);
     };
     // Products of one chunk into acc (per word x and nibble pair q) and the
     // activation sums into asum.
@@ -655,10 +702,20 @@ __global__ __launch_bounds__(512) void gemv_mma_kernel(
         asum = f32x4{0.f, 0.f, 0.f, 0.f};
     };
     auto mma_chunk = [&](const Chunk &d) __attribute__((always_inline)) {
-        const f16x8 unit = __builtin_bit_cast(f16x8, u32x4{0x00010001u, 0x00010001u, 0x00010001u, 0x00010001u});
+        const f16x8 unit = __builtin_bit_cast(f16x8, u32x4{0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u});
 #pragma unroll
         for (int s = 0; s < SETS; ++s) {
-            const uint32_t lo = d.av[s].x, hi = d.av[s].y;
+            uint32_t lo = d.av[s].x, hi = d.av[s].y;
+            if constexpr (ACT == 2) {
+                // a = fp16(silu(g) * u), the dot2 form's rounding
+                auto t2 = [](uint32_t g2, uint32_t u2) __attribute__((always_inline)) {
+                    const float t0 = silu_mul(f16_bits_to_f32(g2 & 0xffffu), f16_bits_to_f32(u2 & 0xffffu));
+                    const float t1 = silu_mul(f16_bits_to_f32(g2 >> 16), f16_bits_to_f32(u2 >> 16));
+                    return (uint32_t)f32_to_f16_bits(t0) | ((uint32_t)f32_to_f16_bits(t1) << 16);
+                };
+                lo = t2(lo, d.au[s].x);
+                hi = t2(hi, d.au[s].y);
+            }
             const f16x8 av = __builtin_bit_cast(
                 f16x8, u32x4{__builtin_amdgcn_perm(0u, lo, sel0), __builtin_amdgcn_perm(0u, lo, sel1),
                              __builtin_amdgcn_perm(0u, hi, sel0), __builtin_amdgcn_perm(0u, hi, sel1)});
@@ -669,10 +726,10 @@ __global__ __launch_bounds__(512) void gemv_mma_kernel(
                 for (int i = 0; i < 4; ++i) {
                     const uint32_t w = x ? d.w[s][i].y : d.w[s][i].x;
                     const uint32_t sh = w >> 8;
-                    p[0][i] = w & kMaskLo;
-                    p[1][i] = w & kMaskHi;
-                    p[2][i] = sh & kMaskLo;
-                    p[3][i] = sh & kMaskHi;
+                    p[0][i] = (w & nk.mask_lo) | nk.bias_lo;
+                    p[1][i] = (w & nk.mask_hi) | nk.bias_hi;
+                    p[2][i] = (sh & nk.mask_lo) | nk.bias_lo;
+                    p[3][i] = (sh & nk.mask_hi) | nk.bias_hi;
                 }
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
@@ -692,41 +749,68 @@ __global__ __launch_bounds__(512) void gemv_mma_kernel(
 #pragma unroll
             for (int q = 0; q < 4; ++q)
 #pragma unroll
-                for (int v = 0; v < RV; ++v) {
+                for (int v = 0; v < DV; ++v) {
                     const int c = q + 4 * (v & 1);  // column within the word
                     const float s = f16_bits_to_f32((sv[x][c >> 1] >> (16 * (c & 1))) & 0xffffu);
                     const uint32_t z = ASYM ? (zword >> (4 * c)) & 0xfu : zp;
-                    const float zs = (float)((q & 1) ? 16u * z : z);
+                    const float zs = (float)((q & 1) ? 64u + z : 1024u + z);
                     tot[x][q][v] = __builtin_fmaf(s, __builtin_fmaf(-zs, asum[v], acc[x][q][v]), tot[x][q][v]);
                 }
         }
     };
 
-    // chunks c_begin + wave, + 8, ...: the workgroup's waves read consecutive rows
-    for (int c = c_begin + wave; c < c_end; c += NW) {
+    // chunks c_begin + wave, + 8, ...: the workgroup's waves read consecutive
+    // rows.  With the row held in registers the per-lane row sums run while
+    // the first chunk's weights are in flight (first chunk peeled); the
+    // cross-lane part follows where every lane of the wave is active.
+    const int c0 = c_begin + wave;
+    int c = c0;
+    if constexpr (kEarlyRows) {
+        if (c0 < c_end) {
+            Chunk d;
+            load_chunk(c0, d);
+            rows.partials(src, ld, K);
+            zero_acc();
+            mma_chunk(d);
+            flush(d.sv, d.zw);
+        } else {
+            rows.partials(src, ld, K);
+        }
+        rows.reduce(s_part, lane, wave);
+        c += NW;
+    }
+    for (; c < c_end; c += NW) {
         Chunk d;
         load_chunk(c, d);
         zero_acc();
         mma_chunk(d);
         flush(d.sv, d.zw);
     }
+    if constexpr (ACT != 0 && !kEarlyRows) {
+        rows.partials(src, ld, K);
+        rows.reduce(s_part, lane, wave);
+    }
 
     __shared__ float red[NW][M][kTileCols];
 #pragma unroll
-    for (int v = 0; v < RV; ++v) {
+    for (int v = 0; v < DV; ++v) {
         const int m = 2 * g + (v >> 1);
         if (m < M) {
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
-                // undo the subnormal encoding: 2^24 for nibbles 0, 2 (q = 0, 2), 2^20 for 1, 3
-                const f32x4 o = {tot[x][0][v] * 16777216.f, tot[x][1][v] * 1048576.f, tot[x][2][v] * 16777216.f,
-                                 tot[x][3][v] * 1048576.f};
+                const f32x4 o = {tot[x][0][v], tot[x][1][v], tot[x][2][v], tot[x][3][v]};
                 *reinterpret_cast<f32x4 *>(&red[wave][m][16 * j + 8 * x + 4 * (v & 1)]) = o;
             }
         }
     }
     __syncthreads();
-    finish_tile<M, NW>(red, [](int) { return 1.0f; }, tile, N, splits, out, counters);
+    finish_tile<M, NW>(
+        red,
+        [&](int m) __attribute__((always_inline)) {
+            if constexpr (ACT != 0) return RowSums<M, ACT, RV, kEarlyRows>::inv(s_part, m, K);
+            else return 1.0f;
+        },
+        tile, N, splits, out, counters);
 }
 
 template <int M, int WORDS, int NW, bool ASYM, bool FOLD, int ACT, int RV = 1>
@@ -775,44 +859,63 @@ hipError_t launch_m(const GemmArgs &g, const GemmPlan &p, int act, const uint16_
     return p.waves == 8 ? launch_v<M, WORDS, 8>(g, p, stream) : launch_v<M, WORDS, 4>(g, p, stream);
 }
 
-template <int M, bool ASYM>
-hipError_t launch_mma_z(const GemmArgs &g, const GemmPlan &p, hipStream_t stream) {
-    hipLaunchKernelGGL((gemv_mma_kernel<M, ASYM>), dim3((unsigned)p.grid), dim3(512), 0, stream, g.a,
-                       reinterpret_cast<const uint32_t *>(g.b), g.scales, reinterpret_cast<const uint32_t *>(g.qzeros),
-                       (int)g.K, (int)g.N, (int)g.G, (uint32_t)g.zp, (int)p.tiles_n, (int)p.split_len, p.splits,
-                       g.out, g.counters);
+template <int M, bool ASYM, int ACT, int RV>
+hipError_t launch_mma_k(const GemmArgs &g, const GemmPlan &p, const uint16_t *src, int ld, hipStream_t stream) {
+    hipLaunchKernelGGL((gemv_mma_kernel<M, ASYM, ACT, RV>), dim3((unsigned)p.grid), dim3(512), 0, stream, g.a, src,
+                       ld, reinterpret_cast<const uint32_t *>(g.b), g.scales,
+                       reinterpret_cast<const uint32_t *>(g.qzeros), (int)g.K, (int)g.N, (int)g.G, (uint32_t)g.zp,
+                       (int)p.tiles_n, (int)p.split_len, p.splits, g.out, g.counters);
     return hipGetLastError();
 }
 
+template <int M, int ACT, int RV>
+hipError_t launch_mma_z(const GemmArgs &g, const GemmPlan &p, const uint16_t *src, int ld, hipStream_t stream) {
+    return g.qzeros ? launch_mma_k<M, true, ACT, RV>(g, p, src, ld, stream)
+                    : launch_mma_k<M, false, ACT, RV>(g, p, src, ld, stream);
+}
+
+// Glue-fused variants: at M <= 2 the row's vectors are held in registers
+// from the start, RV per virtual thread (the glue kernels' own count).
+template <int M, int ACT>
+hipError_t launch_mma_act(const GemmArgs &g, const GemmPlan &p, const uint16_t *src, int ld, hipStream_t stream) {
+    const int64_t per = (g.K / 8 + 1023) / 1024;
+    if (M <= 2 && per > 2) return launch_mma_z<M, ACT, 4>(g, p, src, ld, stream);
+    if (M <= 2 && per > 1) return launch_mma_z<M, ACT, 2>(g, p, src, ld, stream);
+    return launch_mma_z<M, ACT, 1>(g, p, src, ld, stream);
+}
+
 template <int M>
-hipError_t launch_mma(const GemmArgs &g, const GemmPlan &p, hipStream_t stream) {
-    return g.qzeros ? launch_mma_z<M, true>(g, p, stream) : launch_mma_z<M, false>(g, p, stream);
+hipError_t launch_mma(const GemmArgs &g, const GemmPlan &p, int act, const uint16_t *src, int ld, hipStream_t stream) {
+    if (act == 1) return launch_mma_act<M, 1>(g, p, src, ld, stream);
+    if (act == 2) return launch_mma_act<M, 2>(g, p, src, ld, stream);
+    return launch_mma_z<M, 0, 1>(g, p, nullptr, 0, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gemv(const GemmArgs &g, const GemmPlan &p, hipStream_t stream) {
-    if (!p.mma) return launch_gemv_act(g, p, 0, nullptr, 0, stream);
-    if (p.splits > kMaxSplits || p.waves != 8 || g.N % 32 != 0 || g.G % kMmaChunkRows != 0)
-        return hipErrorInvalidValue;
-    switch (g.M) {
-        case 1: return launch_mma<1>(g, p, stream);
-        case 2: return launch_mma<2>(g, p, stream);
-        case 3: return launch_mma<3>(g, p, stream);
-        case 4: return launch_mma<4>(g, p, stream);
-        case 5: return launch_mma<5>(g, p, stream);
-        case 6: return launch_mma<6>(g, p, stream);
-        case 7: return launch_mma<7>(g, p, stream);
-        case 8: return launch_mma<8>(g, p, stream);
-        default: return hipErrorInvalidValue;
-    }
+    return launch_gemv_act(g, p, 0, nullptr, 0, stream);
 }
 
 hipError_t launch_gemv_act(const GemmArgs &g, const GemmPlan &p, int act, const uint16_t *src, int64_t ld,
                            hipStream_t stream) {
-    if (p.splits > kMaxSplits || p.mma) return hipErrorInvalidValue;
+    if (p.splits > kMaxSplits) return hipErrorInvalidValue;
     if (act != 0 && (p.waves != 8 || !src || ld % 8 != 0 || g.K % 8 != 0 || g.K > kGlueMaxWidth))
         return hipErrorInvalidValue;
+    if (p.mma) {
+        if (p.waves != 8 || g.N % 32 != 0 || g.G % kMmaChunkRows != 0) return hipErrorInvalidValue;
+        switch (g.M) {
+            case 1: return launch_mma<1>(g, p, act, src, (int)ld, stream);
+            case 2: return launch_mma<2>(g, p, act, src, (int)ld, stream);
+            case 3: return launch_mma<3>(g, p, act, src, (int)ld, stream);
+            case 4: return launch_mma<4>(g, p, act, src, (int)ld, stream);
+            case 5: return launch_mma<5>(g, p, act, src, (int)ld, stream);
+            case 6: return launch_mma<6>(g, p, act, src, (int)ld, stream);
+            case 7: return launch_mma<7>(g, p, act, src, (int)ld, stream);
+            case 8: return launch_mma<8>(g, p, act, src, (int)ld, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (g.M) {
         case 1: return launch_m<1, 4>(g, p, act, src, (int)ld, stream);
         case 2: return launch_m<2, 4>(g, p, act, src, (int)ld, stream);
