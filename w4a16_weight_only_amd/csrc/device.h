@@ -158,6 +158,28 @@ __device__ __forceinline__ float swap_add(float lo, float hi, int lane) {
     }
 }
 
+// Sum over the 64 lanes of a wave, every lane getting the total, with the
+// pairing of a lane-xor butterfly (32, 16, 8, 4, 2, 1): bit for bit what
+// `for (off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off)` gives (each
+// step adds the same two values in every lane of a pair, and fp32 addition is
+// commutative), on lane swaps and DPP instead of six LDS permutes.  After the
+// xor-8 step lanes 8 apart hold equal values, so a rotation by 4 inside the
+// 16-lane row reads a lane holding the xor-4 partner's value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0u, __builtin_bit_cast(uint32_t, v), CTRL, 0xf,
+                                                                 0xf, false));
+}
+__device__ __forceinline__ float wave_sum(float v, int lane) {
+    v = swap_add<32>(v, v, lane);
+    v = swap_add<16>(v, v, lane);
+    v = swap_add<8>(v, v, lane);
+    v += dpp_f32<0x124>(v);  // row_ror:4
+    v += dpp_f32<0x4e>(v);   // quad_perm [2, 3, 0, 1]: lane ^ 2
+    v += dpp_f32<0xb1>(v);   // quad_perm [1, 0, 3, 2]: lane ^ 1
+    return v;
+}
+
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t bits16) {
     return (float)__builtin_bit_cast(f16, (uint16_t)bits16);
 }

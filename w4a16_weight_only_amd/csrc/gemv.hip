@@ -204,9 +204,7 @@ struct RowSums {
         for (int m = 0; m < M; ++m)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                float v = ss[m][h];
-#pragma unroll
-                for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+                const float v = wave_sum(ss[m][h], lane);
                 if (lane == 0) s_part[8 * h + wave][m] = v;
             }
     }
@@ -766,6 +764,8 @@ __global__ __launch_bounds__(512) void gemv_mma_kernel(
     const int c0 = c_begin + wave;
     int c = c0;
     if constexpr (kEarlyRows) {
+        // (c is the same in every lane of the wave, so each branch below runs
+        // with the whole wave active)
         if (c0 < c_end) {
             Chunk d;
             load_chunk(c0, d);
@@ -776,8 +776,19 @@ __global__ __launch_bounds__(512) void gemv_mma_kernel(
         } else {
             rows.partials(src, ld, K);
         }
-        rows.reduce(s_part, lane, wave);
         c += NW;
+        // the cross-lane row sums while the second chunk's loads are in flight
+        if (c < c_end) {
+            Chunk d;
+            load_chunk(c, d);
+            rows.reduce(s_part, lane, wave);
+            zero_acc();
+            mma_chunk(d);
+            flush(d.sv, d.zw);
+            c += NW;
+        } else {
+            rows.reduce(s_part, lane, wave);
+        }
     }
     for (; c < c_end; c += NW) {
         Chunk d;

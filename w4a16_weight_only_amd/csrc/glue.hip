@@ -20,11 +20,11 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 
-// Sum over the workgroup: xor-shuffle inside each wave, then every thread adds
-// the per-wave sums in wave order (the same order in every thread and run).
+// Sum over the workgroup: a lane-xor butterfly inside each wave (wave_sum),
+// then every thread adds the per-wave sums in wave order (the same order in
+// every thread and run).
 __device__ __forceinline__ float block_sum(float v, float *sh) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    v = wave_sum(v, threadIdx.x & 63);
     if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
     __syncthreads();
     float s = 0.f;
