@@ -173,7 +173,9 @@ int w4a16_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t G, int32_t *path,
  * zero point at M <= 2), gemv_max_m,
  * mfma_target_waves, mfma_splits, mfma_cfg (1..6), mfma_mgroup (row tiles
  * walked per column tile by consecutive workgroups), max_partial_bytes,
- * decode_fuse (0: the decode step runs its glue as separate kernels).  Every
+ * decode_fuse (0: the decode step runs its glue as separate kernels),
+ * decode_swiglu_m (GEMV route: from this many rows on, default 3, SwiGLU +
+ * row-norm runs as a kernel of its own instead of inside the down GEMV).  Every
  * choice computes the same product; they differ in speed and in fp32
  * rounding.  Unknown keys or malformed values: W4A16_ERR_INVALID_ARG and the
  * current settings stay.  Affects calls planned after it returns; not

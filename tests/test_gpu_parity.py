@@ -340,21 +340,23 @@ def tuned(spec, fn):
         w4.w4a16_set_tuning(None)
 
 
-@pytest.mark.parametrize("gemv", ["", "gemv_mma=0"])
+@pytest.mark.parametrize("gemv", ["", "gemv_mma=0", "decode_swiglu_m=9"])
 @pytest.mark.parametrize("M", [1, 2, 5, 12, 24])
 @pytest.mark.parametrize("H,NQ,I", [(256, 384, 512), (512, 768, 9216), (512, 512, 17408)])
 def test_decode_step_fused_matches_unfused(M, H, NQ, I, gemv):
-    """At M <= 8 the row-norm and SwiGLU glue runs inside the consuming GEMVs
-    (the row scale applied to the products; the matrix-core GEMV by default,
-    the dot2 GEMV with gemv_mma=0) and a layer's output row-norm inside the
-    next layer's QKV; at M >= 9 the row-norms run inside the consuming MFMA
-    GEMMs the same way (SwiGLU stays a kernel).  One layer matches the unfused
+    """At M <= 8 the row-norms run inside the consuming GEMVs (the row scale
+    applied to the products; the matrix-core GEMV by default, the dot2 GEMV
+    with gemv_mma=0) and a layer's output row-norm inside the next layer's
+    QKV; SwiGLU + row-norm runs inside the down GEMV at M <= 2 (at every
+    M <= 8 with decode_swiglu_m=9) and as a kernel of its own above; at
+    M >= 9 the row-norms run inside the consuming MFMA GEMMs the same way
+    (SwiGLU a kernel).  One layer matches the unfused
     step (separate glue kernels, forced with decode_fuse=0) and the oracle at
     the per-element bound; two layers (the cross-layer fold) match the unfused
     step to relative L2 <= 1e-2.  Row widths up to 17408 cover one, two and
     four 8-element vectors per virtual thread of the row sums."""
     if gemv and M > 8:
-        pytest.skip("the GEMV forms apply at M <= 8 only")
+        pytest.skip("these GEMV-route forms apply at M <= 8 only")
     G, nl = 128, 2
     layers = []
     for l in range(nl):
@@ -417,18 +419,19 @@ def test_decode_step_in_place_and_rms():
     assert np.allclose(rms, 1.0, atol=5e-3)
 
 
-@pytest.mark.parametrize("gemv", ["", "gemv_mma=0"])
+@pytest.mark.parametrize("gemv", ["", "gemv_mma=0", "decode_swiglu_m=9"])
 @pytest.mark.parametrize("M", [1, 2, 5, 12, 24])
 @pytest.mark.parametrize("I", [9216, 12800])
 def test_decode_step_down_projection_intermediate(M, I, gemv):
     """White box: the step's output is row-normed, which hides a wrong row
     scale in any linear before it.  After a one-layer step the workspace holds
-    the down projection's output and its input: at M <= 8 (SwiGLU + row-norm
-    inside the down GEMV) the first buffer holds the gate+up output and the
-    second the down output, which must be the oracle's down projection of
-    fp16(rn(silu(g) * u)); at M >= 9 the second buffer holds the SwiGLU +
-    row-norm kernel's output (rows of unit rms) and the first the down GEMM's,
-    which must be the oracle's product of the two.  MLP widths 9216 and 12800
+    the down projection's output and its input: where SwiGLU + row-norm runs
+    inside the down GEMV (M <= 2; every M <= 8 with decode_swiglu_m=9) the
+    first buffer holds the gate+up output and the second the down output,
+    which must be the oracle's down projection of fp16(rn(silu(g) * u));
+    elsewhere the second buffer holds the SwiGLU + row-norm kernel's output
+    (rows of unit rms) and the first the down GEMV's or GEMM's, which must be
+    the oracle's product of the two.  MLP widths 9216 and 12800
     give GEMV K-splits with fewer 16-row chunks than row lanes, where a row-sum
     reduction run on only the lanes that hold a chunk lost part of a wave's
     sum."""
@@ -438,12 +441,12 @@ def test_decode_step_down_projection_intermediate(M, I, gemv):
     buf = (M * max(L["N"] for L in layers) * 2 + 255) // 256 * 256
     ws = torch.zeros(2 * buf, dtype=torch.uint8, device="cuda")
     if gemv and M > 8:
-        pytest.skip("the GEMV forms apply at M <= 8 only")
+        pytest.skip("these GEMV-route forms apply at M <= 8 only")
     note("decode down intermediate M=%d I=%d %s" % (M, I, gemv))
     tuned(gemv, lambda: w4.w4a16_decode_step(dev_stack(layers), x, workspace=ws))
     w = host(ws)
     D = layers[3]
-    if M <= 8:
+    if M <= (8 if gemv == "decode_swiglu_m=9" else 2):
         gu = w[:buf].view(np.float16)[:M * 2 * I].reshape(M, 2 * I)
         down = w[buf:].view(np.float16)[:M * H].reshape(M, H)
         h3 = oracle.swiglu_rownorm(gu)

@@ -63,6 +63,7 @@ struct Tune {
     int64_t mfma_mgroup = 0;           // force the MFMA row-tile group (0: by estimated L2 traffic)
     int64_t max_partial_bytes = 64ll << 20;
     int64_t decode_fuse = 1;           // 0: decode-step glue as separate kernels
+    int64_t decode_swiglu_m = 3;       // GEMV route: from this M on, SwiGLU + row-norm as a kernel of its own
 };
 
 // Returns false on an unknown key or a malformed entry (nothing applied).
@@ -95,6 +96,7 @@ bool parse_tune(const char *spec, Tune *out) {
         else if (k == "mfma_mgroup") v.mfma_mgroup = val;
         else if (k == "max_partial_bytes") v.max_partial_bytes = val;
         else if (k == "decode_fuse") v.decode_fuse = val;
+        else if (k == "decode_swiglu_m") v.decode_swiglu_m = val;
         else return false;
     }
     *out = v;
@@ -558,13 +560,25 @@ int w4a16_decode_step(const w4a16_linear *lin, int64_t n_layers, const uint16_t 
                          : run_gemm(x, L[0].b_packed, L[0].scales, L[0].qzeros, M, H, NQ, L[0].G, L[0].zp_bias,
                                     q, stream, !fuse)))
             return rc;
-        if (gemv_route) {
+        if (gemv_route && M < tune().decode_swiglu_m) {
             // q -> o (O), o -> q (gate+up), q -> o (down)
             if ((rc = run_gemm_act(1, q, NQ, L[1], M, H, H, o, stream)) ||
                 (rc = run_gemm_act(1, o, H, L[2], M, H, 2 * I, q, stream)) ||
                 (rc = run_gemm_act(2, q, 2 * I, L[3], M, I, H, o, stream)))
                 return rc;
             pend = o;
+        } else if (gemv_route) {
+            // SwiGLU folded into the down GEMV costs every workgroup M x I
+            // SwiGLUs for its row sums; from decode_swiglu_m rows on it runs
+            // as a kernel of its own.  q -> o (O), o -> q (gate+up),
+            // q -> o (SwiGLU + row-norm), o -> q (down)
+            if ((rc = run_gemm_act(1, q, NQ, L[1], M, H, H, o, stream)) ||
+                (rc = run_gemm_act(1, o, H, L[2], M, H, 2 * I, q, stream)) ||
+                (rc = glue(launch_swiglu_rownorm(q, M, I, o, stream))) ||
+                (rc = run_gemm(o, L[3].b_packed, L[3].scales, L[3].qzeros, M, I, H, L[3].G, L[3].zp_bias, q,
+                               stream)))
+                return rc;
+            pend = q;
         } else if (mfma_route) {
             // q -> o (O), o -> q (gate+up), q -> o (SwiGLU + row-norm), o -> q (down)
             if ((rc = run_gemm_act(1, q, NQ, L[1], M, H, H, o, stream)) ||

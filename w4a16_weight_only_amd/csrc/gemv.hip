@@ -179,25 +179,45 @@ struct RowSums {
         }
     }
     __device__ __forceinline__ void partials(const uint16_t *src, int ld, int K) {
+        if constexpr (EARLY) {
 #pragma unroll
-        for (int m = 0; m < M; ++m)
+            for (int m = 0; m < M; ++m)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                float t = 0.f;
-                if constexpr (EARLY) {
+                for (int h = 0; h < 2; ++h) {
+                    float t = 0.f;
 #pragma unroll
                     for (int j = 0; j < RV; ++j) t = sq_chain<ACT>(rx[m][h][j], ry[m][h][j], t);
-                } else {
-                    const uint16_t *row = src + (size_t)m * ld;
-                    for (int i = (int)threadIdx.x + 512 * h; i < K / 8; i += 1024) {
-                        const u32x4 x = *reinterpret_cast<const u32x4 *>(row + 8 * i);
-                        u32x4 y = x;
-                        if constexpr (ACT == 2) y = *reinterpret_cast<const u32x4 *>(row + K + 8 * i);
-                        t = sq_chain<ACT>(x, y, t);
+                    ss[m][h] = t;
+                }
+        } else {
+            // Pass j requests vector j of both chains of every row at once (one
+            // round trip per pass rather than one per row and chain), then
+            // extends each chain; every chain still runs in increasing j.
+            const int passes = (K / 8 + 1023) / 1024;
+#pragma unroll
+            for (int m = 0; m < M; ++m) ss[m][0] = ss[m][1] = 0.f;
+            for (int j = 0; j < passes; ++j) {
+                u32x4 x[M][2], y[M][2];
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    const __amdgpu_buffer_rsrc_t gr = buffer_rsrc(src + (size_t)m * ld, (uint32_t)K * 2u);
+                    const __amdgpu_buffer_rsrc_t ur =
+                        buffer_rsrc(src + (size_t)m * ld + K, ACT == 2 ? (uint32_t)K * 2u : 0u);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        // a vector past the row reads zeros (adds exactly 0)
+                        const uint32_t off = ((uint32_t)threadIdx.x + 512u * h + 1024u * j) * 16u;
+                        x[m][h] = buffer_load_x4(gr, off, 0);
+                        y[m][h] = x[m][h];
+                        if constexpr (ACT == 2) y[m][h] = buffer_load_x4(ur, off, 0);
                     }
                 }
-                ss[m][h] = t;
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) ss[m][h] = sq_chain<ACT>(x[m][h], y[m][h], ss[m][h]);
             }
+        }
     }
     __device__ __forceinline__ void reduce(float (&s_part)[16][M], int lane, int wave) {
 #pragma unroll
