@@ -5,9 +5,11 @@
 // the nibble's LSB gives (2^e + q) exactly, and one packed subtraction of
 // (2^e + z) leaves the exact integer q - z.  Low nibbles of a byte sit in
 // fraction bits 0..3 under 1024 (0x6400, LSB = 1); high nibbles sit in bits
-// 4..7 under 64 (0x5400, LSB = 1/16, so 16*q/16 = q).  Two rows are converted
-// per 32-bit register: v_perm_b32 gathers byte b of row k and of row k+1 into
-// bytes 0 and 2, one AND-OR then forms both fp16 lanes.
+// 4..7 under 64 (0x5400, LSB = 1/16, so 16*q/16 = q).  The dot2 GEMV converts
+// two rows per 32-bit register: v_perm_b32 gathers byte b of row k and of row
+// k+1 into bytes 0 and 2, one AND-OR then forms both fp16 lanes.  The
+// matrix-core GEMV applies the AND-OR to a packed word as loaded (columns c
+// and c + 4 of one row) and keeps the bias, removing it per chunk.
 #pragma once
 
 #include <hip/hip_runtime.h>

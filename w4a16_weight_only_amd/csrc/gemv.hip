@@ -1,4 +1,6 @@
-// gemv.hip -- W4A16 split-K GEMV for M <= 8 rows on the vector ALUs (gfx950).
+// gemv.hip -- W4A16 split-K GEMV for M <= 8 rows (gfx950), in two forms that
+// share the tiles, the K-split hand-off and the glue folding: the dot2 form
+// below (vector ALUs) and the matrix-core form further down (the default).
 //
 // out = a . ((q - z) * s)  (vLLM PR #37352 write-up, "Code analysis" item 1).
 // Decode is bound by streaming the weights once (inference-engine article,
@@ -594,23 +596,23 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
 // form above, the vector ALUs then do about 0.8 instructions per weight
 // instead of 1.4 (M = 1) to 4.75 (M = 8):
 //
-//  * Weights as fp16 subnormals.  AND-ing a packed word with 0x000F000F gives
-//    nibbles 0 and 4 in the two fp16 halves, each worth q * 2^-24 exactly
-//    (binary16 subnormals are integers times 2^-24); 0x00F000F0 gives nibbles
-//    1 and 5 worth 16 q * 2^-24; the word shifted right by 8 gives nibbles
-//    2, 6 and 3, 7 the same way.  One AND per two weights, no bias to remove.
+//  * Weights as biased fp16.  One AND-OR of a packed word gives nibbles 0 and
+//    4 in the two fp16 halves as 1024 + q (device.h), another nibbles 1 and 5
+//    as 64 + q; the word shifted right by 8 gives nibbles 2, 6 and 3, 7 the
+//    same way: exact values, one instruction per two weights.  (Subnormal
+//    weights, q * 2^-24 with no bias, lost precision on the matrix cores: 4-9
+//    times the dot2 form's error.)
 //  * Two columns per register.  A register of the B operand holds (column c,
 //    column c + 4) of one weight row: its two k-slots.  Activation row mu
 //    occupies A rows 2 mu and 2 mu + 1, which hold the row's activations in
 //    the even and in the odd k-slots only, so D row 2 mu + e collects column
 //    c + 4e.  Up to 8 activation rows fill the 16 A rows.
 //  * Zero point folded per chunk.  A ninth MFMA per set multiplies the same A
-//    by 2^-24 in every slot, giving sum(a) * 2^-24 in the layout of the
-//    products; the chunk's (q - z) sums are D - z' * that (z' = z or 16 z),
-//    scaled by the group scale into an fp32 total, and the 2^24 (2^20) is
-//    applied once at the end.  A zero point that is a power of two cancels
-//    all-z columns exactly (a scaling by a power of two commutes with the
-//    matrix core's rounding).
+//    by ones, giving sum(a) in the layout of the products; the chunk's
+//    (q - z) sums are D - (bias + z) * sum(a), scaled by the group scale into
+//    an fp32 total (the per-group factorisation out = sum_g s (sum a q' -
+//    z' sum a)).  The bias costs about 10 bits of the fp32 sums of one chunk,
+//    leaving an error like the dot2 form's.
 //
 // Lane (j, g) = (lane % 16, lane / 16) loads words 2j, 2j+1 of the tile (8
 // bytes of each row) for rows 16 s + 4 g + i (i < 4) of set s, and the
