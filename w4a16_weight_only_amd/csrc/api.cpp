@@ -236,7 +236,13 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma) {
         if (t.mfma_cfg >= 1 && t.mfma_cfg <= 6) {
             fill(kCfg[t.mfma_cfg - 1][0], kCfg[t.mfma_cfg - 1][1], kCfg[t.mfma_cfg - 1][2]);
         } else if (M <= 16) {
-            fill(1, 2, 4);
+            // One 16-row tile.  Measured on MI355X at M = 9..16: the 256-column
+            // shape wins from N = 8192 on; below, the 128-column 8-K-wave shape
+            // (twice the column tiles, fewer split partials): K = 12800
+            // N = 4096 19.5 -> 15.4 us, K = 4096 N = 4096 10.9 -> 9.3 us,
+            // N = 6144 within 0.1 us at M = 9 and 0.7 us better at M = 16.
+            if (cdiv(N8, 32) <= 24) fill(2, 1, 8);
+            else fill(1, 2, 4);
         } else if (M <= 32) {
             fill(2, 1, 8);
         } else {
