@@ -71,6 +71,26 @@ int w4a16_repack(const int32_t *src_nk8, int32_t *dst_kn8, int64_t K, int64_t N,
                  hipStream_t stream);
 
 /*
+ * Repack checkpoint-layout group scales into the kernel layout.
+ * Defined by: vLLM PR #37352 write-up, "Code analysis" item 2 -- after loading,
+ * the scale tensor has shape (K/G, N).  The page does not print the
+ * checkpoint's own scale layout; this call reads it as per output column,
+ * [N, K/G] (the weights' own orientation), and transposes.  Packed zero
+ * points in the checkpoint, read the same way as packed along the group axis
+ * ([N, (K/G)/8]), become [K/G, N/8] through w4a16_repack(src, dst, K/G, N).
+ *
+ *   src_ng   device, fp16 bits [N, Gn]: scale of (column n, group g).
+ *   dst_gn   device, fp16 bits [Gn, N]: receives it at (g, n).  Must not
+ *            overlap src.
+ *   Gn       number of groups K/G, > 0.  N > 0, a multiple of 8.
+ * Bit-exact.  Errors: INVALID_ARG for NULL pointers, Gn <= 0, N <= 0 or not a
+ * multiple of 8, or overlapping buffers; UNSUPPORTED beyond 32-bit indexing;
+ * HIP if the launch fails.
+ */
+int w4a16_repack_scales(const uint16_t *src_ng, uint16_t *dst_gn, int64_t Gn, int64_t N,
+                        hipStream_t stream);
+
+/*
  * out = a . ((q - z) * s).
  * Defined by: vLLM PR #37352 write-up, "Code analysis" item 1 (formula and call
  * signature) and "Why it is good" item 3 (contiguous inputs, N % 8 == 0).

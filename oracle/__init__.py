@@ -61,6 +61,8 @@ def _load():
         lib.w4o_gemm_sample.argtypes = [P, P, P, P, I64, I64, I64, I64, I32, P, P, I64, P, P]
         lib.w4o_repack.restype = ctypes.c_int
         lib.w4o_repack.argtypes = [P, P, I64, I64]
+        lib.w4o_repack_scales.restype = ctypes.c_int
+        lib.w4o_repack_scales.argtypes = [P, P, I64, I64]
         lib.w4o_rownorm.restype = ctypes.c_int
         lib.w4o_rownorm.argtypes = [P, I64, I64, I64, P]
         lib.w4o_swiglu_rownorm.restype = ctypes.c_int
@@ -165,6 +167,18 @@ def repack(src_nk8, K):
     if rc != 0:
         raise ValueError("oracle repack rejected the shapes (rc=%d)" % rc)
     return dst
+
+
+def repack_scales(src_ng):
+    """Checkpoint group scales fp16 [N, K/G] -> kernel layout fp16 [K/G, N]
+    (the 16-bit patterns unchanged)."""
+    src = _u16(src_ng)
+    N, Gn = src.shape
+    dst = np.zeros((Gn, N), np.uint16)
+    rc = _load().w4o_repack_scales(_ptr(src), _ptr(dst), Gn, N)
+    if rc != 0:
+        raise ValueError("oracle repack_scales rejected the shapes (rc=%d)" % rc)
+    return dst.view(np.float16)
 
 
 def rownorm(x, width=None):

@@ -248,6 +248,19 @@ int w4o_repack(const int32_t *src_nk8, int32_t *dst_kn8, int64_t K, int64_t N)
     return W4O_OK;
 }
 
+/* Checkpoint group scales [N, Gn] -> kernel [Gn, N] (vLLM PR #37352 write-up,
+ * "Code analysis" item 2: the loaded scale tensor has shape (K/G, N); the
+ * checkpoint's own orientation, per output column, is this library's reading).
+ * The value of (column n, group g) moves from src[n][g] to dst[g][n]: 16-bit
+ * patterns copied unchanged.  dst must not alias src. */
+int w4o_repack_scales(const uint16_t *src_ng, uint16_t *dst_gn, int64_t Gn, int64_t N)
+{
+    if (Gn <= 0 || N <= 0) return W4O_EINVAL;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t g = 0; g < Gn; ++g) dst_gn[g * N + n] = src_ng[n * Gn + g];
+    return W4O_OK;
+}
+
 /* ------------------------------------------------------ decode-step glue --- */
 /*
  * The decode step chains four linears per layer (QKV, O, gate+up, down) with

@@ -130,6 +130,18 @@ def test_repack_rejects_null_and_overlap(lib):
     assert lib.w4a16_repack(A, ctypes.c_void_p(A.value + 4), 64, 64, None) == INVALID
 
 
+@pytest.mark.parametrize("Gn,N,status", [(0, 8, INVALID), (4, 0, INVALID), (4, 12, INVALID), (-1, 8, INVALID),
+                                          (1 << 22, 1 << 10, UNSUPPORTED)])
+def test_repack_scales_rejects_sizes(lib, Gn, N, status):
+    assert lib.w4a16_repack_scales(A, B, Gn, N, None) == status
+
+
+def test_repack_scales_rejects_null_and_overlap(lib):
+    assert lib.w4a16_repack_scales(None, B, 4, 8, None) == INVALID
+    assert lib.w4a16_repack_scales(A, None, 4, 8, None) == INVALID
+    assert lib.w4a16_repack_scales(A, ctypes.c_void_p(A.value + 2), 4, 8, None) == INVALID
+
+
 def test_gemm_plan_paths(lib):
     # decode GEMV (matrix cores; the dot2 form on request), batched and prefill shapes
     for M in range(1, 9):

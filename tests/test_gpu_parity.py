@@ -255,6 +255,39 @@ def test_gemm_after_repack_matches_checkpoint_layout():
     check_close(out, want, "repack+gemm")
 
 
+@pytest.mark.parametrize("N,Gn", [(8, 1), (136, 3), (4096, 100), (12800, 32), (256, 200)])
+def test_repack_scales_bit_exact(N, Gn):
+    note("repack_scales N=%d Gn=%d" % (N, Gn))
+    src = synth.rng(N + 7 * Gn).integers(0, 1 << 16, size=(N, Gn), dtype=np.uint16).view(np.float16)
+    want = oracle.repack_scales(src)
+    got = host(w4.w4a16_repack_scales(dev(src)))
+    torch.cuda.synchronize()
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+
+
+@pytest.mark.parametrize("M,K,N,G", [(1, 4096, 1024, 128), (5, 2048, 768, 64), (32, 1024, 512, 128)])
+def test_gemm_after_full_checkpoint_load(M, K, N, G):
+    """The whole load path from a checkpoint layout: weights [N, K/8], group
+    scales [N, K/G] and zero points packed along the group axis [N, (K/G)/8]
+    go through w4a16_repack, w4a16_repack_scales and w4a16_repack (K := K/G);
+    the product matches the oracle's on the kernel-layout tensors."""
+    p = synth.problem(M, K, N, G, True, seed=4000 + M)
+    Gn = K // G
+    b_nk8 = pack_rows(unpack_rows(p["b_packed"]).T)               # [N, K/8]
+    s_ng = np.ascontiguousarray(p["scales"].T)                     # [N, K/G]
+    qz_nk8 = pack_rows(unpack_rows(p["qzeros"]).T)                 # [N, (K/G)/8]
+    note("checkpoint load M=%d K=%d N=%d G=%d" % (M, K, N, G))
+    b = w4.w4a16_repack(dev(b_nk8), K)
+    s = w4.w4a16_repack_scales(dev(s_ng))
+    qz = w4.w4a16_repack(dev(qz_nk8), Gn)
+    assert np.array_equal(host(b), p["b_packed"])
+    assert np.array_equal(host(s).view(np.uint16), p["scales"].view(np.uint16))
+    assert np.array_equal(host(qz), p["qzeros"])
+    out = host(w4.w4a16_gemm(dev(p["a"]), b, s, qz, G))
+    want = oracle.gemm(p["a"], p["b_packed"], p["scales"], p["qzeros"], G, 8)
+    check_close(out, want, "checkpoint load M=%d" % M)
+
+
 # ------------------------------------------- full workload sizes, sampled ---
 
 def sample_idx(M, N, count, seed):

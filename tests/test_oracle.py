@@ -195,6 +195,31 @@ def test_repack_invariants(K, N):
     assert np.array_equal(h1, h2)
 
 
+def test_repack_scales_hand_case():
+    """Checkpoint scales [N = 2, K/G = 3] -> kernel [3, 2]: the value of
+    (column n, group g) moves to row g, column n; 16-bit patterns (-0, inf,
+    a NaN payload, a subnormal) pass unchanged."""
+    src = np.array([[0x3C00, 0x8000, 0x7C00],
+                    [0x7E01, 0x0001, 0xC000]], dtype=np.uint16)
+    want = np.array([[0x3C00, 0x7E01],
+                     [0x8000, 0x0001],
+                     [0x7C00, 0xC000]], dtype=np.uint16)
+    assert np.array_equal(oracle.repack_scales(src.view(np.float16)).view(np.uint16), want)
+
+
+@pytest.mark.parametrize("N,Gn", [(8, 1), (16, 32), (136, 3), (1024, 100)])
+def test_repack_scales_invariants(N, Gn):
+    g = synth.rng(N * 13 + Gn)
+    src = g.integers(0, 1 << 16, size=(N, Gn), dtype=np.uint16)
+    dst = oracle.repack_scales(src.view(np.float16)).view(np.uint16)
+    assert dst.shape == (Gn, N)
+    # applied again (reading [Gn, N] as a checkpoint [N', Gn']) it gives the input back
+    assert np.array_equal(oracle.repack_scales(dst.view(np.float16)).view(np.uint16), src)
+    # a column of the checkpoint (one group) becomes a row of the kernel layout
+    for gi in (0, Gn - 1):
+        assert np.array_equal(dst[gi], src[:, gi])
+
+
 def test_gemm_invariant_under_repack():
     p = synth.problem(3, 256, 128, 64, True, seed=15, from_checkpoint=True)
     dst = oracle.repack(p["b_nk8"], 256)

@@ -17,7 +17,7 @@ import ctypes
 import os
 
 __all__ = [
-    "W4A16Error", "lib", "w4a16_gemm", "w4a16_repack", "w4a16_decode_step",
+    "W4A16Error", "lib", "w4a16_gemm", "w4a16_repack", "w4a16_repack_scales", "w4a16_decode_step",
     "w4a16_decode_workspace_bytes", "w4a16_gemm_plan", "w4a16_release", "Linear",
     "STATUS",
 ]
@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
     L.w4a16_last_error.argtypes = []
     L.w4a16_repack.restype = ctypes.c_int
     L.w4a16_repack.argtypes = [P, P, I64, I64, P]
+    L.w4a16_repack_scales.restype = ctypes.c_int
+    L.w4a16_repack_scales.argtypes = [P, P, I64, I64, P]
     L.w4a16_gemm.restype = ctypes.c_int
     L.w4a16_gemm.argtypes = [P, P, P, P, I64, I64, I64, I64, I32, P, P]
     L.w4a16_decode_workspace_bytes.restype = SZ
@@ -148,6 +150,22 @@ def w4a16_repack(src_nk8, K, out=None):
     else:
         _dev_tensor(out, "out", torch.int32, 2)
     _check(lib().w4a16_repack(src_nk8.data_ptr(), out.data_ptr(), K, N, _stream_ptr(src_nk8.device)))
+    return out
+
+
+def w4a16_repack_scales(src_ng, out=None):
+    """Checkpoint group scales fp16 [N, K/G] -> kernel layout fp16 [K/G, N]
+    (bit-exact transpose)."""
+    torch = _torch()
+    _dev_tensor(src_ng, "src_ng", torch.float16, 2)
+    N, Gn = src_ng.shape
+    if out is None:
+        out = torch.empty((Gn, N), dtype=torch.float16, device=src_ng.device)
+    else:
+        _dev_tensor(out, "out", torch.float16, 2)
+        if tuple(out.shape) != (Gn, N):
+            raise ValueError("out must be [K/G, N] = [%d, %d]" % (Gn, N))
+    _check(lib().w4a16_repack_scales(src_ng.data_ptr(), out.data_ptr(), Gn, N, _stream_ptr(src_ng.device)))
     return out
 
 

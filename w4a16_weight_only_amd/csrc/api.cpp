@@ -492,6 +492,19 @@ int w4a16_repack(const int32_t *src_nk8, int32_t *dst_kn8, int64_t K, int64_t N,
     return ok();
 }
 
+int w4a16_repack_scales(const uint16_t *src_ng, uint16_t *dst_gn, int64_t Gn, int64_t N, hipStream_t stream) {
+    if (!src_ng || !dst_gn) return fail(W4A16_ERR_INVALID_ARG, "src and dst must be non-NULL");
+    if (Gn <= 0 || N <= 0 || N % 8 != 0)
+        return fail(W4A16_ERR_INVALID_ARG, "Gn must be positive and N a positive multiple of 8");
+    if (Gn * N >= (1ll << 31) || N >= (1ll << 30))
+        return fail(W4A16_ERR_UNSUPPORTED, "scales too large for 32-bit indexing");
+    const size_t bytes = (size_t)Gn * N * 2;
+    if (overlaps(src_ng, bytes, dst_gn, bytes)) return fail(W4A16_ERR_INVALID_ARG, "dst overlaps src");
+    hipError_t e = launch_repack_scales(src_ng, dst_gn, Gn, N, stream);
+    if (e != hipSuccess) return fail(W4A16_ERR_HIP, std::string("scale repack launch: ") + hipGetErrorString(e));
+    return ok();
+}
+
 int w4a16_gemm(const uint16_t *a, const int32_t *b_packed, const uint16_t *scales, const int32_t *qzeros,
                int64_t M, int64_t K, int64_t N, int64_t G, int32_t zp_bias, uint16_t *out,
                hipStream_t stream) {

@@ -79,6 +79,8 @@ size_t mfma_rn_extra_floats(const GemmPlan &plan);
 // (mt, waves, kwaves) configuration.
 int mfma_max_splits(int mt, int waves, int kwaves);
 hipError_t launch_repack(const int32_t *src, int32_t *dst, int64_t K, int64_t N, hipStream_t stream);
+// fp16 [N, Gn] -> [Gn, N] (checkpoint group scales to the kernel layout).
+hipError_t launch_repack_scales(const uint16_t *src, uint16_t *dst, int64_t Gn, int64_t N, hipStream_t stream);
 
 // Decode-step glue (fp16 in/out, fp32 math).  Widths (and row strides) must
 // be multiples of 8 and at most kGlueMaxWidth; the launchers return

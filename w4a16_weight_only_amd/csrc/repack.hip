@@ -84,7 +84,40 @@ __global__ __launch_bounds__(256) void repack_kernel(const uint32_t *__restrict_
     }
 }
 
+// Group scales, checkpoint [N, G_n] -> kernel [G_n, N] (G_n = K/G groups): a
+// transpose of 16-bit values through a 64 x 64 LDS tile, so that the reads
+// (along a checkpoint row) and the writes (along a kernel row) both take 64
+// consecutive values per wave.  Tiles are numbered along G_n first in a 1-D
+// grid.  Bit-exact.
+constexpr int kTr = 64;
+
+__global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t *__restrict__ src,
+                                                          uint16_t *__restrict__ dst, int rows, int cols,
+                                                          int tiles_c) {
+    __shared__ uint16_t tile[kTr][kTr + 2];
+    const int tc = blockIdx.x % tiles_c, tr = blockIdx.x / tiles_c;
+    const int c0 = tc * kTr, r0 = tr * kTr;
+    const int tx = threadIdx.x & (kTr - 1), ty = threadIdx.x / kTr;  // 64 x 4 threads
+    for (int i = ty; i < kTr; i += 256 / kTr) {
+        const int r = r0 + i, c = c0 + tx;
+        if (r < rows && c < cols) tile[i][tx] = src[(size_t)r * cols + c];
+    }
+    __syncthreads();
+    for (int i = ty; i < kTr; i += 256 / kTr) {
+        const int c = c0 + i, r = r0 + tx;
+        if (c < cols && r < rows) dst[(size_t)c * rows + r] = tile[tx][i];
+    }
+}
+
 }  // namespace
+
+hipError_t launch_repack_scales(const uint16_t *src, uint16_t *dst, int64_t Gn, int64_t N, hipStream_t stream) {
+    const int tiles_c = (int)((Gn + kTr - 1) / kTr);
+    const int64_t blocks = (int64_t)tiles_c * ((N + kTr - 1) / kTr);
+    hipLaunchKernelGGL(transpose16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, src, dst, (int)N, (int)Gn,
+                       tiles_c);
+    return hipGetLastError();
+}
 
 hipError_t launch_repack(const int32_t *src, int32_t *dst, int64_t K, int64_t N, hipStream_t stream) {
     const int K8 = (int)(K / 8), N8 = (int)(N / 8);
