@@ -83,6 +83,8 @@ def small_cases():
         cases.append((M, 512, 544, 128, M % 2 == 0))
     cases += [(1, 256, 256, 64, False), (2, 1024, 256, 1024, True), (3, 4096, 1024, 128, False),
               (1, 512, 544, 32, False), (6, 256, 288, 32, True)]  # smallest group size on the GEMV path
+    # N = 18432 and 18464: the matrix-core GEMV takes 512-column tiles at M <= 2 (ragged last tile in the second)
+    cases += [(1, 256, 18432, 64, False), (2, 512, 18464, 128, True)]
     for M in (9, 15, 16, 17, 32, 33, 64, 65, 100, 128, 200, 256):  # MFMA path, ragged words/rows
         cases.append((M, 512, 520, 64, M % 2 == 1))
     cases += [(1, 256, 264, 64, True), (7, 384, 8, 128, False),  # N % 32 != 0 at small M
@@ -121,6 +123,7 @@ def test_gemm_dot2_gemv_matches_oracle(M, K, N, G, asym):
 TUNED_FORMS = ["gemv_mma=0", "gemv_mma=0,gemv_fold=0", "gemv_mma=0,gemv_fold=1", "gemv_waves=4",
                "gemv_waves=4,gemv_fold=1", "gemv_mma=0,gemv_splits=1", "gemv_mma=0,gemv_splits=7",
                "gemv_mma=1", "gemv_mma=1,gemv_splits=1", "gemv_mma=1,gemv_splits=7",
+               "gemv_mma_words=4", "gemv_mma_words=4,gemv_splits=3", "gemv_mma_words=2",
                "gemv_max_m=0", "mfma_cfg=4", "mfma_cfg=5,mfma_splits=3",
                "mfma_cfg=3", "mfma_cfg=6", "mfma_cfg=6,mfma_splits=3", "mfma_mgroup=1", "mfma_mgroup=2",
                "mfma_cfg=4,mfma_mgroup=3", "mfma_cfg=1,mfma_mgroup=4,mfma_splits=2"]

@@ -57,6 +57,7 @@ struct Tune {
     int64_t gemv_fold = -1;            // bias/zero removed per chunk: 1 always, 0 never, -1 symmetric M <= 2
     int64_t gemv_max_m = 8;            // largest M sent to the GEMV path (at most 8)
     int64_t gemv_mma = 1;              // GEMV k-reduction on the matrix cores (0: the dot2 GEMV)
+    int64_t gemv_mma_words = 0;        // matrix-core GEMV words per lane: 2 (256-column tiles), 4 (512, M <= 2), 0 by fill
     int64_t mfma_target_waves = 2048;  // aim for about this many MFMA-path waves
     int64_t mfma_splits = 0;           // force the MFMA split count
     int64_t mfma_cfg = 0;  // force (mt, waves, kwaves): 1..6 = (1,2,4) (2,2,4) (4,2,2) (2,1,8) (4,2,4) (4,1,8)
@@ -89,6 +90,7 @@ bool parse_tune(const char *spec, Tune *out) {
         else if (k == "gemv_fold") v.gemv_fold = val;
         else if (k == "gemv_max_m") v.gemv_max_m = val;
         else if (k == "gemv_mma") v.gemv_mma = val;
+        else if (k == "gemv_mma_words") v.gemv_mma_words = val;
 
         else if (k == "mfma_target_waves") v.mfma_target_waves = val;
         else if (k == "mfma_splits") v.mfma_splits = val;
@@ -139,7 +141,7 @@ int validate_sizes(int64_t M, int64_t K, int64_t N, int64_t G) {
 
 namespace w4a16 {
 
-GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma) {
+GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma, bool allow_wide) {
     const Tune &t = tune();
     GemmPlan p;
     const int64_t N8 = N / 8;
@@ -194,6 +196,21 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma) {
         // wave (one round fewer workgroups) was slower at M <= 2 (headline
         // 8.56 us).
         if (allow_mma && p.waves == 8 && t.gemv_mma != 0) {
+            // 512-column tiles (16-byte loads) measured slower wherever 256-column
+            // tiles fill the chip (headline 8.22 -> 8.57 us, M = 8 by 40-60%), but
+            // faster where those leave CUs idle: K = 4096 N = 25600 at M = 1 runs
+            // 100 tiles x 2 splits = 200 workgroups against 50 x 5 = 250,
+            // 13.72 -> 12.27 us.  So at M <= 2, when 256-column tiles fill under
+            // 85% of the CUs and 512-column ones at least 10% more.
+            auto fill = [](int64_t tiles) { return tiles * std::max<int64_t>(1, std::min<int64_t>(32, 256 / tiles)); };
+            const int64_t t2 = cdiv(N8, 32), t4 = cdiv(N8, 64);
+            const bool wide = t.gemv_mma_words == 4 ||
+                              (t.gemv_mma_words == 0 && fill(t2) < 218 && fill(t4) >= fill(t2) + 26);
+            p.words = 2;
+            if (allow_wide && M <= 2 && wide) {
+                p.words = 4;
+                p.tiles_n = t4;
+            }
             const int64_t mchunks = K / kMmaChunkRows;
             int64_t ms = t.gemv_splits > 0 ? t.gemv_splits : std::max<int64_t>(1, 256 / p.tiles_n);
             ms = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(ms, 32), mchunks));
@@ -405,7 +422,7 @@ int run_gemm(const uint16_t *a, const int32_t *b, const uint16_t *s, const int32
 // SwiGLU + row-norm) of `src` (row stride ld), for the decode step.
 int run_gemm_act(int act, const uint16_t *src, int64_t ld, const w4a16_linear &L, int64_t M, int64_t K, int64_t N,
                  uint16_t *out, hipStream_t stream) {
-    GemmPlan plan = plan_gemm(M, K, N, L.G);
+    GemmPlan plan = plan_gemm(M, K, N, L.G, true, act != 2);
     if (plan.path == kPathMfma) {
         if (act != 1) return fail(W4A16_ERR_UNSUPPORTED, "the MFMA path folds the row-norm only");
         plan.partial_floats += mfma_rn_extra_floats(plan);

@@ -238,26 +238,26 @@ struct RowSums {
     }
 };
 
-// Sums the workgroup's per-wave partials of a 256-column tile (red) in wave
+// Sums the workgroup's per-wave partials of a TC-column tile (red) in wave
 // order, multiplies row m by row_scale(m), and writes the tile: directly with
 // one K-split, else through one fixed-point slot per output (device.h), every
 // atomic issued before the first result is looked at.
-template <int M, int NW, typename RowScale>
-__device__ __forceinline__ void finish_tile(const float (&red)[NW][M][kTileCols], RowScale row_scale, int tile,
+template <int M, int NW, typename RowScale, int TC = kTileCols>
+__device__ __forceinline__ void finish_tile(const float (&red)[NW][M][TC], RowScale row_scale, int tile,
                                             int N, int splits, uint16_t *__restrict__ out,
                                             uint32_t *__restrict__ counters) {
     // One (row, column) per thread and pass.
-    constexpr int PASSES = (M * kTileCols + 64 * NW - 1) / (64 * NW);
-    const int col_base = tile * kTileCols;
+    constexpr int PASSES = (M * TC + 64 * NW - 1) / (64 * NW);
+    const int col_base = tile * TC;
     float sums[PASSES];
 #pragma unroll
     for (int i = 0; i < PASSES; ++i) {
         const int t = threadIdx.x + i * 64 * NW;
         float s = 0.f;
-        if (t < M * kTileCols) {
+        if (t < M * TC) {
 #pragma unroll
-            for (int wv = 0; wv < NW; ++wv) s += red[wv][t / kTileCols][t % kTileCols];
-            s *= row_scale(t / kTileCols);
+            for (int wv = 0; wv < NW; ++wv) s += red[wv][t / TC][t % TC];
+            s *= row_scale(t / TC);
         }
         sums[i] = s;
     }
@@ -265,8 +265,8 @@ __device__ __forceinline__ void finish_tile(const float (&red)[NW][M][kTileCols]
 #pragma unroll
         for (int i = 0; i < PASSES; ++i) {
             const int t = threadIdx.x + i * 64 * NW;
-            const int col = col_base + t % kTileCols;
-            if (t < M * kTileCols && col < N) out[(size_t)(t / kTileCols) * N + col] = f32_to_f16_bits(sums[i]);
+            const int col = col_base + t % TC;
+            if (t < M * TC && col < N) out[(size_t)(t / TC) * N + col] = f32_to_f16_bits(sums[i]);
         }
         return;
     }
@@ -275,17 +275,17 @@ __device__ __forceinline__ void finish_tile(const float (&red)[NW][M][kTileCols]
 #pragma unroll
     for (int i = 0; i < PASSES; ++i) {
         const int t = threadIdx.x + i * 64 * NW;
-        const int col = col_base + t % kTileCols;
+        const int col = col_base + t % TC;
         add[i] = slot_contribution(sums[i]);
         old[i] = 0;
-        if (t < M * kTileCols && col < N) old[i] = slot_add(&slots[(size_t)(t / kTileCols) * N + col], add[i]);
+        if (t < M * TC && col < N) old[i] = slot_add(&slots[(size_t)(t / TC) * N + col], add[i]);
     }
 #pragma unroll
     for (int i = 0; i < PASSES; ++i) {
         const int t = threadIdx.x + i * 64 * NW;
-        const int col = col_base + t % kTileCols;
-        if (t < M * kTileCols && col < N && slot_last(old[i], splits)) {
-            const size_t o = (size_t)(t / kTileCols) * N + col;
+        const int col = col_base + t % TC;
+        if (t < M * TC && col < N && slot_last(old[i], splits)) {
+            const size_t o = (size_t)(t / TC) * N + col;
             out[o] = slot_result_f16(old[i] + add[i], splits);
             slot_reset(&slots[o]);
         }
@@ -619,7 +619,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
 // activations of row mu = j / 2 at those rows.  A wave takes chunks of CH rows
 // (CH divides G, so a chunk lies in one group) and issues all of a chunk's
 // loads before its first wait.
-template <int M, bool ASYM, int ACT, int RV>
+template <int M, bool ASYM, int ACT, int RV, int WL = 2>
 __global__ __launch_bounds__(512) void gemv_mma_kernel(
     const uint16_t *__restrict__ a, const uint16_t *__restrict__ src, int ld, const uint32_t *__restrict__ b,
     const uint16_t *__restrict__ scales, const uint32_t *__restrict__ qzeros, int K, int N, int G, uint32_t zp,
@@ -629,6 +629,7 @@ __global__ __launch_bounds__(512) void gemv_mma_kernel(
     constexpr int CH = kMmaChunkRows;
     constexpr int SETS = CH / 16;
     constexpr int DV = M >= 2 ? 4 : 2;  // D elements that can hold rows < M (D row 4 g + v)
+    constexpr int TW = 16 * WL, TC = 8 * TW;  // tile words and columns
     const int logical = xcd_local_index(blockIdx.x, gridDim.x);
     if (logical >= tiles * splits) return;
     const int tile = logical % tiles;
@@ -640,7 +641,7 @@ __global__ __launch_bounds__(512) void gemv_mma_kernel(
     const int g = lane >> 4;
     const int N8 = N >> 3;
     // Lanes past N read a valid (clamped) address; their columns are never stored.
-    const int word = min(tile * kTileWords + 2 * j, N8 - 2);
+    const int word = min(tile * TW + WL * j, N8 - WL);
     const int nchunks = K / CH;
     const int c_begin = split * split_len;
     const int c_end = min(c_begin + split_len, nchunks);
@@ -664,9 +665,9 @@ __global__ __launch_bounds__(512) void gemv_mma_kernel(
     uint32_t sel1 = (j & 1) ? 0x03020c0cu : 0x0c0c0302u;
     if (mu >= M) sel0 = sel1 = 0x0c0c0c0cu;
 
-    f32x4 tot[2][4];
+    f32x4 tot[WL][4];
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
+    for (int x = 0; x < WL; ++x)
 #pragma unroll
         for (int q = 0; q < 4; ++q) tot[x][q] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -682,19 +683,29 @@ __global__ __launch_bounds__(512) void gemv_mma_kernel(
     }
 
     struct Chunk {
-        u32x4 sv[2];     // scales of the lane's 16 columns
-        u32x2 zw;        // packed zeros of its two words (ASYM)
+        u32x4 sv[WL];    // scales of the lane's 8 WL columns
+        uint32_t zw[WL]; // packed zeros of its words (ASYM)
         u32x2 av[SETS];  // activations of row mu at the lane's 4 rows of each set (ACT 2: gate)
         u32x2 au[SETS];  // ACT 2: up
-        u32x2 w[SETS][4];
+        uint32_t w[SETS][4][WL];
     };
     auto load_chunk = [&](int c, Chunk &d) __attribute__((always_inline)) {
         const uint32_t k0 = (uint32_t)c * CH;
         const uint32_t grp = k0 / (uint32_t)G;
-        d.sv[0] = buffer_load_x4(srs, (uint32_t)word * 16u, grp * (uint32_t)N * 2u);
-        d.sv[1] = buffer_load_x4(srs, (uint32_t)word * 16u + 16u, grp * (uint32_t)N * 2u);
-        d.zw = u32x2{0u, 0u};
-        if constexpr (ASYM) d.zw = buffer_load_x2(zrs, (uint32_t)word * 4u, grp * row_bytes);
+#pragma unroll
+        for (int x = 0; x < WL; ++x) {
+            d.sv[x] = buffer_load_x4(srs, (uint32_t)word * 16u + 16u * x, grp * (uint32_t)N * 2u);
+            d.zw[x] = 0u;
+        }
+        if constexpr (ASYM) {
+            if constexpr (WL == 4) {
+                const u32x4 z4 = buffer_load_x4(zrs, (uint32_t)word * 4u, grp * row_bytes);
+                d.zw[0] = z4.x; d.zw[1] = z4.y; d.zw[2] = z4.z; d.zw[3] = z4.w;
+            } else {
+                const u32x2 z2 = buffer_load_x2(zrs, (uint32_t)word * 4u, grp * row_bytes);
+                d.zw[0] = z2.x; d.zw[1] = z2.y;
+            }
+        }
 #pragma unroll
         for (int s = 0; s < SETS; ++s) {
             d.av[s] = buffer_load_x2(ars, a_voff, (k0 + 16u * s) * 2u);
@@ -704,7 +715,15 @@ __global__ __launch_bounds__(512) void gemv_mma_kernel(
 #pragma unroll
         for (int s = 0; s < SETS; ++s)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) d.w[s][i] = buffer_load_x2_nt(brs, b_voff, (k0 + 16u * s + i) * row_bytes);
+            for (int i = 0; i < 4; ++i) {
+                if constexpr (WL == 4) {
+                    const u32x4 v = buffer_load_x4_nt(brs, b_voff, (k0 + 16u * s + i) * row_bytes);
+                    d.w[s][i][0] = v.x; d.w[s][i][1] = v.y; d.w[s][i][2] = v.z; d.w[s][i][3] = v.w;
+                } else {
+                    const u32x2 v = buffer_load_x2_nt(brs, b_voff, (k0 + 16u * s + i) * row_bytes);
+                    d.w[s][i][0] = v.x; d.w[s][i][1] = v.y;
+                }
+            }
         // every load of the chunk is issued before its first use: left free,
         // the scheduler placed the A operand's perms (and with them a wait for
         // the activations) ahead of the weight requests in the glue-fused
@@ -713,10 +732,10 @@ __global__ __launch_bounds__(512) void gemv_mma_kernel(
     };
     // Products of one chunk into acc (per word x and nibble pair q) and the
     // activation sums into asum.
-    f32x4 acc[2][4], asum;
+    f32x4 acc[WL][4], asum;
     auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
+        for (int x = 0; x < WL; ++x)
 #pragma unroll
             for (int q = 0; q < 4; ++q) acc[x][q] = f32x4{0.f, 0.f, 0.f, 0.f};
         asum = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -740,11 +759,11 @@ __global__ __launch_bounds__(512) void gemv_mma_kernel(
                 f16x8, u32x4{__builtin_amdgcn_perm(0u, lo, sel0), __builtin_amdgcn_perm(0u, lo, sel1),
                              __builtin_amdgcn_perm(0u, hi, sel0), __builtin_amdgcn_perm(0u, hi, sel1)});
 #pragma unroll
-            for (int x = 0; x < 2; ++x) {
+            for (int x = 0; x < WL; ++x) {
                 uint32_t p[4][4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const uint32_t w = x ? d.w[s][i].y : d.w[s][i].x;
+                    const uint32_t w = d.w[s][i][x];
                     const uint32_t sh = w >> 8;
                     p[0][i] = (w & nk.mask_lo) | nk.bias_lo;
                     p[1][i] = (w & nk.mask_hi) | nk.bias_hi;
@@ -762,10 +781,10 @@ __global__ __launch_bounds__(512) void gemv_mma_kernel(
     // End of a group: (q - z) sums times the group scale into tot.  acc[x][q]
     // element v is D row 4 g + v = (row 2 g + v / 2, half e = v & 1), column
     // 8 (word + x) + q + 4 e of the lane's words.
-    auto flush = [&](const u32x4 (&sv)[2], const u32x2 &zw) __attribute__((always_inline)) {
+    auto flush = [&](const u32x4 (&sv)[WL], const uint32_t (&zw)[WL]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            const uint32_t zword = x ? zw.y : zw.x;
+        for (int x = 0; x < WL; ++x) {
+            const uint32_t zword = zw[x];
 #pragma unroll
             for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -824,26 +843,24 @@ __global__ __launch_bounds__(512) void gemv_mma_kernel(
         rows.reduce(s_part, lane, wave);
     }
 
-    __shared__ float red[NW][M][kTileCols];
+    auto row_scale_fn = [&](int m) __attribute__((always_inline)) {
+        if constexpr (ACT != 0) return RowSums<M, ACT, RV, kEarlyRows>::inv(s_part, m, K);
+        else return 1.0f;
+    };
+    __shared__ float red[NW][M][TC];
 #pragma unroll
     for (int v = 0; v < DV; ++v) {
         const int m = 2 * g + (v >> 1);
         if (m < M) {
 #pragma unroll
-            for (int x = 0; x < 2; ++x) {
+            for (int x = 0; x < WL; ++x) {
                 const f32x4 o = {tot[x][0][v], tot[x][1][v], tot[x][2][v], tot[x][3][v]};
-                *reinterpret_cast<f32x4 *>(&red[wave][m][16 * j + 8 * x + 4 * (v & 1)]) = o;
+                *reinterpret_cast<f32x4 *>(&red[wave][m][8 * WL * j + 8 * x + 4 * (v & 1)]) = o;
             }
         }
     }
     __syncthreads();
-    finish_tile<M, NW>(
-        red,
-        [&](int m) __attribute__((always_inline)) {
-            if constexpr (ACT != 0) return RowSums<M, ACT, RV, kEarlyRows>::inv(s_part, m, K);
-            else return 1.0f;
-        },
-        tile, N, splits, out, counters);
+    finish_tile<M, NW, decltype(row_scale_fn), TC>(red, row_scale_fn, tile, N, splits, out, counters);
 }
 
 template <int M, int WORDS, int NW, bool ASYM, bool FOLD, int ACT, int RV = 1>
@@ -894,6 +911,16 @@ hipError_t launch_m(const GemmArgs &g, const GemmPlan &p, int act, const uint16_
 
 template <int M, bool ASYM, int ACT, int RV>
 hipError_t launch_mma_k(const GemmArgs &g, const GemmPlan &p, const uint16_t *src, int ld, hipStream_t stream) {
+    if constexpr (M <= 2 && ACT <= 1) {
+        // 512-column tiles (4 words per lane), planned at M <= 2 where they fill more of the chip
+        if (p.words == 4) {
+            hipLaunchKernelGGL((gemv_mma_kernel<M, ASYM, ACT, RV, 4>), dim3((unsigned)p.grid), dim3(512), 0, stream,
+                               g.a, src, ld, reinterpret_cast<const uint32_t *>(g.b), g.scales,
+                               reinterpret_cast<const uint32_t *>(g.qzeros), (int)g.K, (int)g.N, (int)g.G,
+                               (uint32_t)g.zp, (int)p.tiles_n, (int)p.split_len, p.splits, g.out, g.counters);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((gemv_mma_kernel<M, ASYM, ACT, RV>), dim3((unsigned)p.grid), dim3(512), 0, stream, g.a, src,
                        ld, reinterpret_cast<const uint32_t *>(g.b), g.scales,
                        reinterpret_cast<const uint32_t *>(g.qzeros), (int)g.K, (int)g.N, (int)g.G, (uint32_t)g.zp,
@@ -936,7 +963,8 @@ hipError_t launch_gemv_act(const GemmArgs &g, const GemmPlan &p, int act, const 
     if (act != 0 && (p.waves != 8 || !src || ld % 8 != 0 || g.K % 8 != 0 || g.K > kGlueMaxWidth))
         return hipErrorInvalidValue;
     if (p.mma) {
-        if (p.waves != 8 || g.N % 32 != 0 || g.G % kMmaChunkRows != 0) return hipErrorInvalidValue;
+        if (p.waves != 8 || g.N % 32 != 0 || g.G % kMmaChunkRows != 0 || (p.words == 4 && (g.M > 2 || act == 2)))
+            return hipErrorInvalidValue;
         switch (g.M) {
             case 1: return launch_mma<1>(g, p, act, src, (int)ld, stream);
             case 2: return launch_mma<2>(g, p, act, src, (int)ld, stream);

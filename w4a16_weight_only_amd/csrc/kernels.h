@@ -17,8 +17,9 @@ constexpr int kMmaChunkRows = 32;
 // from (M, K, N, G) alone so that it can be inspected without a GPU.
 struct GemmPlan {
     int path = 0;
-    // GEMV: `words` packed words (8 columns each) per lane, `waves` waves per
-    // workgroup.  MFMA: `mt` 16-row tiles per wave, `waves` along N.
+    // GEMV: `words` packed words (8 columns each) per lane (matrix-core form:
+    // 2, or 4 for 512-column tiles), `waves` waves per workgroup.  MFMA: `mt`
+    // 16-row tiles per wave, `waves` along N.
     int words = 4;
     int waves = 4;
     int mt = 1;
@@ -52,9 +53,10 @@ struct GemmArgs {
     uint32_t *counters;  // plan.counters zero-initialised words (or null)
 };
 
-// allow_mma = false keeps a GEMV plan on the dot2 kernel (the glue-fused
-// variants exist only there).
-GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma = true);
+// allow_mma = false keeps a GEMV plan on the dot2 kernel; allow_wide = false
+// keeps the matrix-core GEMV on 256-column tiles (its SwiGLU variant has no
+// 512-column form).
+GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma = true, bool allow_wide = true);
 
 hipError_t launch_gemv(const GemmArgs &args, const GemmPlan &plan, hipStream_t stream);
 // GEMV with the decode step's glue folded in: act 1: out = (src . W) * inv_row,
