@@ -10,13 +10,14 @@ order, group index, scale transposed, zero sign, a transposed activation,
 rounding mode) fails at least one of them.
 """
 import math
+import os
 
 import numpy as np
 import pytest
 import scipy.special
 
 import oracle
-from tests._fixtures import pack_rows, read_cases, unpack_rows, words
+from tests._fixtures import GOLDEN, pack_rows, read_cases, unpack_rows, words
 from w4a16_weight_only_amd import synth
 
 
@@ -306,3 +307,34 @@ def test_decode_step_identity_weights():
     r = oracle.rownorm(oracle.rownorm(x))
     want = oracle.rownorm(oracle.swiglu_rownorm(np.concatenate([r, r], 1)))
     assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+
+
+def _glue_eps_cases():
+    cases = []
+    with open(os.path.join(GOLDEN, "glue_eps_cases.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            lhs, want = line.split("->")
+            kind, width, pattern = lhs.split(None, 2)
+            cases.append((kind, int(width), pattern.strip(), [int(w, 16) for w in want.split()]))
+    return cases
+
+
+@pytest.mark.parametrize("kind,width,pattern,want", _glue_eps_cases(),
+                         ids=lambda v: v if isinstance(v, str) else None)
+def test_glue_closed_form_with_epsilon(kind, width, pattern, want):
+    """Rows whose mean square is comparable to the glue's 1e-6 term
+    (tests/golden/glue_eps_cases.txt, worked out by hand): a different
+    epsilon, none, or a sum in place of the mean each give other fp16 bits."""
+    if kind == "rownorm":
+        pat = np.array([int(w, 16) for w in pattern.split()], np.uint16)
+        row = np.tile(pat, width // len(pat))[None, :]
+        got = oracle.rownorm(row.view(np.float16)).view(np.uint16)[0]
+        assert np.array_equal(got, np.tile(np.array(want, np.uint16), width // len(want)))
+    else:
+        gate, up = (int(w, 16) for w in pattern.split("/"))
+        gu = np.concatenate([np.full(width, gate, np.uint16), np.full(width, up, np.uint16)])[None, :]
+        got = oracle.swiglu_rownorm(gu.view(np.float16)).view(np.uint16)[0]
+        assert np.all(got == want[0])
