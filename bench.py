@@ -36,6 +36,23 @@ KERNEL_SOURCES = ["w4a16_weight_only_amd/csrc/gemv.hip", "w4a16_weight_only_amd/
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemv_M1_K4096_N12800_counters.md")
 
 
+TRIAGE_STOP = 1.3  # [Floor-First] methodology step 3: measured / floor below this means stop tuning
+
+
+def floors(measured_us, nbytes, flops, extra_floor_us=0.0):
+    """Floor-first triage of one row: t_hbm (bytes at peak HBM), t_mfma (2MNK
+    at peak fp16 MFMA), t_opt = the larger (the binding roof), t_sum = both in
+    sequence (no overlap), residual = measured / t_opt, and the triage verdict
+    at 1.3x the floor.  extra_floor_us: a further lower bound (the decode
+    step's launch floor), folded into t_opt when larger."""
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9) * 1e6
+    t_mfma = flops / (FP16_PEAK_TFLOPS * 1e12) * 1e6
+    t_opt = max(t_hbm, t_mfma, extra_floor_us)
+    res = measured_us / t_opt
+    return dict(t_hbm_us=t_hbm, t_mfma_us=t_mfma, floor_us=t_opt, t_sum_us=t_hbm + t_mfma, residual=res,
+                triage="stop" if res < TRIAGE_STOP else "escalate")
+
+
 def alg_bytes(M, K, N, G, asym):
     b = K * N // 2 + (K // G) * N * 2 + 2 * M * K + 2 * M * N
     if asym:
@@ -160,15 +177,14 @@ def bench_gemm(torch, w4, stream, M, K, N, G, asym, steps, warmup, seed):
     path, splits, grid = w4.w4a16_gemm_plan(M, K, N, G)
     del P
     torch.cuda.empty_cache()
-    # floor at the binding roof: max(bytes at peak HBM, 2MNK at peak fp16 MFMA)
-    floor_us = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (FP16_PEAK_TFLOPS * 1e12)) * 1e6
-    return dict(M=M, K=K, N=N, G=G, asym=asym, path={1: "gemv", 2: "mfma", 3: "gemv_mma"}[path], splits=splits,
-                grid=grid, rotated_copies=copies, us_per_call=ms * 1e3, host_us_per_call=host_ms * 1e3,
-                eager_us_per_call=eager_ms * 1e3, alg_bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9,
-                tflops=flops / (ms * 1e-3) / 1e12,
-                hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                mfma_frac=flops / (ms * 1e-3) / 1e12 / FP16_PEAK_TFLOPS,
-                floor_us=floor_us, residual=ms * 1e3 / floor_us)
+    row = dict(M=M, K=K, N=N, G=G, asym=asym, path={1: "gemv", 2: "mfma", 3: "gemv_mma"}[path], splits=splits,
+               grid=grid, rotated_copies=copies, us_per_call=ms * 1e3, host_us_per_call=host_ms * 1e3,
+               eager_us_per_call=eager_ms * 1e3, alg_bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9,
+               tflops=flops / (ms * 1e-3) / 1e12,
+               hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+               mfma_frac=flops / (ms * 1e-3) / 1e12 / FP16_PEAK_TFLOPS)
+    row.update(floors(ms * 1e3, nbytes, flops))
+    return row
 
 
 def bench_repack(torch, w4, stream, K, N, steps, warmup):
@@ -190,8 +206,39 @@ def bench_repack(torch, w4, stream, K, N, steps, warmup):
     ms, _ = timed_graph(torch, stream, launch, steps, warmup)
     del src, dst
     torch.cuda.empty_cache()
-    return dict(K=K, N=N, us_per_call=ms * 1e3, alg_bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9,
-                hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+    row = dict(K=K, N=N, us_per_call=ms * 1e3, alg_bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9,
+               hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+    row.update(floors(ms * 1e3, nbytes, 0.0))
+    return row
+
+
+def launch_floor_us(torch, w4, stream, steps=200):
+    """Per-launch time of the smallest kernel of the library (a one-row,
+    eight-element row-norm: one workgroup, one round trip) replayed back to
+    back from a graph: what every dependent launch of a step costs at least."""
+    x = torch.randn(1, 8, device="cuda").half()
+    y = torch.empty_like(x)
+    L = w4.lib()
+    sp = stream.cuda_stream
+
+    def launch(i):
+        rc = L.w4a16_rownorm(x.data_ptr(), 8, 1, 8, y.data_ptr(), sp)
+        if rc:
+            raise RuntimeError(L.w4a16_last_error().decode())
+
+    ms, _ = timed_graph(torch, stream, launch, steps, 10)
+    return ms * 1e3
+
+
+def decode_launches(w4, M, stack, nl):
+    """Kernel launches of one decode step: one per linear, one more for each
+    glue step that runs as a kernel of its own, and the final row-norm."""
+    n = 1
+    for l in range(nl):
+        for j, glue in enumerate((w4.GLUE_NONE if l == 0 else w4.GLUE_RMSNORM, w4.GLUE_RMSNORM, w4.GLUE_RMSNORM,
+                                  w4.GLUE_SWIGLU)):
+            n += 1 + (w4.w4a16_gemm_glue_workspace_bytes(glue, M, stack[4 * l + j]) > 0)
+    return n
 
 
 def bench_decode(torch, w4, stream, Ms, steps, warmup):
@@ -212,6 +259,7 @@ def bench_decode(torch, w4, stream, Ms, steps, warmup):
             wbytes += K * N // 2 + (K // G) * N * 2
     res = {}
     L = w4.lib()
+    t_launch = launch_floor_us(torch, w4, stream)
     arr = w4._linear_array(stack)
     import ctypes
     arrp = ctypes.cast(arr, ctypes.c_void_p)
@@ -230,16 +278,21 @@ def bench_decode(torch, w4, stream, Ms, steps, warmup):
         ms, _ = timed_graph(torch, stream, launch, steps, warmup)
         eager_ms = timed_eager(torch, stream, launch, steps, 1)
         act = 0
+        flops = 0
         for (K, N) in synth.stack_linear_shapes(H, NQ, I):
             act += 2 * M * (K + N) * nl
+            flops += 2.0 * M * K * N * nl
         rms = float(y.float().pow(2).mean(1).sqrt().mean())
-        res["M%d" % M] = dict(M=M, layers=nl, us_per_step=ms * 1e3, eager_us_per_step=eager_ms * 1e3,
-                              tok_per_s=M / (ms * 1e-3), eager_tok_per_s=M / (eager_ms * 1e-3),
-                              weight_bytes=wbytes, gbs=(wbytes + act) / (ms * 1e-3) / 1e9,
-                              hbm_frac=(wbytes + act) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                              floor_us=(wbytes + act) / (HBM_PEAK_GBS * 1e9) * 1e6,
-                              residual=ms * 1e3 / ((wbytes + act) / (HBM_PEAK_GBS * 1e9) * 1e6),
-                              output_row_rms=rms)
+        row = dict(M=M, layers=nl, us_per_step=ms * 1e3, eager_us_per_step=eager_ms * 1e3,
+                   tok_per_s=M / (ms * 1e-3), eager_tok_per_s=M / (eager_ms * 1e-3),
+                   weight_bytes=wbytes, gbs=(wbytes + act) / (ms * 1e-3) / 1e9,
+                   hbm_frac=(wbytes + act) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                   target_tok_per_s_70pct=0.7 * M / ((wbytes + act) / (HBM_PEAK_GBS * 1e9)),
+                   output_row_rms=rms)
+        n_launch = decode_launches(w4, M, stack, nl)
+        row.update(floors(ms * 1e3, wbytes + act, flops, n_launch * t_launch))
+        row.update(launches=n_launch, launch_us=t_launch, launch_floor_us=n_launch * t_launch)
+        res["M%d" % M] = row
     del stack
     torch.cuda.empty_cache()
     return res
@@ -302,23 +355,69 @@ EXTRA_ROWS = {
 }
 
 
-def cpu_baseline(seconds=10.0):
-    """The oracle (plain single-threaded C, fp64) on the same M=1 workload,
-    repeated for about `seconds`."""
-    import oracle
-    from w4a16_weight_only_amd import synth
-    p = synth.workload("gemv")
-    nbytes = alg_bytes(1, 4096, 12800, 128, False)
-    n = 0
-    t0 = time.perf_counter()
+def _timed(fn, seconds):
+    """Run fn() at least once and until `seconds` have passed; (calls, s)."""
+    n, t0 = 0, time.perf_counter()
     while True:
-        oracle.gemm(p["a"], p["b_packed"], p["scales"], None, 128, 8)
+        fn()
         n += 1
         if time.perf_counter() - t0 >= seconds:
-            break
+            return n, time.perf_counter() - t0
+
+
+def cpu_baseline(seconds=10.0):
+    """The oracle (plain C, fp64, unchanged) on the host's cores: its products
+    split over column slices run on one thread per core (at most 16), each
+    slice the same loops over a smaller instance.  The headline figure is the
+    M = 1 workload repeated for about `seconds`; the other rows are bounded
+    samples of the M = 32, M = 256 and 40-layer decode workloads, scaled to
+    their metric."""
+    import oracle
+    from w4a16_weight_only_amd import synth
+    cores = oracle.host_workers()
+    p = synth.workload("gemv")
+    nbytes = alg_bytes(1, 4096, 12800, 128, False)
+    parts = oracle.split_columns(p["b_packed"], p["scales"], None)
+    n, dt = _timed(lambda: oracle.gemm_split(p["a"], parts, 128, 8), seconds)
+    head = dict(value=nbytes * n / dt / 1e9, unit="GB/s", cores=cores, kind="oracle",
+                sample="%d full M=1 K=4096 N=12800 G=128 products (%.1f s, %d threads over column slices, fp64)"
+                       % (n, dt, cores))
+    rows = {}
+    b = synth.workload("batched")
+    b["b_packed"] = oracle.repack(b["b_nk8"], b["K"])
+    parts = oracle.split_columns(b["b_packed"], b["scales"], b["qzeros"])
+    n, dt = _timed(lambda: oracle.gemm_split(b["a"], parts, 128, 8), seconds / 4)
+    f = 2.0 * 32 * 4096 * 12800
+    rows["batched_M32"] = dict(value=f * n / dt / 1e12, unit="TFLOP/s", gbs=alg_bytes(32, 4096, 12800, 128, True)
+                               * n / dt / 1e9, cores=cores, sample="%d full M=32 products (%.1f s)" % (n, dt))
+    pf = synth.workload("prefill")
+    rows_m = 32
+    a32 = pf["a"][:rows_m]
+    parts = oracle.split_columns(pf["b_packed"], pf["scales"], pf["qzeros"])
+    n, dt = _timed(lambda: oracle.gemm_split(a32, parts, 128, 8), seconds / 4)
+    f = 2.0 * rows_m * 12800 * 4096
+    rows["prefill_M256"] = dict(value=f * n / dt / 1e12, unit="TFLOP/s", cores=cores,
+                                sample="%d products of the first %d of the 256 rows, K=12800 N=4096 (%.1f s); the "
+                                       "oracle's cost per output is the same for every row" % (n, rows_m, dt))
+    layers = synth.stack_layer(0) + synth.stack_layer(1)
+    x = synth.stack_input(1)
+    t0 = time.perf_counter()
+    y = oracle.decode_layer_columns(layers[:4], x)
+    oracle.decode_layer_columns(layers[4:], y)
     dt = time.perf_counter() - t0
-    return dict(value=nbytes * n / dt / 1e9, unit="GB/s", cores=1, kind="oracle",
-                sample="%d full M=1 K=4096 N=12800 G=128 products (%.1f s, single thread, fp64)" % (n, dt))
+    per_layer = dt / 2
+    rows["decode_step_M1"] = dict(value=1.0 / (per_layer * synth.STACK["layers"]), unit="tok/s", cores=cores,
+                                  sample="layers 0 and 1 of the 8B-class stack at M=1 (%.1f s), scaled to 40 "
+                                         "layers" % dt)
+    x32 = synth.stack_input(32)
+    t0 = time.perf_counter()
+    oracle.decode_layer_columns(layers[:4], x32)
+    dt = time.perf_counter() - t0
+    rows["decode_step_M32"] = dict(value=32.0 / (dt * synth.STACK["layers"]), unit="tok/s", cores=cores,
+                                   sample="layer 0 of the 8B-class stack at M=32 (%.1f s), scaled to 40 layers"
+                                          % dt)
+    head["rows"] = rows
+    return head
 
 
 def host_info():

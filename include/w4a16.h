@@ -110,12 +110,27 @@ int w4a16_repack_scales(const uint16_t *src_ng, uint16_t *dst_gn, int64_t Gn, in
  *            qzeros is NULL.
  *   out      device, fp16 [M, N], caller-allocated; must not overlap any input.
  *
- * Paths: M <= 8 runs a split-K GEMV on the vector ALUs; M >= 9 runs an MFMA
- * kernel (fp16 inputs, fp32 accumulation).  Split-K partial sums live in a
- * scratch buffer that the library allocates lazily per (device, stream) on the
- * first call that needs it and keeps until w4a16_release(); concurrent calls
- * on the same stream from several host threads are not supported.  The result
- * is deterministic (fixed reduction order) for a given shape.
+ * Paths (w4a16_gemm_plan reports which): M <= 8 (with N % 32 == 0) runs a
+ * split-K GEMV whose k-reduction runs on the matrix cores
+ * (v_mfma_f32_16x16x32_f16 on exactly converted weights, 1024 + q or 64 + q,
+ * with the zero term removed per 32-row chunk by the same MFMA chain; packed
+ * zeros, and a symmetric zero point on request (tuning key gemv_mma_exact),
+ * take exact (q - z) weights instead); the tuning key gemv_mma=0 selects the
+ * same GEMV with v_dot2_f32_f16 on the vector ALUs.  M >= 9 runs an MFMA
+ * GEMM that dequantises the weights in registers to exact (q - z) fp16
+ * operands and applies each group's scale to the fp32 sums of that group.
+ * Accumulation is fp32 throughout.  K-splits across workgroups meet in
+ * fixed point (GEMV) or in split order (MFMA GEMM), so the result is
+ * deterministic for a given shape and plan.
+ *
+ * Scratch: split-K partials and counters live in buffers the library
+ * allocates per (device, stream) on the first call that needs them; a call
+ * that needs more allocates a larger set and keeps the old one (graphs that
+ * captured it stay valid) until w4a16_release().  An allocation cannot be
+ * captured: a call that would need one while its stream is capturing returns
+ * W4A16_ERR_WORKSPACE, so run a shape once on the stream before capturing
+ * it.  Calls on one stream from several host threads at once are not
+ * supported.
  *
  * Errors: INVALID_ARG for NULL b_packed/scales (or a/out with M > 0), M < 0, K/N/G <= 0,
  * N % 8 != 0, K % G != 0, zp_bias outside [0, 15] without qzeros, or `out`
@@ -137,9 +152,59 @@ typedef struct {
     int32_t zp_bias;
 } w4a16_linear;
 
+/* Glue applied to a linear's input by w4a16_gemm_glue. */
+typedef enum {
+    W4A16_GLUE_NONE = 0,    /* out = x[:, :K] . W                                   */
+    W4A16_GLUE_RMSNORM = 1, /* out = rn(x[:, :K]) . W                               */
+    W4A16_GLUE_SWIGLU = 2   /* out = rn(silu(x[:, :K]) * x[:, K:2K]) . W            */
+} w4a16_glue;
+
+/*
+ * One W4A16 linear on glue-transformed activations: the linears of the decode
+ * step (w4a16_decode_step is exactly a sequence of these calls, below).
+ * Follows: the vLLM PR #37352 write-up, "Code analysis" item 1, for the
+ * product; the glue between the linears of a decode pass (the inference-
+ * engine article, section 1.1, gives the blocks but no glue) is this
+ * library's reading:
+ *     rn(v)   = v / sqrt(mean(v^2) + 1e-6) per row, in fp32
+ *     silu(g) = g / (1 + exp(-g))
+ * Where the glue runs inside the GEMM (the default for the GEMV of M <= 8:
+ * the row-norm, and SwiGLU below 3 rows) the row scale multiplies the
+ * products, so the normalised activations are not rounded to fp16 on their
+ * own; where it runs as a kernel of its own (the default for the MFMA GEMM
+ * of M >= 9), its fp16 output goes through `workspace` and the GEMM reads it.
+ *
+ *   glue       a w4a16_glue value.
+ *   x          device fp16 rows of ldx elements: NONE reads [M, K] (ldx must
+ *              equal K), RMSNORM [M, K], SWIGLU [M, 2K] (gate, then up).
+ *   ldx        row stride in elements, a multiple of 8.
+ *   lin        host pointer to the linear (weights as for w4a16_gemm).
+ *   M          >= 0 rows (0: no-op).
+ *   out        device fp16 [M, N]; must not overlap x, the weights or
+ *              workspace.
+ *   workspace  device scratch of w4a16_gemm_glue_workspace_bytes() bytes
+ *              (0 when the glue runs inside the GEMM; NULL is then allowed),
+ *              caller-owned, not overlapping x or out.
+ * Errors: as w4a16_gemm; INVALID_ARG for a bad glue value, ldx, overlap or a
+ * short workspace; UNSUPPORTED for glue with K % 8 != 0 or K > 32768.
+ */
+size_t w4a16_gemm_glue_workspace_bytes(int glue, int64_t M, const w4a16_linear *lin);
+int w4a16_gemm_glue(int glue, const uint16_t *x, int64_t ldx, const w4a16_linear *lin, int64_t M,
+                    uint16_t *out, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * y[m][0..width) = rn(x[m][0..width)) (rn as for w4a16_gemm_glue), rounded to
+ * fp16: the last step of w4a16_decode_step.  x device fp16 rows of ldx
+ * elements (ldx >= width, both multiples of 8, width <= 32768); y device fp16
+ * [M, width], not overlapping x.  Errors: INVALID_ARG / UNSUPPORTED for bad
+ * sizes, HIP on launch failure.
+ */
+int w4a16_rownorm(const uint16_t *x, int64_t ldx, int64_t M, int64_t width, uint16_t *y, hipStream_t stream);
+
 /*
  * Scratch bytes w4a16_decode_step needs for M rows and this stack (0 if the
- * stack is malformed).  Host-only, no HIP calls.
+ * stack is malformed): three buffers of M x (widest linear output) fp16.
+ * Host-only, no HIP calls.
  */
 size_t w4a16_decode_workspace_bytes(int64_t M, const w4a16_linear *lin, int64_t n_layers);
 
@@ -157,7 +222,17 @@ size_t w4a16_decode_workspace_bytes(int64_t M, const w4a16_linear *lin, int64_t 
  *     h3 = rn(silu(gu[:, :I]) * gu[:, I:])
  *     x  = rn(lin[4l+3](h3))             [M, H]
  * rn(v) = v / sqrt(mean(v^2) + 1e-6) per row, computed in fp32; silu(x) =
- * x / (1 + exp(-x)).  Intermediates are stored as fp16.
+ * x / (1 + exp(-x)).  The step is exactly these calls (P, Q, R the three
+ * workspace buffers, glue scratch in R):
+ *     layer 0:   w4a16_gemm_glue(NONE, x_in, H, qkv)          -> P
+ *     layer l>0: w4a16_gemm_glue(RMSNORM, Q, H, qkv)          -> P
+ *                w4a16_gemm_glue(RMSNORM, P, Nq, o)           -> Q
+ *                w4a16_gemm_glue(RMSNORM, Q, H, gate_up)      -> P
+ *                w4a16_gemm_glue(SWIGLU, P, 2I, down)         -> Q
+ *     then       w4a16_rownorm(Q, H, M, H)                    -> x_out
+ * so each row-norm and SwiGLU folds into the GEMM that consumes it where
+ * that GEMM can take it (see w4a16_gemm_glue).  Intermediates are stored as
+ * fp16.
  *
  *   lin        host array of 4*n_layers linears: qkv, o, gate_up, down per layer
  *              (shapes must chain as above, else INVALID_ARG; H and I must be
@@ -176,8 +251,8 @@ int w4a16_decode_step(const w4a16_linear *lin, int64_t n_layers, const uint16_t 
 /*
  * Describe the plan w4a16_gemm would run for a shape (host-only, no HIP calls):
  * path 1 = GEMV on the vector ALUs (dot2), 3 = GEMV with its k-reduction on
- * the matrix cores (M <= 8), 2 = MFMA GEMM (tiles of 16+ rows); splits =
- * K-splits across workgroups;
+ * the matrix cores (M <= 8, the default there), 2 = MFMA GEMM (tiles of 16+
+ * rows); splits = K-splits across workgroups;
  * grid = workgroups launched.  Returns the status w4a16_gemm would return from
  * validation of the sizes alone (pointers are not examined).
  */
@@ -187,23 +262,32 @@ int w4a16_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t G, int32_t *path,
 /* Replace the planner's tuning overrides (the same "key=value,..." form the
  * environment variable W4A16_TUNE gives at first use; NULL or "" restores the
  * defaults).  Keys: gemv_mma (1 default: the matrix-core GEMV at M <= 8;
- * 0: the dot2 GEMV), gemv_target_waves (the dot2 GEMV's M <= 2 wave target),
+ * 0: the dot2 GEMV), gemv_mma_exact (1: the matrix-core GEMV takes exact
+ * (q - z) weights with a symmetric zero point too), gemv_mma_words (2 or 4
+ * words per lane: 256- or 512-column tiles, M <= 2; 0 by fill),
+ * gemv_target_waves (the dot2 GEMV's M <= 2 wave target),
  * gemv_waves (4 or 8; 4 selects the dot2 GEMV), gemv_splits,
  * gemv_fold (dot2 GEMV: 1 folded form, 0 exact form, -1 folded for symmetric
  * zero point at M <= 2), gemv_max_m,
- * mfma_target_waves, mfma_splits, mfma_cfg (1..6), mfma_mgroup (row tiles
+ * mfma_target_waves, mfma_splits, mfma_cfg (1..3: 16-row x 256-column, 32 x 256,
+ * 32 x 128 wave tiles), mfma_mgroup (row tiles
  * walked per column tile by consecutive workgroups), max_partial_bytes,
  * decode_fuse (0: the decode step runs its glue as separate kernels),
  * decode_swiglu_m (GEMV route: from this many rows on, default 3, SwiGLU +
- * row-norm runs as a kernel of its own instead of inside the down GEMV).  Every
+ * row-norm runs as a kernel of its own instead of inside the down GEMV),
+ * decode_rn_mfma (1: the MFMA GEMMs of M >= 9 fold the row-norm, applying the
+ * row scale to the products, instead of reading the row-norm kernel's fp16
+ * output).  Every
  * choice computes the same product; they differ in speed and in fp32
  * rounding.  Unknown keys or malformed values: W4A16_ERR_INVALID_ARG and the
  * current settings stay.  Affects calls planned after it returns; not
  * meant to race with calls in flight on other threads. */
 int w4a16_set_tuning(const char *spec);
 
-/* Free library-owned scratch on every device after synchronising the streams
- * that used it.  Safe to call at any time no w4a16 call is in flight. */
+/* Free library-owned scratch on every device (current and retired sets) after
+ * synchronising the streams that used it.  Safe to call at any time no w4a16
+ * call is in flight; graphs that captured w4a16 calls must not be replayed
+ * afterwards (their scratch is gone). */
 int w4a16_release(void);
 
 #ifdef __cplusplus

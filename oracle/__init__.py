@@ -20,6 +20,7 @@ from __future__ import annotations
 import ctypes
 import os
 import subprocess
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -218,3 +219,58 @@ def decode_step(layers, x, n_layers):
     if rc != 0:
         raise ValueError("oracle decode_step rejected the stack")
     return y.view(np.float16)
+
+
+def host_workers():
+    """Threads for the parallel helpers: the host's cores, at most 16 (the CPU
+    share of one GPU on the test machines)."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def split_columns(b_kn8, scales, qzeros, cols=512):
+    """Column slices (each a multiple of 8 columns, the last possibly shorter)
+    of the weights, scales and zero points, as contiguous arrays."""
+    b = _i32(b_kn8); s = _u16(scales); qz = _i32(qzeros)
+    N = b.shape[1] * 8
+    edges = list(range(0, N, cols)) + [N]
+    return [(np.ascontiguousarray(b[:, c0 // 8:c1 // 8]), np.ascontiguousarray(s[:, c0:c1]),
+             None if qz is None else np.ascontiguousarray(qz[:, c0 // 8:c1 // 8]))
+            for c0, c1 in zip(edges[:-1], edges[1:])]
+
+
+def gemm_split(a, parts, G, zp_bias=8, workers=None):
+    """gemm() over prepared column slices (split_columns), one thread per
+    slice at a time, the slices' outputs side by side.  Each output element is
+    computed by the same C function from the same inputs (a column slice is a
+    smaller instance of the same definition), so the result is identical to
+    one gemm() call; the library releases the GIL while it runs."""
+    a = _u16(a)
+    with ThreadPoolExecutor(max_workers=workers or host_workers()) as ex:
+        outs = list(ex.map(lambda t: gemm(a, t[0], t[1], t[2], G, zp_bias), parts))
+    return np.concatenate(outs, axis=1)
+
+
+def gemm_columns(a, b_kn8, scales, qzeros, G, zp_bias=8, workers=None, cols=512):
+    """gemm() evaluated over column slices in parallel threads (identical to
+    one gemm() call)."""
+    return gemm_split(a, split_columns(b_kn8, scales, qzeros, cols), G, zp_bias, workers)
+
+
+def decode_layer_columns(layers, x, workers=None):
+    """One decode-stack layer (the four linears of decode_step with its glue,
+    in the same order and roundings) with each product evaluated by
+    gemm_columns.  Equal bit for bit to decode_step(layers, x, 1)."""
+    L = layers
+    H = x.shape[1]
+    q = gemm_columns(x, L[0]["b_packed"], L[0]["scales"], L[0].get("qzeros"), L[0]["G"], L[0].get("zp_bias", 8),
+                     workers)
+    h = rownorm(q, H)
+    o = gemm_columns(h, L[1]["b_packed"], L[1]["scales"], L[1].get("qzeros"), L[1]["G"], L[1].get("zp_bias", 8),
+                     workers)
+    h = rownorm(o)
+    gu = gemm_columns(h, L[2]["b_packed"], L[2]["scales"], L[2].get("qzeros"), L[2]["G"], L[2].get("zp_bias", 8),
+                      workers)
+    h = swiglu_rownorm(gu)
+    d = gemm_columns(h, L[3]["b_packed"], L[3]["scales"], L[3].get("qzeros"), L[3]["G"], L[3].get("zp_bias", 8),
+                     workers)
+    return rownorm(d)

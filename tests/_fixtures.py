@@ -53,3 +53,11 @@ def unpack_rows(w):
     for j in range(8):
         q[:, j::8] = (w >> np.uint32(4 * j)) & 0xF
     return q
+
+
+
+def oracle_gemm_columns(a, b_kn8, scales, qzeros, G, zp_bias=8):
+    """The oracle's full product over column slices on the host's cores
+    (identical to one oracle.gemm call)."""
+    import oracle
+    return oracle.gemm_columns(a, b_kn8, scales, qzeros, G, zp_bias)

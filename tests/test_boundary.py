@@ -176,8 +176,8 @@ def _stack(K=64, NQ=96, I=128, G=32, layers=1, bad=False):
 def test_decode_workspace_bytes(lib):
     arr = _stack()
     nb = lib.w4a16_decode_workspace_bytes(3, ctypes.cast(arr, ctypes.c_void_p), 1)
-    # two buffers of 3 x max N (256) fp16, each 256-aligned
-    assert nb == 2 * 1536
+    # three buffers of 3 x max N (256) fp16, each 256-aligned
+    assert nb == 3 * 1536
     assert lib.w4a16_decode_workspace_bytes(3, ctypes.cast(_stack(bad=True), ctypes.c_void_p), 1) == 0
     assert lib.w4a16_decode_workspace_bytes(0, ctypes.cast(arr, ctypes.c_void_p), 1) == 0
 
@@ -208,3 +208,59 @@ def test_python_binding_rejects_host_tensors_and_bad_dtypes(lib):
         w4.w4a16_gemm(a.float(), b, s, None, 64)
     with pytest.raises(TypeError):
         w4.w4a16_repack(b.to(torch.int64), 256)
+
+
+def _linear(K=4096, N=12800, G=128):
+    return w4.Linear(B.value, S.value, None, K, N, G, 8)
+
+
+def test_gemm_glue_workspace_bytes(lib):
+    """Glue inside the GEMM needs no scratch: the row-norm in every GEMM path,
+    SwiGLU in the GEMV below 3 rows; otherwise M x K fp16 values, 256-aligned."""
+    down = _linear(12800, 4096)
+    ptr = ctypes.cast(ctypes.pointer(down), ctypes.c_void_p)
+    ws = lib.w4a16_gemm_glue_workspace_bytes
+    assert ws(w4.GLUE_NONE, 1, ptr) == 0
+    assert ws(w4.GLUE_RMSNORM, 1, ptr) == 0 and ws(w4.GLUE_RMSNORM, 32, ptr) == 32 * 12800 * 2
+    assert ws(w4.GLUE_SWIGLU, 1, ptr) == 0 and ws(w4.GLUE_SWIGLU, 2, ptr) == 0
+    assert ws(w4.GLUE_SWIGLU, 3, ptr) == 3 * 12800 * 2
+    assert ws(w4.GLUE_SWIGLU, 32, ptr) == 32 * 12800 * 2
+    assert ws(3, 1, ptr) == 0 and ws(w4.GLUE_RMSNORM, 0, ptr) == 0
+    try:
+        w4.w4a16_set_tuning("decode_fuse=0")  # every glue step a kernel of its own
+        assert ws(w4.GLUE_RMSNORM, 1, ptr) == 12800 * 2
+        w4.w4a16_set_tuning("decode_rn_mfma=1")  # the MFMA GEMM folds the row-norm
+        assert ws(w4.GLUE_RMSNORM, 32, ptr) == 0
+    finally:
+        w4.w4a16_set_tuning(None)
+
+
+def test_gemm_glue_rejects(lib):
+    lin = _linear(4096, 12800)
+    ptr = ctypes.cast(ctypes.pointer(lin), ctypes.c_void_p)
+    W = ctypes.c_void_p(0x20_0000_0000)
+    call = lib.w4a16_gemm_glue
+    assert call(3, A, 4096, ptr, 1, O, None, 0, None) == INVALID                   # bad glue value
+    assert call(w4.GLUE_NONE, A, 4104, ptr, 1, O, None, 0, None) == INVALID        # NONE needs ldx == K
+    assert call(w4.GLUE_SWIGLU, A, 4096, ptr, 1, O, None, 0, None) == INVALID      # SwiGLU reads 2K
+    assert call(w4.GLUE_RMSNORM, A, 4100, ptr, 1, O, None, 0, None) == INVALID     # ldx % 8
+    assert call(w4.GLUE_RMSNORM, None, 4096, ptr, 1, O, None, 0, None) == INVALID
+    assert call(w4.GLUE_RMSNORM, A, 4096, None, 1, O, None, 0, None) == INVALID
+    assert call(w4.GLUE_RMSNORM, A, 4096, ptr, 1, ctypes.c_void_p(A.value + 16), None, 0, None) == INVALID
+    assert call(w4.GLUE_SWIGLU, A, 8192, ptr, 32, O, None, 0, None) == INVALID     # needs workspace
+    assert call(w4.GLUE_SWIGLU, A, 8192, ptr, 32, O, ctypes.c_void_p(A.value), 1 << 24, None) == INVALID
+    assert call(w4.GLUE_RMSNORM, A, 4096, ptr, 32, O, None, 0, None) == INVALID    # M >= 9: row-norm kernel
+    assert call(w4.GLUE_RMSNORM, A, 4096, ptr, 0, None, None, 0, None) == OK      # M == 0
+    wide = _linear(32800, 4096, 32)
+    assert call(w4.GLUE_RMSNORM, A, 32800, ctypes.cast(ctypes.pointer(wide), ctypes.c_void_p), 1, O, W, 1 << 30,
+                None) == UNSUPPORTED
+
+
+def test_rownorm_rejects(lib):
+    call = lib.w4a16_rownorm
+    assert call(A, 64, 2, 60, O, None) == INVALID              # width % 8
+    assert call(A, 56, 2, 64, O, None) == INVALID              # ldx < width
+    assert call(None, 64, 2, 64, O, None) == INVALID
+    assert call(A, 64, 2, 64, ctypes.c_void_p(A.value + 64), None) == INVALID   # y overlaps x
+    assert call(A, 32776, 2, 32776, O, None) == UNSUPPORTED    # wider than the glue kernels take
+    assert call(A, 64, 0, 64, None, None) == OK

@@ -338,3 +338,17 @@ def test_glue_closed_form_with_epsilon(kind, width, pattern, want):
         gu = np.concatenate([np.full(width, gate, np.uint16), np.full(width, up, np.uint16)])[None, :]
         got = oracle.swiglu_rownorm(gu.view(np.float16)).view(np.uint16)[0]
         assert np.all(got == want[0])
+
+
+def test_parallel_helpers_equal_the_plain_calls():
+    """gemm_columns (column slices on threads) and decode_layer_columns equal
+    gemm and decode_step bit for bit, ragged last slice included."""
+    p = synth.problem(3, 256, 1032, 64, True, seed=21)
+    full = oracle.gemm(p["a"], p["b_packed"], p["scales"], p["qzeros"], 64)
+    par = oracle.gemm_columns(p["a"], p["b_packed"], p["scales"], p["qzeros"], 64, cols=256)
+    assert np.array_equal(full.view(np.uint16), par.view(np.uint16))
+    layers = _tiny_stack(1)
+    x = synth.stack_input(2, 64)
+    a = oracle.decode_step(layers, x, 1)
+    b = oracle.decode_layer_columns(layers, x)
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))

@@ -18,8 +18,9 @@ import os
 
 __all__ = [
     "W4A16Error", "lib", "w4a16_gemm", "w4a16_repack", "w4a16_repack_scales", "w4a16_decode_step",
-    "w4a16_decode_workspace_bytes", "w4a16_gemm_plan", "w4a16_release", "Linear",
-    "STATUS",
+    "w4a16_decode_workspace_bytes", "w4a16_gemm_glue", "w4a16_gemm_glue_workspace_bytes", "w4a16_rownorm",
+    "w4a16_gemm_plan", "w4a16_set_tuning", "w4a16_release", "Linear", "STATUS",
+    "GLUE_NONE", "GLUE_RMSNORM", "GLUE_SWIGLU",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -27,6 +28,7 @@ LIB_PATH = os.path.join(_HERE, "libw4a16.so")
 
 STATUS = {0: "W4A16_OK", 1: "W4A16_ERR_INVALID_ARG", 2: "W4A16_ERR_UNSUPPORTED",
           3: "W4A16_ERR_HIP", 4: "W4A16_ERR_WORKSPACE"}
+GLUE_NONE, GLUE_RMSNORM, GLUE_SWIGLU = 0, 1, 2
 
 
 class W4A16Error(RuntimeError):
@@ -68,6 +70,12 @@ def lib() -> ctypes.CDLL:
     L.w4a16_decode_workspace_bytes.argtypes = [I64, P, I64]
     L.w4a16_decode_step.restype = ctypes.c_int
     L.w4a16_decode_step.argtypes = [P, I64, P, P, I64, P, SZ, P]
+    L.w4a16_gemm_glue_workspace_bytes.restype = SZ
+    L.w4a16_gemm_glue_workspace_bytes.argtypes = [ctypes.c_int, I64, P]
+    L.w4a16_gemm_glue.restype = ctypes.c_int
+    L.w4a16_gemm_glue.argtypes = [ctypes.c_int, P, I64, P, I64, P, P, SZ, P]
+    L.w4a16_rownorm.restype = ctypes.c_int
+    L.w4a16_rownorm.argtypes = [P, I64, I64, I64, P, P]
     L.w4a16_gemm_plan.restype = ctypes.c_int
     L.w4a16_gemm_plan.argtypes = [I64, I64, I64, I64, ctypes.POINTER(ctypes.c_int32),
                                   ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]
@@ -210,6 +218,57 @@ def w4a16_decode_step(stack, x, out=None, workspace=None):
     _check(lib().w4a16_decode_step(ctypes.cast(arr, ctypes.c_void_p), nl, x.data_ptr(), out.data_ptr(), M,
                                    workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                    _stream_ptr(x.device)))
+    return out
+
+
+def _one_linear(linear):
+    arr = _linear_array([linear])
+    return arr, ctypes.cast(arr, ctypes.c_void_p)
+
+
+def w4a16_gemm_glue_workspace_bytes(glue, M, linear):
+    _keep, ptr = _one_linear(linear)
+    return int(lib().w4a16_gemm_glue_workspace_bytes(glue, M, ptr))
+
+
+def w4a16_gemm_glue(glue, x, linear, ldx=None, out=None, workspace=None):
+    """One linear on glue-transformed rows of x (fp16 [M, ldx] on the GPU):
+    GLUE_NONE out = x . W, GLUE_RMSNORM out = rn(x[:, :K]) . W, GLUE_SWIGLU
+    out = rn(silu(x[:, :K]) * x[:, K:2K]) . W; `linear` is a dict like the
+    decode stack's entries."""
+    torch = _torch()
+    _dev_tensor(x, "x", torch.float16, 2)
+    M = x.shape[0]
+    ldx = x.shape[1] if ldx is None else ldx
+    keep, ptr = _one_linear(linear)
+    N = keep[0].N
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    else:
+        _dev_tensor(out, "out", torch.float16, 2)
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out must be [M, N] = [%d, %d]" % (M, N))
+    need = int(lib().w4a16_gemm_glue_workspace_bytes(glue, M, ptr))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wptr = None if workspace is None else workspace.data_ptr()
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().w4a16_gemm_glue(glue, x.data_ptr(), ldx, ptr, M, out.data_ptr(), wptr, wbytes,
+                                 _stream_ptr(x.device)))
+    return out
+
+
+def w4a16_rownorm(x, width=None, out=None):
+    """y = rn(x[:, :width]) (fp16 [M, width]) for fp16 rows x on the GPU."""
+    torch = _torch()
+    _dev_tensor(x, "x", torch.float16, 2)
+    M, ldx = x.shape
+    width = ldx if width is None else width
+    if out is None:
+        out = torch.empty((M, width), dtype=torch.float16, device=x.device)
+    else:
+        _dev_tensor(out, "out", torch.float16, 2)
+    _check(lib().w4a16_rownorm(x.data_ptr(), ldx, M, width, out.data_ptr(), _stream_ptr(x.device)))
     return out
 
 

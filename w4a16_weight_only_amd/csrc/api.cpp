@@ -12,6 +12,7 @@
 #include <mutex>
 #include <string>
 #include <utility>
+#include <vector>
 
 #include "w4a16.h"
 #include "kernels.h"
@@ -58,13 +59,15 @@ struct Tune {
     int64_t gemv_max_m = 8;            // largest M sent to the GEMV path (at most 8)
     int64_t gemv_mma = 1;              // GEMV k-reduction on the matrix cores (0: the dot2 GEMV)
     int64_t gemv_mma_words = 0;        // matrix-core GEMV words per lane: 2 (256-column tiles), 4 (512, M <= 2), 0 by fill
+    int64_t gemv_mma_exact = 0;        // matrix-core GEMV, symmetric zero point: 1 exact (q - z) weights
     int64_t mfma_target_waves = 2048;  // aim for about this many MFMA-path waves
     int64_t mfma_splits = 0;           // force the MFMA split count
-    int64_t mfma_cfg = 0;  // force (mt, waves, kwaves): 1..6 = (1,2,4) (2,2,4) (4,2,2) (2,1,8) (4,2,4) (4,1,8)
+    int64_t mfma_cfg = 0;  // force (mt, waves, kwaves): 1..3 = (1,2,4) (2,2,4) (2,1,8)
     int64_t mfma_mgroup = 0;           // force the MFMA row-tile group (0: by estimated L2 traffic)
     int64_t max_partial_bytes = 64ll << 20;
     int64_t decode_fuse = 1;           // 0: decode-step glue as separate kernels
     int64_t decode_swiglu_m = 3;       // GEMV route: from this M on, SwiGLU + row-norm as a kernel of its own
+    int64_t decode_rn_mfma = 0;        // 1: the MFMA GEMMs fold the row-norm (no fp16 rounding of rn(x))
 };
 
 // Returns false on an unknown key or a malformed entry (nothing applied).
@@ -91,6 +94,7 @@ bool parse_tune(const char *spec, Tune *out) {
         else if (k == "gemv_max_m") v.gemv_max_m = val;
         else if (k == "gemv_mma") v.gemv_mma = val;
         else if (k == "gemv_mma_words") v.gemv_mma_words = val;
+        else if (k == "gemv_mma_exact") v.gemv_mma_exact = val;
 
         else if (k == "mfma_target_waves") v.mfma_target_waves = val;
         else if (k == "mfma_splits") v.mfma_splits = val;
@@ -99,6 +103,7 @@ bool parse_tune(const char *spec, Tune *out) {
         else if (k == "max_partial_bytes") v.max_partial_bytes = val;
         else if (k == "decode_fuse") v.decode_fuse = val;
         else if (k == "decode_swiglu_m") v.decode_swiglu_m = val;
+        else if (k == "decode_rn_mfma") v.decode_rn_mfma = val;
         else return false;
     }
     *out = v;
@@ -180,7 +185,7 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma, b
                 if (fewer < splits && 4 * fewer * p.tiles_n >= 3 * 256 * per_cu) splits = fewer;
             }
         }
-        splits = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(splits, 32), nchunks));
+        splits = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(splits, kGemvMaxSplits), nchunks));
         p.split_len = cdiv(nchunks, splits);
         p.splits = (int)cdiv(nchunks, p.split_len);
         p.tiles_m = 1;
@@ -202,7 +207,9 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma, b
             // 100 tiles x 2 splits = 200 workgroups against 50 x 5 = 250,
             // 13.72 -> 12.27 us.  So at M <= 2, when 256-column tiles fill under
             // 85% of the CUs and 512-column ones at least 10% more.
-            auto fill = [](int64_t tiles) { return tiles * std::max<int64_t>(1, std::min<int64_t>(32, 256 / tiles)); };
+            auto fill = [](int64_t tiles) {
+                return tiles * std::max<int64_t>(1, std::min<int64_t>(kGemvMaxSplits, 256 / tiles));
+            };
             const int64_t t2 = cdiv(N8, 32), t4 = cdiv(N8, 64);
             const bool wide = t.gemv_mma_words == 4 ||
                               (t.gemv_mma_words == 0 && fill(t2) < 218 && fill(t4) >= fill(t2) + 26);
@@ -213,10 +220,11 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma, b
             }
             const int64_t mchunks = K / kMmaChunkRows;
             int64_t ms = t.gemv_splits > 0 ? t.gemv_splits : std::max<int64_t>(1, 256 / p.tiles_n);
-            ms = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(ms, 32), mchunks));
+            ms = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(ms, kGemvMaxSplits), mchunks));
             p.split_len = cdiv(mchunks, ms);
             p.splits = (int)cdiv(mchunks, p.split_len);
             p.mma = true;
+            p.exact = t.gemv_mma_exact != 0;
             p.fold = p.fold_asym = false;
         }
     } else {
@@ -249,8 +257,8 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma, b
             p.split_len = cdiv(nsteps, splits);
             p.splits = (int)cdiv(nsteps, p.split_len);
         };
-        static const int kCfg[6][3] = {{1, 2, 4}, {2, 2, 4}, {4, 2, 2}, {2, 1, 8}, {4, 2, 4}, {4, 1, 8}};
-        if (t.mfma_cfg >= 1 && t.mfma_cfg <= 6) {
+        static const int kCfg[3][3] = {{1, 2, 4}, {2, 2, 4}, {2, 1, 8}};
+        if (t.mfma_cfg >= 1 && t.mfma_cfg <= 3) {
             fill(kCfg[t.mfma_cfg - 1][0], kCfg[t.mfma_cfg - 1][1], kCfg[t.mfma_cfg - 1][2]);
         } else if (M <= 16) {
             // One 16-row tile.  Measured on MI355X at M = 9..16: the 256-column
@@ -260,21 +268,18 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma, b
             // N = 6144 within 0.1 us at M = 9 and 0.7 us better at M = 16.
             if (cdiv(N8, 32) <= 24) fill(2, 1, 8);
             else fill(1, 2, 4);
-        } else if (M <= 32) {
-            fill(2, 1, 8);
         } else {
-            // 64-row wave tiles: 256 columns with 2 or 4 K-waves, or 128 columns
-            // with 8 K-waves (twice the tiles, so half the K-splits, or a full
-            // chip where 256-column tiles leave CUs idle).  Measured on MI355X:
-            // prefer the shape that keeps the most CUs busy per round of
-            // workgroups, then the fewest K-splits (split partials go through
-            // memory), then the fewest workgroups.
-            static const int kBig[3][3] = {{4, 2, 2}, {4, 2, 4}, {4, 1, 8}};
+            // 32-row wave tiles (a wave keeps each group's sums and the scaled
+            // totals, 128 accumulator registers): 256 columns with 4 K-waves or
+            // 128 columns with 8.  Prefer the shape that keeps the most CUs
+            // busy per round of workgroups, then the fewest K-splits (split
+            // partials go through memory), then the fewest workgroups.
+            static const int kBig[2][3] = {{2, 1, 8}, {2, 2, 4}};
             int best = -1;
             double best_eff = -1;
             int best_splits = 0;
             int64_t best_grid = 0;
-            for (int c = 0; c < 3; ++c) {
+            for (int c = 0; c < 2; ++c) {
                 fill(kBig[c][0], kBig[c][1], kBig[c][2]);
                 const int64_t grid = p.tiles_n * p.tiles_m * p.splits;
                 const int64_t rounds = cdiv(grid, 256);
@@ -335,7 +340,11 @@ namespace {
 // Split-K partials and arrival counters / fixed-point slots, one set per
 // (device, stream).  The counter words are zeroed once at allocation; the
 // last arrival at each counter or slot zeroes it again, so they are zero
-// whenever the stream is idle.
+// whenever the stream is idle.  A set that is outgrown is retired, not
+// freed: a captured graph may still launch kernels that use it, so retired
+// sets live until w4a16_release().  Growing needs an allocation, which is
+// refused while the stream is being captured (a captured graph cannot record
+// it); the caller runs the call once outside capture first.
 struct Scratch {
     float *partials = nullptr;
     size_t partial_cap = 0;  // floats
@@ -345,6 +354,7 @@ struct Scratch {
 
 std::mutex g_mu;
 std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
+std::vector<std::pair<int, void *>> g_retired;  // (device, pointer), freed by w4a16_release
 
 int get_scratch(hipStream_t stream, const GemmPlan &plan, float **partials, uint32_t **counters) {
     *partials = nullptr;
@@ -356,28 +366,32 @@ int get_scratch(hipStream_t stream, const GemmPlan &plan, float **partials, uint
     std::lock_guard<std::mutex> lock(g_mu);
     Scratch &s = g_scratch[{dev, stream}];
     if (s.partial_cap < plan.partial_floats || s.counter_cap < plan.counters) {
-        // Growing: the old buffers may still be read by queued kernels.
-        if (s.partials || s.counters) {
-            e = hipStreamSynchronize(stream);
-            if (e != hipSuccess) return fail(W4A16_ERR_HIP, std::string("hipStreamSynchronize: ") + hipGetErrorString(e));
-            (void)hipFree(s.partials);
-            (void)hipFree(s.counters);
-            s = Scratch();
-        }
-        const size_t pcap = std::max<size_t>(plan.partial_floats, (size_t)1 << 20);
-        const size_t ccap = std::max<size_t>(plan.counters, (size_t)1 << 14);
-        e = hipMalloc((void **)&s.partials, pcap * sizeof(float));
-        if (e != hipSuccess) { s = Scratch(); return fail(W4A16_ERR_WORKSPACE, "hipMalloc of split-K partials failed"); }
-        e = hipMalloc((void **)&s.counters, ccap * sizeof(uint32_t));
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        e = hipStreamIsCapturing(stream, &cap);
+        if (e != hipSuccess || cap != hipStreamCaptureStatusNone)
+            return fail(W4A16_ERR_WORKSPACE,
+                        "split-K scratch for this shape must be allocated outside stream capture: run the call "
+                        "once on this stream before capturing it");
+        Scratch n;
+        n.partial_cap = std::max<size_t>(std::max(plan.partial_floats, s.partial_cap), (size_t)1 << 20);
+        n.counter_cap = std::max<size_t>(std::max(plan.counters, s.counter_cap), (size_t)1 << 14);
+        e = hipMalloc((void **)&n.partials, n.partial_cap * sizeof(float));
+        if (e != hipSuccess) return fail(W4A16_ERR_WORKSPACE, "hipMalloc of split-K partials failed");
+        e = hipMalloc((void **)&n.counters, n.counter_cap * sizeof(uint32_t));
         if (e != hipSuccess) {
-            (void)hipFree(s.partials);
-            s = Scratch();
+            (void)hipFree(n.partials);
             return fail(W4A16_ERR_WORKSPACE, "hipMalloc of split-K counters failed");
         }
-        e = hipMemsetAsync(s.counters, 0, ccap * sizeof(uint32_t), stream);
-        if (e != hipSuccess) return fail(W4A16_ERR_HIP, std::string("hipMemsetAsync: ") + hipGetErrorString(e));
-        s.partial_cap = pcap;
-        s.counter_cap = ccap;
+        e = hipMemsetAsync(n.counters, 0, n.counter_cap * sizeof(uint32_t), stream);
+        if (e != hipSuccess) {
+            (void)hipFree(n.partials);
+            (void)hipFree(n.counters);
+            return fail(W4A16_ERR_HIP, std::string("hipMemsetAsync: ") + hipGetErrorString(e));
+        }
+        // queued or captured work may still use the old set
+        if (s.partials) g_retired.emplace_back(dev, s.partials);
+        if (s.counters) g_retired.emplace_back(dev, s.counters);
+        s = n;
     }
     *partials = s.partials;
     *counters = s.counters;
@@ -418,16 +432,17 @@ int run_gemm(const uint16_t *a, const int32_t *b, const uint16_t *s, const int32
     return ok();
 }
 
-// GEMV whose activations are the glue transform (act 1: row-norm, act 2:
-// SwiGLU + row-norm) of `src` (row stride ld), for the decode step.
-int run_gemm_act(int act, const uint16_t *src, int64_t ld, const w4a16_linear &L, int64_t M, int64_t K, int64_t N,
-                 uint16_t *out, hipStream_t stream) {
-    GemmPlan plan = plan_gemm(M, K, N, L.G, true, act != 2);
+// GEMM on glue-transformed activations (act 1: row-norm of src[:, :K];
+// act 2: SwiGLU + row-norm of src[:, :2K]) with the glue inside the kernel:
+// the GEMV (8-wave plans) folds both, the MFMA GEMM the row-norm.
+int run_gemm_act(int act, const uint16_t *src, int64_t ld, const w4a16_linear &L, int64_t M, uint16_t *out,
+                 hipStream_t stream) {
+    GemmPlan plan = plan_gemm(M, L.K, L.N, L.G, true, act != 2);
     if (plan.path == kPathMfma) {
         if (act != 1) return fail(W4A16_ERR_UNSUPPORTED, "the MFMA path folds the row-norm only");
         plan.partial_floats += mfma_rn_extra_floats(plan);
     }
-    GemmArgs args{nullptr, L.b_packed, L.scales, L.qzeros, M, K, N, L.G, L.zp_bias, out, nullptr, nullptr};
+    GemmArgs args{nullptr, L.b_packed, L.scales, L.qzeros, M, L.K, L.N, L.G, L.zp_bias, out, nullptr, nullptr};
     int rc = get_scratch(stream, plan, &args.partials, &args.counters);
     if (rc != W4A16_OK) return rc;
     hipError_t e = plan.path == kPathMfma ? launch_mfma_rn(args, plan, true, src, ld, stream)
@@ -440,13 +455,66 @@ int run_gemm_act(int act, const uint16_t *src, int64_t ld, const w4a16_linear &L
 // default shape (M <= 8, 8 waves).
 bool fusable(const GemmPlan &p) { return p.path == kPathGemv && p.waves == 8; }
 
-// Decode-step workspace layout: two buffers of M x maxN fp16 (maxN = the
-// widest linear output), each 256-byte aligned.
-struct DecodeShape {
-    int64_t H = 0, NQ = 0, I = 0, maxN = 0, maxK = 0;
-};
+// Where the glue of one linear runs: inside its GEMM, or as a kernel of its
+// own into a scratch buffer of M x K fp16 values (the row-normed input, or
+// the SwiGLU output).  The GEMV (M <= 8) folds the row-norm, and SwiGLU below
+// decode_swiglu_m rows, applying the row scale to the products.  The MFMA
+// GEMM (M >= 9) takes the glue as a kernel of its own by default, so that the
+// normalised activations are rounded to fp16 as the glue reading rounds
+// them: folded (decode_rn_mfma=1) the rounding is skipped, and on an 8B-class
+// layer at M = 16 and 32 a SwiGLU outlier of 73x the row rms carried that
+// difference to 0.0107 of an output against the 0.01 bound (every linear on
+// its own stays within 0.005).  With decode_fuse=0 every glue step is a
+// kernel of its own and the GEMMs take the oracle's roundings (the dot2
+// GEMV's exact form).
+bool glue_in_kernel(int act, int64_t M, const w4a16_linear &L) {
+    if (act == 0) return true;
+    const Tune &t = tune();
+    if (t.decode_fuse == 0) return false;
+    const GemmPlan p = plan_gemm(M, L.K, L.N, L.G, true, act != 2);
+    if (act == 1) return fusable(p) || (p.path == kPathMfma && t.decode_rn_mfma != 0);
+    return fusable(p) && M < t.decode_swiglu_m;  // SwiGLU: inside GEMVs below decode_swiglu_m rows
+}
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t glue_tmp_bytes(int act, int64_t M, const w4a16_linear &L) {
+    return glue_in_kernel(act, M, L) ? 0 : align256((size_t)M * L.K * 2);
+}
+
+// One linear on glue-transformed activations (act 0: none; src is then dense
+// [M, K]).  tmp: glue_tmp_bytes() bytes, distinct from src and out.
+int run_linear_glue(int act, const uint16_t *src, int64_t ld, const w4a16_linear &L, int64_t M, uint16_t *out,
+                    uint16_t *tmp, hipStream_t stream) {
+    if (M == 0) return ok();
+    const bool exact_form = tune().decode_fuse == 0;
+    if (act == 0)
+        return run_gemm(src, L.b_packed, L.scales, L.qzeros, M, L.K, L.N, L.G, L.zp_bias, out, stream, exact_form);
+    if (glue_in_kernel(act, M, L)) return run_gemm_act(act, src, ld, L, M, out, stream);
+    hipError_t e = act == 1 ? launch_rownorm(src, M, ld, L.K, tmp, stream)
+                            : launch_swiglu_rownorm(src, M, ld, L.K, tmp, stream);
+    if (e != hipSuccess) return fail(W4A16_ERR_HIP, std::string("glue launch: ") + hipGetErrorString(e));
+    return run_gemm(tmp, L.b_packed, L.scales, L.qzeros, M, L.K, L.N, L.G, L.zp_bias, out, stream, exact_form);
+}
+
+// Host checks of one linear (weights, sizes, zero point, alignment).
+int check_linear(const w4a16_linear &L) {
+    if (!L.b_packed || !L.scales) return fail(W4A16_ERR_INVALID_ARG, "linear with NULL weights or scales");
+    int rc = validate_sizes(1, L.K, L.N, L.G);
+    if (rc != W4A16_OK) return rc;
+    if (!L.qzeros && (L.zp_bias < 0 || L.zp_bias > 15))
+        return fail(W4A16_ERR_INVALID_ARG, "zp_bias must be in [0, 15]");
+    if (!aligned16(L.b_packed) || !aligned16(L.scales) || (L.qzeros && !aligned16(L.qzeros)))
+        return fail(W4A16_ERR_UNSUPPORTED, "weights, scales and qzeros must be 16-byte aligned");
+    return W4A16_OK;
+}
+
+// Decode-step workspace layout: three buffers of M x maxN fp16 (maxN = the
+// widest linear output, which is at least every K of the stack), each
+// 256-byte aligned.
+struct DecodeShape {
+    int64_t H = 0, maxN = 0;
+};
 
 int check_stack(const w4a16_linear *lin, int64_t n_layers, DecodeShape *sh) {
     if (!lin || n_layers <= 0) return fail(W4A16_ERR_INVALID_ARG, "empty stack");
@@ -460,22 +528,13 @@ int check_stack(const w4a16_linear *lin, int64_t n_layers, DecodeShape *sh) {
             L[3].K != I || L[3].N != H)
             return fail(W4A16_ERR_INVALID_ARG, "stack shapes do not chain (qkv, o, gate_up, down)");
         for (int j = 0; j < 4; ++j) {
-            if (!L[j].b_packed || !L[j].scales)
-                return fail(W4A16_ERR_INVALID_ARG, "stack linear with NULL weights or scales");
-            int rc = validate_sizes(1, L[j].K, L[j].N, L[j].G);
+            int rc = check_linear(L[j]);
             if (rc != W4A16_OK) return rc;
-            if (!L[j].qzeros && (L[j].zp_bias < 0 || L[j].zp_bias > 15))
-                return fail(W4A16_ERR_INVALID_ARG, "zp_bias must be in [0, 15]");
-            if (!aligned16(L[j].b_packed) || !aligned16(L[j].scales) || (L[j].qzeros && !aligned16(L[j].qzeros)))
-                return fail(W4A16_ERR_UNSUPPORTED, "stack tensors must be 16-byte aligned");
             d.maxN = std::max(d.maxN, L[j].N);
         }
         if (H % 8 != 0 || I % 8 != 0 || H > kGlueMaxWidth || I > kGlueMaxWidth)
             return fail(W4A16_ERR_UNSUPPORTED, "decode step needs H and I multiples of 8 and at most 32768");
-        d.I = std::max(d.I, I);
-        d.NQ = std::max(d.NQ, L[0].N);
     }
-    d.maxK = std::max(d.H, d.I);
     *sh = d;
     return W4A16_OK;
 }
@@ -544,7 +603,7 @@ int w4a16_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t G, int32_t *path, i
 size_t w4a16_decode_workspace_bytes(int64_t M, const w4a16_linear *lin, int64_t n_layers) {
     DecodeShape d;
     if (M <= 0 || check_stack(lin, n_layers, &d) != W4A16_OK) return 0;
-    return 2 * align256((size_t)M * d.maxN * 2);
+    return 3 * align256((size_t)M * d.maxN * 2);
 }
 
 int w4a16_decode_step(const w4a16_linear *lin, int64_t n_layers, const uint16_t *x_in, uint16_t *x_out,
@@ -555,7 +614,7 @@ int w4a16_decode_step(const w4a16_linear *lin, int64_t n_layers, const uint16_t 
     int rc = check_stack(lin, n_layers, &d);
     if (rc != W4A16_OK) return rc;
     const size_t buf_bytes = align256((size_t)M * d.maxN * 2);
-    const size_t need = 2 * buf_bytes;
+    const size_t need = 3 * buf_bytes;
     if (workspace_bytes < need) return fail(W4A16_ERR_INVALID_ARG, "workspace smaller than w4a16_decode_workspace_bytes()");
     if (M * d.maxN >= (1ll << 31)) return fail(W4A16_ERR_UNSUPPORTED, "decode step too large for 32-bit kernel indexing");
     if (!aligned16(x_in) || !aligned16(x_out) || !aligned16(workspace))
@@ -563,81 +622,78 @@ int w4a16_decode_step(const w4a16_linear *lin, int64_t n_layers, const uint16_t 
     const size_t x_b = (size_t)M * d.H * 2;
     if (overlaps(workspace, need, x_in, x_b) || overlaps(workspace, need, x_out, x_b))
         return fail(W4A16_ERR_INVALID_ARG, "workspace overlaps x_in or x_out");
-    // Two buffers, each M x maxN: every kernel reads one and writes the other.
-    uint16_t *A = static_cast<uint16_t *>(workspace);
-    uint16_t *B = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + buf_bytes);
-    auto other = [&](const uint16_t *p) { return p == A ? B : A; };
-    auto glue = [](hipError_t e) {
-        return e == hipSuccess ? W4A16_OK
-                               : fail(W4A16_ERR_HIP, std::string("glue launch: ") + hipGetErrorString(e));
-    };
-    const bool fuse = tune().decode_fuse != 0;
-    const uint16_t *x = x_in;  // the layer input, row-normed (when pend is null)
-    uint16_t *pend = nullptr;  // or: the previous layer's down output, its row-norm not yet applied
+    // Three buffers P, Q, R of M x maxN.  Per layer, the w4a16_gemm_glue calls
+    // the header lists: q -> P, o -> Q, gate+up -> P, down -> Q; R takes a glue
+    // step that runs as a kernel of its own.
+    char *ws = static_cast<char *>(workspace);
+    uint16_t *P = reinterpret_cast<uint16_t *>(ws), *Q = reinterpret_cast<uint16_t *>(ws + buf_bytes),
+             *R = reinterpret_cast<uint16_t *>(ws + 2 * buf_bytes);
+    const int64_t H = d.H;
     for (int64_t l = 0; l < n_layers; ++l) {
         const w4a16_linear *L = lin + 4 * l;
-        const int64_t H = d.H, NQ = L[0].N, I = L[2].N / 2;
-        const GemmPlan pq = plan_gemm(M, H, NQ, L[0].G), po = plan_gemm(M, H, H, L[1].G),
-                       pg = plan_gemm(M, H, 2 * I, L[2].G), pd = plan_gemm(M, I, H, L[3].G);
-        // GEMV route (M <= 8): every glue step runs inside the GEMV that consumes
-        // it.  MFMA route: the row-norms run inside the MFMA GEMMs that consume
-        // them; SwiGLU + row-norm stays a kernel of its own.
-        const bool gemv_route = fuse && fusable(po) && fusable(pg) && fusable(pd);
-        const bool mfma_route = fuse && !gemv_route && po.path == kPathMfma && pg.path == kPathMfma;
-        const bool qkv_rn = pend && ((gemv_route && fusable(pq)) || (mfma_route && pq.path == kPathMfma));
-        if (pend && !qkv_rn) {
-            if ((rc = glue(launch_rownorm(pend, M, H, H, x_out, stream)))) return rc;
-            x = x_out;
-            pend = nullptr;
-        }
-        uint16_t *q = pend ? other(pend) : A;
-        uint16_t *o = other(q);
-        if ((rc = qkv_rn ? run_gemm_act(1, pend, H, L[0], M, H, NQ, q, stream)
-                         : run_gemm(x, L[0].b_packed, L[0].scales, L[0].qzeros, M, H, NQ, L[0].G, L[0].zp_bias,
-                                    q, stream, !fuse)))
+        const int64_t NQ = L[0].N, I = L[2].N / 2;
+        if ((rc = l == 0 ? run_linear_glue(0, x_in, H, L[0], M, P, R, stream)
+                         : run_linear_glue(1, Q, H, L[0], M, P, R, stream)) ||
+            (rc = run_linear_glue(1, P, NQ, L[1], M, Q, R, stream)) ||
+            (rc = run_linear_glue(1, Q, H, L[2], M, P, R, stream)) ||
+            (rc = run_linear_glue(2, P, 2 * I, L[3], M, Q, R, stream)))
             return rc;
-        if (gemv_route && M < tune().decode_swiglu_m) {
-            // q -> o (O), o -> q (gate+up), q -> o (down)
-            if ((rc = run_gemm_act(1, q, NQ, L[1], M, H, H, o, stream)) ||
-                (rc = run_gemm_act(1, o, H, L[2], M, H, 2 * I, q, stream)) ||
-                (rc = run_gemm_act(2, q, 2 * I, L[3], M, I, H, o, stream)))
-                return rc;
-            pend = o;
-        } else if (gemv_route) {
-            // SwiGLU folded into the down GEMV costs every workgroup M x I
-            // SwiGLUs for its row sums; from decode_swiglu_m rows on it runs
-            // as a kernel of its own.  q -> o (O), o -> q (gate+up),
-            // q -> o (SwiGLU + row-norm), o -> q (down)
-            if ((rc = run_gemm_act(1, q, NQ, L[1], M, H, H, o, stream)) ||
-                (rc = run_gemm_act(1, o, H, L[2], M, H, 2 * I, q, stream)) ||
-                (rc = glue(launch_swiglu_rownorm(q, M, I, o, stream))) ||
-                (rc = run_gemm(o, L[3].b_packed, L[3].scales, L[3].qzeros, M, I, H, L[3].G, L[3].zp_bias, q,
-                               stream)))
-                return rc;
-            pend = q;
-        } else if (mfma_route) {
-            // q -> o (O), o -> q (gate+up), q -> o (SwiGLU + row-norm), o -> q (down)
-            if ((rc = run_gemm_act(1, q, NQ, L[1], M, H, H, o, stream)) ||
-                (rc = run_gemm_act(1, o, H, L[2], M, H, 2 * I, q, stream)) ||
-                (rc = glue(launch_swiglu_rownorm(q, M, I, o, stream))) ||
-                (rc = run_gemm(o, L[3].b_packed, L[3].scales, L[3].qzeros, M, I, H, L[3].G, L[3].zp_bias, q,
-                               stream, true)))
-                return rc;
-            pend = q;
-        } else {
-            // every glue step a kernel of its own
-            if ((rc = glue(launch_rownorm(q, M, NQ, H, o, stream))) ||
-                (rc = run_gemm(o, L[1].b_packed, L[1].scales, L[1].qzeros, M, H, H, L[1].G, L[1].zp_bias, q, stream, true)) ||
-                (rc = glue(launch_rownorm(q, M, H, H, o, stream))) ||
-                (rc = run_gemm(o, L[2].b_packed, L[2].scales, L[2].qzeros, M, H, 2 * I, L[2].G, L[2].zp_bias, q, stream, true)) ||
-                (rc = glue(launch_swiglu_rownorm(q, M, I, o, stream))) ||
-                (rc = run_gemm(o, L[3].b_packed, L[3].scales, L[3].qzeros, M, I, H, L[3].G, L[3].zp_bias, q, stream, true)) ||
-                (rc = glue(launch_rownorm(q, M, H, H, x_out, stream))))
-                return rc;
-            x = x_out;
-        }
     }
-    if (pend && (rc = glue(launch_rownorm(pend, M, d.H, d.H, x_out, stream)))) return rc;
+    hipError_t e = launch_rownorm(Q, M, H, H, x_out, stream);
+    if (e != hipSuccess) return fail(W4A16_ERR_HIP, std::string("glue launch: ") + hipGetErrorString(e));
+    return ok();
+}
+
+size_t w4a16_gemm_glue_workspace_bytes(int glue, int64_t M, const w4a16_linear *lin) {
+    if (!lin || M <= 0 || glue < 0 || glue > 2 || check_linear(*lin) != W4A16_OK) return 0;
+    return glue_tmp_bytes(glue, M, *lin);
+}
+
+int w4a16_gemm_glue(int glue, const uint16_t *x, int64_t ldx, const w4a16_linear *lin, int64_t M, uint16_t *out,
+                    void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!lin) return fail(W4A16_ERR_INVALID_ARG, "lin must be non-NULL");
+    if (glue < 0 || glue > 2) return fail(W4A16_ERR_INVALID_ARG, "glue must be 0 (none), 1 (row-norm) or 2 (SwiGLU)");
+    int rc = check_linear(*lin);
+    if (rc != W4A16_OK) return rc;
+    const w4a16_linear &L = *lin;
+    if (M < 0) return fail(W4A16_ERR_INVALID_ARG, "M must be >= 0");
+    if (M == 0) return ok();
+    if (!x || !out) return fail(W4A16_ERR_INVALID_ARG, "x and out must be non-NULL when M > 0");
+    rc = validate_sizes(M, L.K, L.N, L.G);
+    if (rc != W4A16_OK) return rc;
+    const int64_t width = glue == 2 ? 2 * L.K : L.K;
+    if (glue == 0 && ldx != L.K) return fail(W4A16_ERR_INVALID_ARG, "without glue x must be dense: ldx == K");
+    if (ldx < width || ldx % 8 != 0) return fail(W4A16_ERR_INVALID_ARG, "ldx must be a multiple of 8 covering the row");
+    if (glue != 0 && (L.K % 8 != 0 || L.K > kGlueMaxWidth))
+        return fail(W4A16_ERR_UNSUPPORTED, "glue needs K a multiple of 8 and at most 32768");
+    if (M * std::max(ldx, L.N) >= (1ll << 31)) return fail(W4A16_ERR_UNSUPPORTED, "too large for 32-bit kernel indexing");
+    const size_t need = glue_tmp_bytes(glue, M, L);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(W4A16_ERR_INVALID_ARG, "workspace smaller than w4a16_gemm_glue_workspace_bytes()");
+    const size_t x_b = (size_t)((M - 1) * ldx + width) * 2, out_b = (size_t)M * L.N * 2;
+    if (!aligned16(x) || !aligned16(out) || (need && !aligned16(workspace)))
+        return fail(W4A16_ERR_UNSUPPORTED, "x, out and workspace must be 16-byte aligned");
+    if (overlaps(out, out_b, x, x_b) || overlaps(out, out_b, L.b_packed, (size_t)L.K * (L.N / 8) * 4) ||
+        overlaps(out, out_b, L.scales, (size_t)(L.K / L.G) * L.N * 2) ||
+        overlaps(out, out_b, L.qzeros, (size_t)(L.K / L.G) * (L.N / 8) * 4) ||
+        (need && (overlaps(workspace, need, x, x_b) || overlaps(workspace, need, out, out_b))))
+        return fail(W4A16_ERR_INVALID_ARG, "out, x and workspace must not overlap (nor out an input)");
+    return run_linear_glue(glue, x, ldx, L, M, out, need ? static_cast<uint16_t *>(workspace) : nullptr, stream);
+}
+
+int w4a16_rownorm(const uint16_t *x, int64_t ldx, int64_t M, int64_t width, uint16_t *y, hipStream_t stream) {
+    if (M < 0 || width <= 0) return fail(W4A16_ERR_INVALID_ARG, "M must be >= 0 and width > 0");
+    if (M == 0) return ok();
+    if (!x || !y) return fail(W4A16_ERR_INVALID_ARG, "x and y must be non-NULL when M > 0");
+    if (width % 8 != 0 || ldx < width || ldx % 8 != 0)
+        return fail(W4A16_ERR_INVALID_ARG, "width and ldx must be multiples of 8 with ldx >= width");
+    if (width > kGlueMaxWidth || M * ldx >= (1ll << 31))
+        return fail(W4A16_ERR_UNSUPPORTED, "width above 32768 or too large for 32-bit indexing");
+    if (!aligned16(x) || !aligned16(y)) return fail(W4A16_ERR_UNSUPPORTED, "x and y must be 16-byte aligned");
+    if (overlaps(y, (size_t)M * width * 2, x, (size_t)((M - 1) * ldx + width) * 2))
+        return fail(W4A16_ERR_INVALID_ARG, "y overlaps x");
+    hipError_t e = launch_rownorm(x, M, ldx, width, y, stream);
+    if (e != hipSuccess) return fail(W4A16_ERR_HIP, std::string("row-norm launch: ") + hipGetErrorString(e));
     return ok();
 }
 
@@ -655,16 +711,21 @@ int w4a16_set_tuning(const char *spec) {
 int w4a16_release(void) {
     std::lock_guard<std::mutex> lock(g_mu);
     int rc = W4A16_OK;
+    int cur = 0;
+    (void)hipGetDevice(&cur);
     for (auto &kv : g_scratch) {
-        int cur = 0;
-        (void)hipGetDevice(&cur);
         if (hipSetDevice(kv.first.first) != hipSuccess) rc = W4A16_ERR_HIP;
         if (hipStreamSynchronize(kv.first.second) != hipSuccess) rc = W4A16_ERR_HIP;
         if (kv.second.partials) (void)hipFree(kv.second.partials);
         if (kv.second.counters) (void)hipFree(kv.second.counters);
-        (void)hipSetDevice(cur);
     }
+    for (auto &r : g_retired) {
+        if (hipSetDevice(r.first) != hipSuccess) rc = W4A16_ERR_HIP;
+        (void)hipFree(r.second);  // hipFree waits for work on the device that may use it
+    }
+    (void)hipSetDevice(cur);
     g_scratch.clear();
+    g_retired.clear();
     if (rc != W4A16_OK) return fail(rc, "synchronising a stream during release failed");
     return ok();
 }

@@ -235,27 +235,39 @@ __device__ __forceinline__ float load_partial(const float *p) {
 }
 // Split-K reduction in exact fixed point, so the result does not depend on the
 // order in which splits arrive.  Each output owns one zero-initialised 64-bit
-// slot:
-//   bits 58..63  arrivals
-//   bits 52..57  non-finite partials
-//   bits  0..51  sum over the finite partials p of round(p * 2^26) + 2^46
-// A split adds its partial (saturated to |p| <= 2^20 - 1) with one atomic.
+// slot, and each split adds its fp32 partial p with one atomic:
+//   bits 60..63  arrivals
+//   bits 55..59  "positive beyond range" partials: +inf, or finite p >= 2^17
+//   bits 50..54  "negative beyond range" partials: -inf, or finite p <= -2^17
+//                (a NaN partial counts in both fields)
+//   bits  0..49  splits * 2^45 + the sum over the other partials of
+//                round(p * 2^28)
 // The arrival that brings the count to `splits` holds the total (the value it
 // got back plus its own addition), writes the output and zeroes the slot for
-// the next call.  At most 32 splits, so no field carries into the next.
-constexpr int kFixFracBits = 26;
-constexpr int kSlotPoisonShift = 52;
-constexpr int kSlotCountShift = 58;
-constexpr int64_t kFixBias = 1ll << 46;
-constexpr float kFixMax = 1048575.0f;  // 2^20 - 1
+// the next call.  At most kGemvMaxSplits (16) splits, so no field carries into
+// the next.  Every partial with |p| < 2^17 (twice the fp16 range) enters the
+// sum exactly up to its 2^-28 rounding; beyond that the result is exact or
+// loud: an infinite partial gives that infinity (NaN with both signs, as fp32
+// addition does), and a finite partial past 2^17 gives the infinity of its
+// sign when the rest cannot pull the sum back inside fp16 range (the other
+// partials sum to less than 2^16 against it), NaN otherwise.
+constexpr int kFixFracBits = 28;
+constexpr int kSlotNegShift = 50;
+constexpr int kSlotPosShift = 55;
+constexpr int kSlotCountShift = 60;
+constexpr int64_t kFixBias = 1ll << 45;
+constexpr float kFixMax = 131072.0f;  // 2^17
 
 __device__ __forceinline__ uint64_t slot_contribution(float p) {
-    uint64_t add = 1ull << kSlotCountShift;
-    if (__builtin_isfinite(p)) {
-        const float c = fminf(fmaxf(p, -kFixMax), kFixMax);
-        add += (uint64_t)((int64_t)rintf(c * (float)(1 << kFixFracBits)) + kFixBias);
+    // every split adds the bias once, so the sum field holds splits * bias
+    // plus the fixed-point partials of the splits in range
+    uint64_t add = (1ull << kSlotCountShift) + (uint64_t)kFixBias;
+    if (__builtin_fabsf(p) < kFixMax) {
+        add += (uint64_t)(int64_t)rintf(p * (float)(1 << kFixFracBits));
     } else {
-        add += 1ull << kSlotPoisonShift;
+        // +-inf, a finite partial beyond 2^17, or NaN (both fields)
+        if (!(p < 0.f)) add += 1ull << kSlotPosShift;
+        if (!(p > 0.f)) add += 1ull << kSlotNegShift;
     }
     return add;
 }
@@ -265,11 +277,16 @@ __device__ __forceinline__ uint64_t slot_add(uint64_t *slot, uint64_t v) {
 __device__ __forceinline__ bool slot_last(uint64_t old, int splits) {
     return (old >> kSlotCountShift) == (uint64_t)(splits - 1);
 }
-// fp16 output for a slot's final value (NaN if any partial was not finite).
+// fp16 output for a slot's final value.
 __device__ __forceinline__ uint16_t slot_result_f16(uint64_t total, int splits) {
-    if ((total >> kSlotPoisonShift) & 63u) return 0x7e00u;
-    const int64_t s = (int64_t)(total & ((1ull << kSlotPoisonShift) - 1)) - (int64_t)splits * kFixBias;
-    return f32_to_f16_bits((float)((double)s * (1.0 / (double)(1 << kFixFracBits))));
+    const uint32_t pos = (uint32_t)(total >> kSlotPosShift) & 31u;
+    const uint32_t neg = (uint32_t)(total >> kSlotNegShift) & 31u;
+    const int64_t s = (int64_t)(total & ((1ull << kSlotNegShift) - 1)) - (int64_t)splits * kFixBias;
+    constexpr int64_t kRange = 1ll << (16 + kFixFracBits);  // 2^16 in fixed point
+    if (pos && neg) return 0x7e00u;
+    if (pos) return s > -kRange ? 0x7c00u : 0x7e00u;
+    if (neg) return s < kRange ? 0xfc00u : 0x7e00u;
+    return f32_to_f16_bits((float)((double)s * (1.0 / (double)(1ll << kFixFracBits))));
 }
 __device__ __forceinline__ void slot_reset(uint64_t *slot) {
     __hip_atomic_store(slot, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -11,15 +11,19 @@
 // MFMA column tile: tile t's column j is matrix column 8*(word0 + j) + t.  The
 // dequantised weights therefore never leave registers -- no LDS round trip and
 // no transpose -- and lane j of every tile owns 8 adjacent output columns, so
-// the epilogue stores 16 contiguous bytes per row.  Dequantisation is
-// (q - z) exact in fp16 (device.h), times the group scale rounded to fp16.
+// the epilogue stores 16 contiguous bytes per row.  The operands are the exact
+// integers (q - z) in fp16 (device.h); the group scale multiplies the fp32
+// sums of each group (group accumulators flushed into running totals when a
+// group ends), so no weight is rounded: the same per-group factorisation
+// out = sum_g s_g (sum_k a_k (q_k - z_g)) the definition allows, with fp32
+// rounding only in the sums.
 //
 // Pipeline.  A wave computes (16*MT rows) x (128 columns) over a contiguous
-// block of 32-row K-steps.  The loop is unrolled by four over a ring of four
+// block of 32-row K-steps.  The loop is unrolled by two over a ring of two
 // packed-word slots and two A-operand slots, so nothing is copied between
 // iterations: the MFMAs of step s run while the VALU dequantises step s+1
 // into the B operand registers the MFMAs have just read (explicit scheduling
-// regions keep that order), A for step s+1 and B for step s+4 are in flight.
+// regions keep that order), A for step s+1 and B for step s+2 are in flight.
 // Loads are issued in the order they are consumed, so waiting for the data of
 // one step never waits for a later prefetch.  All loads are buffer loads whose
 // per-row/per-step offset is an SGPR: no vector address arithmetic.
@@ -49,7 +53,7 @@ struct Cfg {
     static constexpr int kTileCols = 128 * NWN;
     // f32x4 units of the workgroup tile per thread in the split-K reduction.
     static constexpr int kUnits = kTileRows * (kTileCols / 4) / kThreads;
-    static constexpr int kMaxSplits = MT >= 4 ? 4 : 8;  // in-flight loads of the last workgroup
+    static constexpr int kMaxSplits = 8;  // in-flight loads of the last workgroup
     static constexpr int kChunk = kSplitLoads / kMaxSplits < kUnits ? kSplitLoads / kMaxSplits : kUnits;
     static_assert(kUnits >= 1 && kTileRows * (kTileCols / 4) % kThreads == 0, "whole units per thread");
     static_assert(kChunk >= 1 && kUnits % kChunk == 0, "whole chunks");
@@ -90,21 +94,12 @@ template <int A>
 struct Gcd<A, 0> : std::integral_constant<int, A> {};
 
 // Pipeline depths: steps of B (packed words, scales, zeros) and of A in
-// flight.  (A third A slot measured no faster at MT = 4.)
-// Two B slots where eight waves of 64-row tiles share a CU (256 VGPRs each).
+// flight.  Two B slots: with each group's sums and the scaled totals (128
+// accumulator registers at 32-row wave tiles), a third or fourth slot spills.
 template <int MT, int NWK>
-struct RingW : std::integral_constant<int, (MT == 4 && NWK >= 4) ? 2 : 4> {};
+struct RingW : std::integral_constant<int, 2> {};
 template <int MT>
 struct RingA : std::integral_constant<int, 2> {};
-
-// Scale pairs (s_t, s_t) for the 8 columns of one word from their fp16 bits.
-__device__ __forceinline__ void scale_pairs(const u32x4 &sv, f16x2 (&sp)[8]) {
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-        sp[2 * x] = as_f16x2(__builtin_amdgcn_perm(sv[x], sv[x], 0x01000100u));
-        sp[2 * x + 1] = as_f16x2(__builtin_amdgcn_perm(sv[x], sv[x], 0x03020302u));
-    }
-}
 
 template <bool ASYM>
 __device__ __forceinline__ void zero_pairs(uint32_t zw, uint32_t zp, const NibbleConsts &nk, f16x2 (&zc)[8]) {
@@ -130,16 +125,16 @@ __device__ __forceinline__ void zero_pairs(uint32_t zw, uint32_t zp, const Nibbl
 }
 
 // Dequantise byte position B (nibbles 2B, 2B+1) of the 8 words of rows
-// k0+8*kq .. +7 of one packed column-of-words into B operands 2B and 2B+1.
+// k0+8*kq .. +7 of one packed column-of-words into B operands 2B and 2B+1:
+// the exact integers q - z in fp16.
 template <int B>
 __device__ __forceinline__ void dequant_byte(const uint32_t (&wd)[8], const f16x2 (&zc)[8],
-                                             const f16x2 (&sp)[8], const NibbleConsts &nk,
-                                             f16x8 (&bop)[8]) {
+                                             const NibbleConsts &nk, f16x8 (&bop)[8]) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const uint32_t pr = gather_byte_pair<B>(wd[2 * j], wd[2 * j + 1]);
-        const f16x2 v0 = (as_f16x2(biased_pair<0>(pr, nk)) - zc[2 * B]) * sp[2 * B];
-        const f16x2 v1 = (as_f16x2(biased_pair<1>(pr, nk)) - zc[2 * B + 1]) * sp[2 * B + 1];
+        const f16x2 v0 = as_f16x2(biased_pair<0>(pr, nk)) - zc[2 * B];
+        const f16x2 v1 = as_f16x2(biased_pair<1>(pr, nk)) - zc[2 * B + 1];
         bop[2 * B][2 * j] = v0.x;
         bop[2 * B][2 * j + 1] = v0.y;
         bop[2 * B + 1][2 * j] = v1.x;
@@ -218,14 +213,28 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
     // Accumulators start from distinct (opaque) zeros: with one shared zero
     // constant the register allocator gave MFMA results and their srcC
     // different registers and copied the accumulators every step.
-    f32x4 acc[MT][8];
+    // acc: the current group's sums; tot: the scaled totals of the groups
+    // before it.
+    static_assert(MT <= 2, "group sums and totals of 64-row wave tiles do not fit the registers");
+    f32x4 acc[MT][8], tot[MT][8];
+    auto zero_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                asm volatile("" : "+v"(z));
+                acc[mt][t] = z;
+            }
+    };
+    zero_acc();
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             f32x4 z = {0.f, 0.f, 0.f, 0.f};
             asm volatile("" : "+v"(z));
-            acc[mt][t] = z;
+            tot[mt][t] = z;
         }
 
     // This K-wave's contiguous block of 32-row steps (groups change rarely).
@@ -270,10 +279,8 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
     using I4 = std::integral_constant<int, 4>;
     using I6 = std::integral_constant<int, 6>;
 
-    // Ring of four packed-word / scale / zero slots (B data for steps s..s+3)
-    // and two A-operand slots; one set of B operands `bop`.
-    // B ring depth (steps of B prefetch): 4, or 2 where 128 accumulator
-    // registers per wave leave no room for more.
+    // Ring of packed-word / scale / zero slots (B data for steps s, s+1) and
+    // two A-operand slots; one set of B operands `bop`.
     constexpr int kRing = RingW<MT, NWK>::value;  // B / scale / zero slots
     constexpr int kRingA = RingA<MT>::value;  // A slots
     constexpr int kUnroll = kRing * kRingA / Gcd<kRing, kRingA>::value;
@@ -281,23 +288,37 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
     u32x4 sv[kRing];
     uint32_t zw[kRing] = {};
     f16x8 av[kRingA][MT], bop[8];
-    f16x2 sp[8], zc[8];
+    f16x2 zc[8];
+    // End of a group: totals += group scale * group sums (tile t of the lane
+    // is column 8 * word + t, scale element t of the word's scale vector).
+    auto flush = [&](const u32x4 &scl) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float st = f16_bits_to_f32((scl[t >> 1] >> (16 * (t & 1))) & 0xffffu);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) tot[mt][t][v] = __builtin_fmaf(st, acc[mt][t][v], tot[mt][t][v]);
+        }
+        zero_acc();
+    };
 
     // One K-step s held in ring slot U (A slot U & 1).  Four scheduling
     // regions, each issuing the MFMAs of one B operand pair of step s next to
     // the VALU work that rewrites the pair the previous region consumed:
-    //   1: MFMA pair 0,1 | dequantise pair 6,7 of step s; scale/zero of s+1
+    //   1: MFMA pair 0,1 | dequantise pair 6,7 of step s; zeros of s+1
     //   2: MFMA pair 2,3 | dequantise pair 0,1 of step s+1
     //   3: MFMA pair 4,5 | dequantise pair 2,3 of step s+1
     //   4: MFMA pair 6,7 | dequantise pair 4,5 of step s+1
-    // A for s+1 is requested at the top, B/scale/zero for s+4 after region 1
-    // frees slot U.  Steps past the block clamp their loads (data unused).
-    // Inside a region, alternate one MFMA with a share of the region's VALU
-    // work (28 conversion ops per operand pair; the first region also builds
-    // the next step's scale and zero pairs), so that the matrix core and the
-    // VALU stay busy together; left alone the scheduler clusters them.
-    constexpr int kValuPair = (28 + 2 * MT - 1) / (2 * MT);
-    constexpr int kValuFirst = (28 + 8 + (ASYM ? 16 : 0) + (RN ? 8 * MT : 0) + 2 * MT - 1) / (2 * MT);
+    // then, when step s ends a group, the group flush.  A for s+1 is
+    // requested at the top, B/scale/zero for s+2 after region 1 frees slot U.
+    // Steps past the block clamp their loads (data unused).  Inside a region,
+    // alternate one MFMA with a share of the region's VALU work (20
+    // conversion ops per operand pair; the first region also builds the next
+    // step's zero pairs), so that the matrix core and the VALU stay busy
+    // together; left alone the scheduler clusters them.
+    constexpr int kValuPair = (20 + 2 * MT - 1) / (2 * MT);
+    constexpr int kValuFirst = (20 + (ASYM ? 16 : 0) + (RN ? 8 * MT : 0) + 2 * MT - 1) / (2 * MT);
     float sq[MT];  // RN: this lane's sum of squares of its A values (row m0 + 16 mt + j16)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) sq[mt] = 0.f;
@@ -305,7 +326,8 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
         constexpr int U = decltype(uc)::value;
         constexpr int AC = U % kRingA, AN = (U + kRingA - 1) % kRingA, WC = U % kRing, WN = (U + 1) % kRing;
         load_a(stc(s + kRingA - 1), av[AN]);
-        f16x2 spn[8], zcn[8];
+        const u32x4 scl = sv[WC];  // this step's group scales (the slot is refilled below)
+        f16x2 zcn[8];
         mfma_pair(av[AC], bop, I0{});
         if constexpr (RN) {
 #pragma unroll
@@ -313,36 +335,34 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
 #pragma unroll
                 for (int e = 0; e < 8; ++e) sq[mt] = __builtin_fmaf((float)av[AC][mt][e], (float)av[AC][mt][e], sq[mt]);
         }
-        dequant_byte<3>(w[WC], zc, sp, nk, bop);
-        scale_pairs(sv[WN], spn);
+        dequant_byte<3>(w[WC], zc, nk, bop);
         zero_pairs<ASYM>(zw[WN], zp, nk, zcn);
         interleave<2 * MT, kValuFirst>();
         pin(bop[6], bop[7]);
 #pragma unroll
-        for (int x = 0; x < 8; x += 2) pin2(spn[x], spn[x + 1], zcn[x], zcn[x + 1]);
+        for (int x = 0; x < 8; x += 4) pin2(zcn[x], zcn[x + 1], zcn[x + 2], zcn[x + 3]);
         __builtin_amdgcn_sched_barrier(0);
         load_b(stc(s + kRing), w[WC]);
         load_sz(stc(s + kRing), sv[WC], zw[WC]);
         mfma_pair(av[AC], bop, I2{});
-        dequant_byte<0>(w[WN], zcn, spn, nk, bop);
+        dequant_byte<0>(w[WN], zcn, nk, bop);
         interleave<2 * MT, kValuPair>();
         pin(bop[0], bop[1]);
         __builtin_amdgcn_sched_barrier(0);
         mfma_pair(av[AC], bop, I4{});
-        dequant_byte<1>(w[WN], zcn, spn, nk, bop);
+        dequant_byte<1>(w[WN], zcn, nk, bop);
         interleave<2 * MT, kValuPair>();
         pin(bop[2], bop[3]);
         __builtin_amdgcn_sched_barrier(0);
         mfma_pair(av[AC], bop, I6{});
-        dequant_byte<2>(w[WN], zcn, spn, nk, bop);
+        dequant_byte<2>(w[WN], zcn, nk, bop);
         interleave<2 * MT, kValuPair>();
         pin(bop[4], bop[5]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-            sp[x] = spn[x];
-            zc[x] = zcn[x];
-        }
+        for (int x = 0; x < 8; ++x) zc[x] = zcn[x];
+        // the group of step s ends here (G is a multiple of 32), or the block does
+        if (s + 1 == n || ((w_begin + s + 1) * 32) % G == 0) flush(scl);
     };
 
     if (n > 0) {
@@ -356,11 +376,10 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
             load_b(stc(r), w[r]);
             load_sz(stc(r), sv[r], zw[r]);
         }
-        scale_pairs(sv[0], sp);
         zero_pairs<ASYM>(zw[0], zp, nk, zc);
-        dequant_byte<0>(w[0], zc, sp, nk, bop);
-        dequant_byte<1>(w[0], zc, sp, nk, bop);
-        dequant_byte<2>(w[0], zc, sp, nk, bop);
+        dequant_byte<0>(w[0], zc, nk, bop);
+        dequant_byte<1>(w[0], zc, nk, bop);
+        dequant_byte<2>(w[0], zc, nk, bop);
         int i = 0;
         for (; i + kUnroll <= n; i += kUnroll)
             static_for<0, kUnroll>([&](auto uc) __attribute__((always_inline)) { step(i + decltype(uc)::value, uc); });
@@ -371,7 +390,7 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
 
     // K-wave reduction and tile store.  A "row slot" (mt, v) is the row
     // m0 + 16*mt + 4*kq + v of every lane, 8 columns 8*word + 0..7 per lane:
-    // acc[mt][0..7][v].  Every wave writes its slots to LDS at once (in rounds
+    // tot[mt][0..7][v].  Every wave writes its slots to LDS at once (in rounds
     // of MTC row tiles, so the buffer stays within LDS); after one barrier,
     // each K-wave of an N-wave group sums its share of the slots over the
     // group's NWK waves in order wk = 0, 1, ... (deterministic) and stores
@@ -400,10 +419,10 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
         }
     };
     auto slot_lo = [&](int mt, int v) __attribute__((always_inline)) {
-        return f32x4{acc[mt][0][v], acc[mt][1][v], acc[mt][2][v], acc[mt][3][v]};
+        return f32x4{tot[mt][0][v], tot[mt][1][v], tot[mt][2][v], tot[mt][3][v]};
     };
     auto slot_hi = [&](int mt, int v) __attribute__((always_inline)) {
-        return f32x4{acc[mt][4][v], acc[mt][5][v], acc[mt][6][v], acc[mt][7][v]};
+        return f32x4{tot[mt][4][v], tot[mt][5][v], tot[mt][6][v], tot[mt][7][v]};
     };
     if constexpr (NWK == 1) {
 #pragma unroll
@@ -559,10 +578,7 @@ hipError_t launch_cfg(const GemmArgs &g, const GemmPlan &p, bool rn, const uint1
 int mfma_max_splits(int mt, int waves, int kwaves) {
     if (mt == 1 && waves == 2 && kwaves == 4) return Cfg<1, 2, 4>::kMaxSplits;
     if (mt == 2 && waves == 2 && kwaves == 4) return Cfg<2, 2, 4>::kMaxSplits;
-    if (mt == 4 && waves == 2 && kwaves == 2) return Cfg<4, 2, 2>::kMaxSplits;
     if (mt == 2 && waves == 1 && kwaves == 8) return Cfg<2, 1, 8>::kMaxSplits;
-    if (mt == 4 && waves == 2 && kwaves == 4) return Cfg<4, 2, 4>::kMaxSplits;
-    if (mt == 4 && waves == 1 && kwaves == 8) return Cfg<4, 1, 8>::kMaxSplits;
     return 1;
 }
 
@@ -571,10 +587,7 @@ hipError_t launch_mfma_rn(const GemmArgs &g, const GemmPlan &p, bool rn, const u
     // (MT, NWN, NWK) combinations the planner emits.
     if (p.mt == 1 && p.waves == 2 && p.kwaves == 4) return launch_cfg<1, 2, 4>(g, p, rn, a, lda, stream);
     if (p.mt == 2 && p.waves == 2 && p.kwaves == 4) return launch_cfg<2, 2, 4>(g, p, rn, a, lda, stream);
-    if (p.mt == 4 && p.waves == 2 && p.kwaves == 2) return launch_cfg<4, 2, 2>(g, p, rn, a, lda, stream);
     if (p.mt == 2 && p.waves == 1 && p.kwaves == 8) return launch_cfg<2, 1, 8>(g, p, rn, a, lda, stream);
-    if (p.mt == 4 && p.waves == 2 && p.kwaves == 4) return launch_cfg<4, 2, 4>(g, p, rn, a, lda, stream);
-    if (p.mt == 4 && p.waves == 1 && p.kwaves == 8) return launch_cfg<4, 1, 8>(g, p, rn, a, lda, stream);
     return hipErrorInvalidValue;
 }
 

@@ -33,13 +33,14 @@
 #include "device.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace w4a16 {
 namespace {
 
 constexpr int kTileWords = 32;  // 256 columns per workgroup tile
 constexpr int kTileCols = 256;
 constexpr int kChunkRows = 16;  // rows per lane chunk = 8 row pairs
-constexpr int kMaxSplits = 32;  // bound of the planner's K-split count
 
 template <int W>
 struct Words {
@@ -607,24 +608,43 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
 //    occupies A rows 2 mu and 2 mu + 1, which hold the row's activations in
 //    the even and in the odd k-slots only, so D row 2 mu + e collects column
 //    c + 4e.  Up to 8 activation rows fill the 16 A rows.
-//  * Zero point folded per chunk.  A ninth MFMA per set multiplies the same A
-//    by ones, giving sum(a) in the layout of the products; the chunk's
-//    (q - z) sums are D - (bias + z) * sum(a), scaled by the group scale into
-//    an fp32 total (the per-group factorisation out = sum_g s (sum a q' -
-//    z' sum a)).  The bias costs about 10 bits of the fp32 sums of one chunk,
-//    leaving an error like the dot2 form's.
+//  * Zero point.  Symmetric: folded per chunk.  The zero term
+//    sum(a) * (bias + zp) runs the same MFMA chain as the products, on two B
+//    operands that hold (bias + zp) in every k-slot (bias 1024 and 64); the
+//    chunk's (q - z) sums are D minus that term, scaled by the group scale
+//    into an fp32 total (the per-group factorisation out = sum_g s (sum a q'
+//    - z' sum a)).  A column whose nibbles all equal zp gets the same MFMA
+//    inputs twice, so it cancels to exactly 0.  The bias costs about 10 bits
+//    of the fp32 sums of one chunk, leaving an error like the dot2 form's.
+//    Packed zeros (and, on request, a symmetric zero point: the exact form):
+//    the zero word is unpacked like a weight word and one packed subtraction
+//    per register leaves the exact (q - z) before the MFMA (zeros vary by
+//    column, so a folded term would take one MFMA per word and nibble pair).
+//    Packed zeros that all equal zp give bit for bit the exact form's
+//    symmetric result: the same exact products in the same order.
+//  * Non-finite activations.  The biased sums would turn an infinite
+//    activation into inf - inf; when the zero term of a chunk is not finite
+//    (exactly when one of its activations is not), the wave recomputes all
+//    its chunks after the loop in the exact form, so infinities keep their
+//    sign and a zero weight times an infinity gives NaN, as in the
+//    definition.
 //
 // Lane (j, g) = (lane % 16, lane / 16) loads words 2j, 2j+1 of the tile (8
 // bytes of each row) for rows 16 s + 4 g + i (i < 4) of set s, and the
 // activations of row mu = j / 2 at those rows.  A wave takes chunks of CH rows
 // (CH divides G, so a chunk lies in one group) and issues all of a chunk's
 // loads before its first wait.
-template <int M, bool ASYM, int ACT, int RV, int WL = 2>
+// Zero-point forms of the matrix-core GEMV (template argument ZM).
+enum ZeroMode { kZeroFolded = 0, kZeroPacked = 1, kZeroExact = 2 };
+
+template <int M, int ZM, int ACT, int RV, int WL = 2>
 __global__ __launch_bounds__(512) void gemv_mma_kernel(
     const uint16_t *__restrict__ a, const uint16_t *__restrict__ src, int ld, const uint32_t *__restrict__ b,
     const uint16_t *__restrict__ scales, const uint32_t *__restrict__ qzeros, int K, int N, int G, uint32_t zp,
     int tiles, int split_len, int splits, uint16_t *__restrict__ out, uint32_t *__restrict__ counters) {
     static_assert(M >= 1 && M <= 8, "two A rows per activation row");
+    constexpr bool ASYM = ZM == kZeroPacked;  // packed zero points
+    constexpr bool kExact = ZM != kZeroFolded;  // B holds exact (q - z)
     constexpr int NW = 8;
     constexpr int CH = kMmaChunkRows;
     constexpr int SETS = CH / 16;
@@ -664,6 +684,11 @@ __global__ __launch_bounds__(512) void gemv_mma_kernel(
     uint32_t sel0 = (j & 1) ? 0x01000c0cu : 0x0c0c0100u;
     uint32_t sel1 = (j & 1) ? 0x03020c0cu : 0x0c0c0302u;
     if (mu >= M) sel0 = sel1 = 0x0c0c0c0cu;
+    // Symmetric zero term: B operands holding (1024 + zp) and (64 + zp) in
+    // every k-slot (the biased weights' values where q == zp).
+    const uint32_t zb0 = kMagicLo | zp | (zp << 16), zb1 = kMagicHi | (zp << 4) | (zp << 20);
+    const f16x8 zb_lo = __builtin_bit_cast(f16x8, u32x4{zb0, zb0, zb0, zb0});
+    const f16x8 zb_hi = __builtin_bit_cast(f16x8, u32x4{zb1, zb1, zb1, zb1});
 
     f32x4 tot[WL][4];
 #pragma unroll
@@ -730,18 +755,30 @@ __global__ __launch_bounds__(512) void gemv_mma_kernel(
         // variants, one memory round trip per chunk
         __builtin_amdgcn_sched_barrier(0);
     };
-    // Products of one chunk into acc (per word x and nibble pair q) and the
-    // activation sums into asum.
-    f32x4 acc[WL][4], asum;
+    // Products of one chunk into acc (per word x and nibble pair q) and, with a
+    // symmetric zero point, the zero term into cz (one accumulator per bias).
+    f32x4 acc[WL][4], cz[2];
     auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int x = 0; x < WL; ++x)
 #pragma unroll
             for (int q = 0; q < 4; ++q) acc[x][q] = f32x4{0.f, 0.f, 0.f, 0.f};
-        asum = f32x4{0.f, 0.f, 0.f, 0.f};
+        cz[0] = cz[1] = f32x4{0.f, 0.f, 0.f, 0.f};
     };
-    auto mma_chunk = [&](const Chunk &d) __attribute__((always_inline)) {
-        const f16x8 unit = __builtin_bit_cast(f16x8, u32x4{0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u});
+    // (bias + z) pairs of word x, nibble pair q (the weights' own unpacking
+    // applied to the zero word; symmetric: the same for every word).
+    auto zero_pair_q = [&](const Chunk &d, int x, int q) __attribute__((always_inline)) {
+        if constexpr (ASYM) {
+            const uint32_t zw = q >= 2 ? d.zw[x] >> 8 : d.zw[x];
+            return (q & 1) ? ((zw & nk.mask_hi) | nk.bias_hi) : ((zw & nk.mask_lo) | nk.bias_lo);
+        } else {
+            return (q & 1) ? (kMagicHi | (zp << 4) | (zp << 20)) : (kMagicLo | zp | (zp << 16));
+        }
+    };
+    // EXACT: B holds (q - z) (packed zeros, and the rare non-finite redo);
+    // otherwise bias + q and the zero term in cz.
+    auto mma_chunk = [&](const Chunk &d, auto exact_c) __attribute__((always_inline)) {
+        constexpr bool EXACT = decltype(exact_c)::value;
 #pragma unroll
         for (int s = 0; s < SETS; ++s) {
             uint32_t lo = d.av[s].x, hi = d.av[s].y;
@@ -770,30 +807,52 @@ __global__ __launch_bounds__(512) void gemv_mma_kernel(
                     p[2][i] = (sh & nk.mask_lo) | nk.bias_lo;
                     p[3][i] = (sh & nk.mask_hi) | nk.bias_hi;
                 }
+                if constexpr (EXACT) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f16x2 zq = as_f16x2(zero_pair_q(d, x, q));
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) p[q][i] = as_u32(as_f16x2(p[q][i]) - zq);
+                    }
+                }
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     acc[x][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                         av, __builtin_bit_cast(f16x8, u32x4{p[q][0], p[q][1], p[q][2], p[q][3]}), acc[x][q], 0, 0, 0);
             }
-            asum = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, unit, asum, 0, 0, 0);
+            if constexpr (!EXACT) {
+                cz[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, zb_lo, cz[0], 0, 0, 0);
+                cz[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, zb_hi, cz[1], 0, 0, 0);
+            }
+        }
+    };
+    // Products of one chunk (packed zeros: the exact form).  With a
+    // symmetric zero point `nonfinite` records a zero term that is not finite
+    // (the wave then redoes its chunks in the exact form after the loop, where
+    // the loop's registers are free).
+    bool nonfinite = false;
+    auto chunk = [&](const Chunk &d) __attribute__((always_inline)) {
+        zero_acc();
+        mma_chunk(d, std::integral_constant<bool, kExact>{});
+        if constexpr (!kExact) {
+#pragma unroll
+            for (int v = 0; v < DV; ++v) nonfinite |= !__builtin_isfinite(cz[0][v]);
         }
     };
     // End of a group: (q - z) sums times the group scale into tot.  acc[x][q]
     // element v is D row 4 g + v = (row 2 g + v / 2, half e = v & 1), column
     // 8 (word + x) + q + 4 e of the lane's words.
-    auto flush = [&](const u32x4 (&sv)[WL], const uint32_t (&zw)[WL]) __attribute__((always_inline)) {
+    auto flush = [&](const u32x4 (&sv)[WL]) __attribute__((always_inline)) {
 #pragma unroll
         for (int x = 0; x < WL; ++x) {
-            const uint32_t zword = zw[x];
 #pragma unroll
             for (int q = 0; q < 4; ++q)
 #pragma unroll
                 for (int v = 0; v < DV; ++v) {
                     const int c = q + 4 * (v & 1);  // column within the word
                     const float s = f16_bits_to_f32((sv[x][c >> 1] >> (16 * (c & 1))) & 0xffffu);
-                    const uint32_t z = ASYM ? (zword >> (4 * c)) & 0xfu : zp;
-                    const float zs = (float)((q & 1) ? 64u + z : 1024u + z);
-                    tot[x][q][v] = __builtin_fmaf(s, __builtin_fmaf(-zs, asum[v], acc[x][q][v]), tot[x][q][v]);
+                    const float d = kExact ? acc[x][q][v] : acc[x][q][v] - cz[q & 1][v];
+                    tot[x][q][v] = __builtin_fmaf(s, d, tot[x][q][v]);
                 }
         }
     };
@@ -811,9 +870,8 @@ __global__ __launch_bounds__(512) void gemv_mma_kernel(
             Chunk d;
             load_chunk(c0, d);
             rows.partials(src, ld, K);
-            zero_acc();
-            mma_chunk(d);
-            flush(d.sv, d.zw);
+            chunk(d);
+            flush(d.sv);
         } else {
             rows.partials(src, ld, K);
         }
@@ -823,9 +881,8 @@ __global__ __launch_bounds__(512) void gemv_mma_kernel(
             Chunk d;
             load_chunk(c, d);
             rows.reduce(s_part, lane, wave);
-            zero_acc();
-            mma_chunk(d);
-            flush(d.sv, d.zw);
+            chunk(d);
+            flush(d.sv);
             c += NW;
         } else {
             rows.reduce(s_part, lane, wave);
@@ -834,9 +891,23 @@ __global__ __launch_bounds__(512) void gemv_mma_kernel(
     for (; c < c_end; c += NW) {
         Chunk d;
         load_chunk(c, d);
-        zero_acc();
-        mma_chunk(d);
-        flush(d.sv, d.zw);
+        chunk(d);
+        flush(d.sv);
+    }
+    // Rare: some activation of the wave's chunks was not finite.  Redo them
+    // all with exact (q - z) weights (wave-uniform branch).
+    if (!kExact && __builtin_amdgcn_ballot_w64(nonfinite) != 0) {
+#pragma unroll
+        for (int x = 0; x < WL; ++x)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) tot[x][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ce = c0; ce < c_end; ce += NW) {
+            Chunk d;
+            load_chunk(ce, d);
+            zero_acc();
+            mma_chunk(d, std::true_type{});
+            flush(d.sv);
+        }
     }
     if constexpr (ACT != 0 && !kEarlyRows) {
         rows.partials(src, ld, K);
@@ -909,29 +980,32 @@ hipError_t launch_m(const GemmArgs &g, const GemmPlan &p, int act, const uint16_
     return p.waves == 8 ? launch_v<M, WORDS, 8>(g, p, stream) : launch_v<M, WORDS, 4>(g, p, stream);
 }
 
-template <int M, bool ASYM, int ACT, int RV>
+template <int M, int ZM, int ACT, int RV>
 hipError_t launch_mma_k(const GemmArgs &g, const GemmPlan &p, const uint16_t *src, int ld, hipStream_t stream) {
     if constexpr (M <= 2 && ACT <= 1) {
         // 512-column tiles (4 words per lane), planned at M <= 2 where they fill more of the chip
         if (p.words == 4) {
-            hipLaunchKernelGGL((gemv_mma_kernel<M, ASYM, ACT, RV, 4>), dim3((unsigned)p.grid), dim3(512), 0, stream,
+            hipLaunchKernelGGL((gemv_mma_kernel<M, ZM, ACT, RV, 4>), dim3((unsigned)p.grid), dim3(512), 0, stream,
                                g.a, src, ld, reinterpret_cast<const uint32_t *>(g.b), g.scales,
                                reinterpret_cast<const uint32_t *>(g.qzeros), (int)g.K, (int)g.N, (int)g.G,
                                (uint32_t)g.zp, (int)p.tiles_n, (int)p.split_len, p.splits, g.out, g.counters);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((gemv_mma_kernel<M, ASYM, ACT, RV>), dim3((unsigned)p.grid), dim3(512), 0, stream, g.a, src,
+    hipLaunchKernelGGL((gemv_mma_kernel<M, ZM, ACT, RV>), dim3((unsigned)p.grid), dim3(512), 0, stream, g.a, src,
                        ld, reinterpret_cast<const uint32_t *>(g.b), g.scales,
                        reinterpret_cast<const uint32_t *>(g.qzeros), (int)g.K, (int)g.N, (int)g.G, (uint32_t)g.zp,
                        (int)p.tiles_n, (int)p.split_len, p.splits, g.out, g.counters);
     return hipGetLastError();
 }
 
+// Packed zeros: the exact form; symmetric zero point: folded (default) or,
+// with plan.exact, the exact form.
 template <int M, int ACT, int RV>
 hipError_t launch_mma_z(const GemmArgs &g, const GemmPlan &p, const uint16_t *src, int ld, hipStream_t stream) {
-    return g.qzeros ? launch_mma_k<M, true, ACT, RV>(g, p, src, ld, stream)
-                    : launch_mma_k<M, false, ACT, RV>(g, p, src, ld, stream);
+    if (g.qzeros) return launch_mma_k<M, kZeroPacked, ACT, RV>(g, p, src, ld, stream);
+    return p.exact ? launch_mma_k<M, kZeroExact, ACT, RV>(g, p, src, ld, stream)
+                   : launch_mma_k<M, kZeroFolded, ACT, RV>(g, p, src, ld, stream);
 }
 
 // Glue-fused variants: at M <= 2 the row's vectors are held in registers
@@ -959,7 +1033,7 @@ hipError_t launch_gemv(const GemmArgs &g, const GemmPlan &p, hipStream_t stream)
 
 hipError_t launch_gemv_act(const GemmArgs &g, const GemmPlan &p, int act, const uint16_t *src, int64_t ld,
                            hipStream_t stream) {
-    if (p.splits > kMaxSplits) return hipErrorInvalidValue;
+    if (p.splits > kGemvMaxSplits) return hipErrorInvalidValue;
     if (act != 0 && (p.waves != 8 || !src || ld % 8 != 0 || g.K % 8 != 0 || g.K > kGlueMaxWidth))
         return hipErrorInvalidValue;
     if (p.mma) {

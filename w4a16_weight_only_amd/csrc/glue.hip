@@ -79,13 +79,13 @@ __global__ __launch_bounds__(kThreads) void rownorm_kernel(const uint16_t *__res
     }
 }
 
-// y[m][i] = rn_row(silu(gu[m][i]) * gu[m][I + i]), gu is [M, 2I]; same
-// vector layout as rownorm_kernel over the I outputs.
+// y[m][i] = rn_row(silu(gu[m][i]) * gu[m][I + i]), gu rows ld >= 2I elements
+// apart; same vector layout as rownorm_kernel over the I outputs.
 template <int V>
-__global__ __launch_bounds__(kThreads) void swiglu_rownorm_kernel(const uint16_t *__restrict__ gu,
+__global__ __launch_bounds__(kThreads) void swiglu_rownorm_kernel(const uint16_t *__restrict__ gu, int ld,
                                                                   int I, uint16_t *__restrict__ y) {
     __shared__ float sh[kWaves];
-    const uint16_t *gr = gu + (size_t)blockIdx.x * 2 * I;
+    const uint16_t *gr = gu + (size_t)blockIdx.x * ld;
     const int nvec = I >> 3;
     u32x4 g[V], u[V];
 #pragma unroll
@@ -133,14 +133,14 @@ hipError_t launch_rownorm(const uint16_t *x, int64_t M, int64_t ldx, int64_t wid
     return hipGetLastError();
 }
 
-hipError_t launch_swiglu_rownorm(const uint16_t *gu, int64_t M, int64_t I, uint16_t *y,
+hipError_t launch_swiglu_rownorm(const uint16_t *gu, int64_t M, int64_t ld, int64_t I, uint16_t *y,
                                  hipStream_t stream) {
-    if (I % 8 != 0 || I > kGlueMaxWidth) return hipErrorInvalidValue;
+    if (I % 8 != 0 || ld % 8 != 0 || ld < 2 * I || I > kGlueMaxWidth) return hipErrorInvalidValue;
     const dim3 grid((unsigned)M), block(kThreads);
     switch (vectors_per_thread(I)) {
-        case 1: hipLaunchKernelGGL(swiglu_rownorm_kernel<1>, grid, block, 0, stream, gu, (int)I, y); break;
-        case 2: hipLaunchKernelGGL(swiglu_rownorm_kernel<2>, grid, block, 0, stream, gu, (int)I, y); break;
-        default: hipLaunchKernelGGL(swiglu_rownorm_kernel<4>, grid, block, 0, stream, gu, (int)I, y); break;
+        case 1: hipLaunchKernelGGL(swiglu_rownorm_kernel<1>, grid, block, 0, stream, gu, (int)ld, (int)I, y); break;
+        case 2: hipLaunchKernelGGL(swiglu_rownorm_kernel<2>, grid, block, 0, stream, gu, (int)ld, (int)I, y); break;
+        default: hipLaunchKernelGGL(swiglu_rownorm_kernel<4>, grid, block, 0, stream, gu, (int)ld, (int)I, y); break;
     }
     return hipGetLastError();
 }

@@ -12,6 +12,9 @@ enum GemmPath { kPathGemv = 1, kPathMfma = 2 };
 // Rows per chunk of the matrix-core GEMV (a multiple of 16 dividing every G,
 // which is a multiple of 32).
 constexpr int kMmaChunkRows = 32;
+// Most K-splits of a GEMV: its fixed-point split-K slots count arrivals in
+// four bits (device.h).
+constexpr int kGemvMaxSplits = 16;
 
 // Everything a GEMM launch needs besides the tensors; computed on the host
 // from (M, K, N, G) alone so that it can be inspected without a GPU.
@@ -28,6 +31,8 @@ struct GemmPlan {
                               // kMmaChunkRows-row chunks); false: the dot2 GEMV
     bool fold = false;        // GEMV, symmetric zero point: remove bias and zero per chunk, not per pair
     bool fold_asym = false;   // the same with packed zeros
+    bool exact = false;       // matrix-core GEMV, symmetric zero point: exact (q - z) weights
+                              // instead of biased weights with the zero term folded per chunk
     int64_t tiles_n = 0;      // workgroup tiles along N
     int64_t tiles_m = 1;      // workgroup tiles along M (MFMA)
     int m_group = 1;          // MFMA: consecutive workgroups walk this many row tiles of one
@@ -91,8 +96,8 @@ constexpr int64_t kGlueMaxWidth = 32768;
 // y[m][0..width) = rn(x[m][0..width)) with x row stride ldx.
 hipError_t launch_rownorm(const uint16_t *x, int64_t M, int64_t ldx, int64_t width, uint16_t *y,
                           hipStream_t stream);
-// y[m][i] = rn_row(silu(gu[m][i]) * gu[m][I + i]), gu is [M, 2I].
-hipError_t launch_swiglu_rownorm(const uint16_t *gu, int64_t M, int64_t I, uint16_t *y,
+// y[m][i] = rn_row(silu(gu[m][i]) * gu[m][I + i]), gu rows ld >= 2I apart.
+hipError_t launch_swiglu_rownorm(const uint16_t *gu, int64_t M, int64_t ld, int64_t I, uint16_t *y,
                                  hipStream_t stream);
 
 }  // namespace w4a16
