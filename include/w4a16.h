@@ -112,11 +112,11 @@ int w4a16_repack_scales(const uint16_t *src_ng, uint16_t *dst_gn, int64_t Gn, in
  *
  * Paths (w4a16_gemm_plan reports which): M <= 8 (with N % 32 == 0) runs a
  * split-K GEMV whose k-reduction runs on the matrix cores
- * (v_mfma_f32_16x16x32_f16 on exactly converted weights, 1024 + q or 64 + q,
- * with the zero term removed per 32-row chunk by the same MFMA chain; packed
- * zeros, and a symmetric zero point on request (tuning key gemv_mma_exact),
- * take exact (q - z) weights instead); the tuning key gemv_mma=0 selects the
- * same GEMV with v_dot2_f32_f16 on the vector ALUs.  M >= 9 runs an MFMA
+ * (v_mfma_f32_16x16x32_f16 on the exact integers q - z in fp16; with the
+ * tuning key gemv_mma_exact=0 and a symmetric zero point, on biased weights
+ * 1024 + q or 64 + q with the zero term removed per 32-row chunk by the same
+ * MFMA chain); the tuning key gemv_mma=0 selects the same GEMV with
+ * v_dot2_f32_f16 on the vector ALUs.  M >= 9 runs an MFMA
  * GEMM that dequantises the weights in registers to exact (q - z) fp16
  * operands and applies each group's scale to the fp32 sums of that group.
  * Accumulation is fp32 throughout.  K-splits across workgroups meet in
@@ -262,8 +262,9 @@ int w4a16_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t G, int32_t *path,
 /* Replace the planner's tuning overrides (the same "key=value,..." form the
  * environment variable W4A16_TUNE gives at first use; NULL or "" restores the
  * defaults).  Keys: gemv_mma (1 default: the matrix-core GEMV at M <= 8;
- * 0: the dot2 GEMV), gemv_mma_exact (1: the matrix-core GEMV takes exact
- * (q - z) weights with a symmetric zero point too), gemv_mma_words (2 or 4
+ * 0: the dot2 GEMV), gemv_mma_exact (1 default: the matrix-core GEMV takes
+ * exact (q - z) weights; 0: with a symmetric zero point, biased weights and
+ * the zero term folded per chunk), gemv_mma_words (2 or 4
  * words per lane: 256- or 512-column tiles, M <= 2; 0 by fill),
  * gemv_target_waves (the dot2 GEMV's M <= 2 wave target),
  * gemv_waves (4 or 8; 4 selects the dot2 GEMV), gemv_splits,

@@ -132,7 +132,7 @@ def test_gemm_dot2_gemv_matches_oracle(M, K, N, G, asym):
 TUNED_FORMS = ["gemv_mma=0", "gemv_mma=0,gemv_fold=0", "gemv_mma=0,gemv_fold=1", "gemv_waves=4",
                "gemv_waves=4,gemv_fold=1", "gemv_mma=0,gemv_splits=1", "gemv_mma=0,gemv_splits=7",
                "gemv_mma=1", "gemv_mma=1,gemv_splits=1", "gemv_mma=1,gemv_splits=7", "gemv_mma=1,gemv_splits=16",
-               "gemv_mma_exact=1", "gemv_mma_exact=1,gemv_mma_words=4",
+               "gemv_mma_exact=0", "gemv_mma_exact=0,gemv_mma_words=4",
                "gemv_mma_words=4", "gemv_mma_words=4,gemv_splits=3", "gemv_mma_words=2",
                "gemv_max_m=0", "mfma_cfg=3", "mfma_cfg=2,mfma_splits=3",
                "mfma_cfg=1", "mfma_cfg=2", "mfma_cfg=3,mfma_splits=3", "mfma_cfg=3,mfma_splits=8",
@@ -180,15 +180,15 @@ def f16_ulp(x):
 
 @pytest.mark.parametrize("M", [1, 2, 5, 8, 12, 32, 256])
 def test_gemm_identities(M):
-    """All-8 nibbles with zero point 8 give exactly 0 on every path (the
-    matrix-core GEMV forms its zero term with the same MFMA chain as the
-    products, the dot2 GEMV with the same dot chain, the MFMA GEMM takes exact
-    (q - z) operands).  qzeros all 8 equal the symmetric call bit for bit where
-    both take the same arithmetic form: by default the symmetric matrix-core
-    GEMV and the dot2 GEMV at M <= 2 fold the zero point per chunk while
-    packed zeros take exact (q - z) weights, so there the two agree within the
-    tolerance and bit for bit with the exact form forced (gemv_mma_exact=1,
-    gemv_fold=0).  Doubling every scale doubles the output: exactly where the
+    """All-8 nibbles with zero point 8 give exactly 0 on every path and form
+    (exact (q - z) operands on the matrix-core GEMV and the MFMA GEMM; in the
+    folded forms the zero term runs the same MFMA or dot chain as the
+    products).  qzeros all 8 equal the symmetric call bit for bit where both
+    take the same arithmetic form: everywhere by default except the dot2 GEMV
+    at M <= 2 (gemv_mma=0), which folds a symmetric zero point per chunk while
+    packed zeros take exact (q - z) weights; there, and for the matrix-core
+    GEMV's folded form (gemv_mma_exact=0), the two agree within the tolerance,
+    and bit for bit with the exact form forced.  Doubling every scale doubles the output: exactly where the
     K-splits meet in fp32 (the MFMA GEMM scales each group's fp32 sums), and to
     within one fp16 step where the GEMVs' K-splits meet in 2^-28 fixed point
     (each split's partial is rounded to that grid, which does not commute with
@@ -198,21 +198,23 @@ def test_gemm_identities(M):
     p = synth.problem(M, K, N, G, False, seed=55 + M)
     a, b, s = dev(p["a"]), dev(p["b_packed"]), dev(p["scales"])
     eights = torch.full_like(b, np.uint32(0x88888888).view(np.int32).item())
-    for spec in ("", "gemv_mma=0", "gemv_mma_exact=1", "gemv_mma=0,gemv_fold=0"):
+    for spec in ("", "gemv_mma=0", "gemv_mma_exact=0", "gemv_mma=0,gemv_fold=0"):
         zero = tuned(spec, lambda: host(w4.w4a16_gemm(a, eights, s, None, G, 8)))
         assert np.all(zero == 0), spec
     qz8 = torch.full((K // G, N // 8), np.uint32(0x88888888).view(np.int32).item(), dtype=torch.int32, device="cuda")
     sym = host(w4.w4a16_gemm(a, b, s, None, G, 8))
     asym = host(w4.w4a16_gemm(a, b, s, qz8, G, 3))
-    if path == 3 or (path == 1 and M <= 2):
-        check_close(asym, sym, "asym vs folded sym")
-        exact = "gemv_mma_exact=1" if path == 3 else "gemv_fold=0"
-        sym0 = tuned(exact, lambda: host(w4.w4a16_gemm(a, b, s, None, G, 8)))
-        asym0 = tuned(exact, lambda: host(w4.w4a16_gemm(a, b, s, qz8, G, 3)))
-        assert np.array_equal(sym0.view(np.uint16), asym0.view(np.uint16))
-        assert np.array_equal(asym0.view(np.uint16), asym.view(np.uint16))  # packed zeros: exact form already
-    else:
-        assert np.array_equal(sym.view(np.uint16), asym.view(np.uint16))
+    assert np.array_equal(sym.view(np.uint16), asym.view(np.uint16))
+    for folded, exact in (("gemv_mma_exact=0", ""), ("gemv_mma=0", "gemv_mma=0,gemv_fold=0")):
+        fpath = tuned(folded, lambda: w4.w4a16_gemm_plan(M, K, N, G))[0]
+        sym_f = tuned(folded, lambda: host(w4.w4a16_gemm(a, b, s, None, G, 8)))
+        asym_f = tuned(folded, lambda: host(w4.w4a16_gemm(a, b, s, qz8, G, 3)))
+        check_close(asym_f, sym_f, "asym vs sym, %s" % folded)
+        if fpath == 1 and M <= 2 or folded == "gemv_mma_exact=0" and fpath == 3:  # folded: agree within tolerance
+            sym_e = tuned(exact, lambda: host(w4.w4a16_gemm(a, b, s, None, G, 8)))
+            assert np.array_equal(sym_e.view(np.uint16), asym_f.view(np.uint16))  # packed zeros: exact form
+        else:
+            assert np.array_equal(sym_f.view(np.uint16), asym_f.view(np.uint16))
     dbl = host(w4.w4a16_gemm(a, b, s * 2, None, G, 8)).astype(np.float64)
     two = 2 * sym.astype(np.float64)
     if path in (1, 3) and splits > 1:
@@ -228,7 +230,7 @@ def same_fp16(got, want):
     return np.array_equal(gn, rn) and np.array_equal(g[~gn], r[~rn])
 
 
-NONFINITE_FORMS = ["", "gemv_mma_exact=1", "gemv_mma=0,gemv_fold=0", "gemv_max_m=0"]
+NONFINITE_FORMS = ["", "gemv_mma_exact=0", "gemv_mma=0,gemv_fold=0", "gemv_max_m=0"]
 
 
 @pytest.mark.parametrize("spec", NONFINITE_FORMS)
@@ -238,8 +240,8 @@ def test_gemm_nonfinite_and_overflow(M, K, N, spec):
     the exact forms: an infinity times a nonzero (q - z) gives an infinity of
     the product's sign, times zero NaN, and infinities of both signs in one
     sum NaN -- the oracle's classes and signs, element for element (the
-    matrix-core GEMV redoes such chunks with exact weights; its K-splits keep
-    +-inf apart in the fixed-point slots).  Activations of +-60000 against
+    matrix-core GEMV's folded form redoes such chunks with exact weights; the
+    GEMVs' K-splits keep +-inf apart in the fixed-point slots).  Activations of +-60000 against
     all-15 nibbles overflow fp16 to inf of the oracle's sign, also where split
     partials exceed the fixed-point range."""
     G = 128 if K >= 128 else K
@@ -267,8 +269,7 @@ def test_gemm_nonfinite_and_overflow(M, K, N, spec):
     assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
 
 
-@pytest.mark.parametrize("spec", ["gemv_splits=2,gemv_mma_exact=1", "gemv_splits=2,gemv_mma=0,gemv_fold=0",
-                                  "gemv_max_m=0"])
+@pytest.mark.parametrize("spec", ["gemv_splits=2", "gemv_splits=2,gemv_mma=0,gemv_fold=0", "gemv_max_m=0"])
 def test_gemm_split_cancellation(spec):
     """Two K-splits whose partials cancel, on the forms whose products are
     exact ((q - z) weights).  Within the fixed-point range of the GEMVs'
@@ -435,7 +436,7 @@ def composed_step(dstack, x):
     return w4.w4a16_rownorm(d)
 
 
-@pytest.mark.parametrize("spec", ["", "gemv_mma=0", "decode_fuse=0", "decode_swiglu_m=9", "gemv_mma_exact=1",
+@pytest.mark.parametrize("spec", ["", "gemv_mma=0", "decode_fuse=0", "decode_swiglu_m=9", "gemv_mma_exact=0",
                                   "decode_rn_mfma=1"])
 @pytest.mark.parametrize("M", [1, 2, 5, 20, 32])
 def test_decode_step_is_the_composition(M, spec):
@@ -443,7 +444,7 @@ def test_decode_step_is_the_composition(M, spec):
     its header lists gives (two layers), on every route: the fused GEMVs, the
     dot2 GEMVs, separate glue kernels, SwiGLU inside the GEMV at M <= 8, the
     MFMA route with the row-norm as a kernel and folded."""
-    if spec in ("gemv_mma=0", "decode_swiglu_m=9", "gemv_mma_exact=1") and M > 8:
+    if spec in ("gemv_mma=0", "decode_swiglu_m=9", "gemv_mma_exact=0") and M > 8:
         pytest.skip("GEMV-route forms apply at M <= 8 only")
     H, NQ, I, G = 256, 384, 512, 64
     layers = synth.stack_layer(0, H=H, NQ=NQ, I=I, G=G, seed_base=2900) + \

@@ -59,7 +59,8 @@ struct Tune {
     int64_t gemv_max_m = 8;            // largest M sent to the GEMV path (at most 8)
     int64_t gemv_mma = 1;              // GEMV k-reduction on the matrix cores (0: the dot2 GEMV)
     int64_t gemv_mma_words = 0;        // matrix-core GEMV words per lane: 2 (256-column tiles), 4 (512, M <= 2), 0 by fill
-    int64_t gemv_mma_exact = 0;        // matrix-core GEMV, symmetric zero point: 1 exact (q - z) weights
+    int64_t gemv_mma_exact = 1;        // matrix-core GEMV, symmetric zero point: 1 exact (q - z) weights,
+                                       // 0 biased weights with the zero term folded per chunk
     int64_t mfma_target_waves = 2048;  // aim for about this many MFMA-path waves
     int64_t mfma_splits = 0;           // force the MFMA split count
     int64_t mfma_cfg = 0;  // force (mt, waves, kwaves): 1..3 = (1,2,4) (2,2,4) (2,1,8)

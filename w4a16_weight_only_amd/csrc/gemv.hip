@@ -608,26 +608,27 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(
 //    occupies A rows 2 mu and 2 mu + 1, which hold the row's activations in
 //    the even and in the odd k-slots only, so D row 2 mu + e collects column
 //    c + 4e.  Up to 8 activation rows fill the 16 A rows.
-//  * Zero point.  Symmetric: folded per chunk.  The zero term
-//    sum(a) * (bias + zp) runs the same MFMA chain as the products, on two B
-//    operands that hold (bias + zp) in every k-slot (bias 1024 and 64); the
-//    chunk's (q - z) sums are D minus that term, scaled by the group scale
-//    into an fp32 total (the per-group factorisation out = sum_g s (sum a q'
-//    - z' sum a)).  A column whose nibbles all equal zp gets the same MFMA
-//    inputs twice, so it cancels to exactly 0.  The bias costs about 10 bits
-//    of the fp32 sums of one chunk, leaving an error like the dot2 form's.
-//    Packed zeros (and, on request, a symmetric zero point: the exact form):
-//    the zero word is unpacked like a weight word and one packed subtraction
-//    per register leaves the exact (q - z) before the MFMA (zeros vary by
-//    column, so a folded term would take one MFMA per word and nibble pair).
-//    Packed zeros that all equal zp give bit for bit the exact form's
-//    symmetric result: the same exact products in the same order.
-//  * Non-finite activations.  The biased sums would turn an infinite
-//    activation into inf - inf; when the zero term of a chunk is not finite
-//    (exactly when one of its activations is not), the wave recomputes all
-//    its chunks after the loop in the exact form, so infinities keep their
-//    sign and a zero weight times an infinity gives NaN, as in the
-//    definition.
+//  * Zero point.  By default (and always with packed zeros) the zero word is
+//    unpacked like a weight word and one packed subtraction per register
+//    leaves the exact integer (q - z) in fp16 before the MFMA: the products
+//    are exact, so a column whose nibbles all equal its zero point sums to
+//    exactly 0, and packed zeros that all equal zp give bit for bit the
+//    symmetric result.  Measured on MI355X the subtraction costs nothing
+//    visible (headline 8.24 -> 8.22 us).  Folded form (a symmetric zero point
+//    with the tuning key gemv_mma_exact=0): B holds the biased weights and the
+//    zero term sum(a) * (bias + zp) runs the same MFMA chain as the products,
+//    on two B operands that hold (bias + zp) in every k-slot (bias 1024 and
+//    64); the chunk's (q - z) sums are D minus that term, scaled by the group
+//    scale into an fp32 total (the per-group factorisation out = sum_g s
+//    (sum a q' - z' sum a)).  An all-zp column gets the same MFMA inputs
+//    twice and cancels to exactly 0, but the biased sums (about 1000x the
+//    result) carry fp32 rounding of their own size.
+//  * Non-finite activations.  In the folded form the biased sums would turn
+//    an infinite activation into inf - inf; when the zero term of a chunk is
+//    not finite (exactly when one of its activations is not), the wave
+//    recomputes all its chunks after the loop in the exact form, so
+//    infinities keep their sign and a zero weight times an infinity gives
+//    NaN, as in the definition (and as the exact form gives directly).
 //
 // Lane (j, g) = (lane % 16, lane / 16) loads words 2j, 2j+1 of the tile (8
 // bytes of each row) for rows 16 s + 4 g + i (i < 4) of set s, and the
