@@ -143,6 +143,26 @@ int w4a16_gemm(const uint16_t *a, const int32_t *b_packed, const uint16_t *scale
                const int32_t *qzeros, int64_t M, int64_t K, int64_t N, int64_t G,
                int32_t zp_bias, uint16_t *out, hipStream_t stream);
 
+/*
+ * w4a16_gemm without any allocation, for callers that cannot allocate device
+ * memory: code under HIP graph capture that has not run the shape before,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * plans, kernels and results as w4a16_gemm (bit for bit); the split-K scratch
+ * is a fixed array of 4 MiB (counters and fixed-point slots) + 12 MiB (fp32
+ * partials) in the library's device data, one per GPU, held until the
+ * process ends.  Its device address is taken on the first call on each
+ * device, which also clears the counters with a kernel on `stream` (no
+ * allocation, no memset); every call leaves them zero again.  All calls on
+ * one GPU share the array: calls that overlap in time on one GPU (several
+ * streams or threads) race and must not be issued.
+ * Errors: as w4a16_gemm; UNSUPPORTED when the shape's plan needs more scratch
+ * than the array holds (M * N * 8 bytes of slots for the GEMV; splits * M * N
+ * * 4 bytes of partials for the MFMA GEMM), with the sizes in the message.
+ */
+int w4a16_gemm_noalloc(const uint16_t *a, const int32_t *b_packed, const uint16_t *scales,
+                       const int32_t *qzeros, int64_t M, int64_t K, int64_t N, int64_t G,
+                       int32_t zp_bias, uint16_t *out, hipStream_t stream);
+
 /* One W4A16 linear of a decode stack (host struct; pointers are device). */
 typedef struct {
     const int32_t *b_packed;  /* [K, N/8] */

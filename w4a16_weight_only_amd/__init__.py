@@ -17,7 +17,7 @@ import ctypes
 import os
 
 __all__ = [
-    "W4A16Error", "lib", "w4a16_gemm", "w4a16_repack", "w4a16_repack_scales", "w4a16_decode_step",
+    "W4A16Error", "lib", "w4a16_gemm", "w4a16_gemm_noalloc", "w4a16_repack", "w4a16_repack_scales", "w4a16_decode_step",
     "w4a16_decode_workspace_bytes", "w4a16_gemm_glue", "w4a16_gemm_glue_workspace_bytes", "w4a16_rownorm",
     "w4a16_gemm_plan", "w4a16_set_tuning", "w4a16_release", "Linear", "STATUS",
     "GLUE_NONE", "GLUE_RMSNORM", "GLUE_SWIGLU",
@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
     L.w4a16_repack_scales.argtypes = [P, P, I64, I64, P]
     L.w4a16_gemm.restype = ctypes.c_int
     L.w4a16_gemm.argtypes = [P, P, P, P, I64, I64, I64, I64, I32, P, P]
+    L.w4a16_gemm_noalloc.restype = ctypes.c_int
+    L.w4a16_gemm_noalloc.argtypes = [P, P, P, P, I64, I64, I64, I64, I32, P, P]
     L.w4a16_decode_workspace_bytes.restype = SZ
     L.w4a16_decode_workspace_bytes.argtypes = [I64, P, I64]
     L.w4a16_decode_step.restype = ctypes.c_int
@@ -143,6 +145,28 @@ def w4a16_gemm(a, b_packed, scales, qzeros=None, G=128, zp_bias=8, out=None):
     _check(lib().w4a16_gemm(a.data_ptr(), b_packed.data_ptr(), scales.data_ptr(),
                             None if qzeros is None else qzeros.data_ptr(), M, K, N, G, zp_bias,
                             out.data_ptr(), _stream_ptr(a.device)))
+    return out
+
+
+def w4a16_gemm_noalloc(a, b_packed, scales, qzeros, G, zp_bias, out):
+    """w4a16_gemm into a caller-allocated `out`, with the library's split-K
+    scratch in its fixed per-GPU array: no allocation at all."""
+    torch = _torch()
+    _dev_tensor(a, "a", torch.float16, 2)
+    _dev_tensor(b_packed, "b_packed", torch.int32, 2)
+    _dev_tensor(scales, "scales", torch.float16, 2)
+    _dev_tensor(out, "out", torch.float16, 2)
+    M, K = a.shape
+    N = b_packed.shape[1] * 8
+    if b_packed.shape[0] != K or tuple(scales.shape) != (K // G, N) or tuple(out.shape) != (M, N):
+        raise ValueError("shapes do not match a [M, K], b_packed [K, N/8], scales [K/G, N], out [M, N]")
+    if qzeros is not None:
+        _dev_tensor(qzeros, "qzeros", torch.int32, 2)
+        if tuple(qzeros.shape) != (K // G, N // 8):
+            raise ValueError("qzeros must be [K/G, N/8]")
+    _check(lib().w4a16_gemm_noalloc(a.data_ptr(), b_packed.data_ptr(), scales.data_ptr(),
+                                    None if qzeros is None else qzeros.data_ptr(), M, K, N, G, zp_bias,
+                                    out.data_ptr(), _stream_ptr(a.device)))
     return out
 
 

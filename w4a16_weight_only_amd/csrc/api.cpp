@@ -590,6 +590,31 @@ int w4a16_gemm(const uint16_t *a, const int32_t *b_packed, const uint16_t *scale
     return run_gemm(a, b_packed, scales, qzeros, M, K, N, G, zp_bias, out, stream);
 }
 
+int w4a16_gemm_noalloc(const uint16_t *a, const int32_t *b_packed, const uint16_t *scales, const int32_t *qzeros,
+                       int64_t M, int64_t K, int64_t N, int64_t G, int32_t zp_bias, uint16_t *out,
+                       hipStream_t stream) {
+    int rc = validate_gemm(a, b_packed, scales, qzeros, M, K, N, G, zp_bias, out);
+    if (rc != W4A16_OK) return rc;
+    if (M == 0) return ok();
+    const GemmPlan plan = plan_gemm(M, K, N, G);
+    const size_t cbytes = plan.counters * sizeof(uint32_t), pbytes = plan.partial_floats * sizeof(float);
+    if (cbytes > kNoAllocCounterBytes || pbytes > kNoAllocPartialBytes)
+        return fail(W4A16_ERR_UNSUPPORTED,
+                    "this shape's split-K scratch (" + std::to_string(cbytes) + " counter bytes, " +
+                        std::to_string(pbytes) + " partial bytes) exceeds the allocation-free entry point's " +
+                        std::to_string(kNoAllocCounterBytes) + " + " + std::to_string(kNoAllocPartialBytes) +
+                        " bytes; use w4a16_gemm");
+    GemmArgs args{a, b_packed, scales, qzeros, M, K, N, G, zp_bias, out, nullptr, nullptr};
+    hipError_t e = hipSuccess;
+    if (plan.splits > 1) {
+        e = noalloc_scratch(stream, &args.counters, &args.partials);
+        if (e != hipSuccess) return fail(W4A16_ERR_HIP, std::string("scratch set-up: ") + hipGetErrorString(e));
+    }
+    e = plan.path == kPathGemv ? launch_gemv(args, plan, stream) : launch_mfma(args, plan, stream);
+    if (e != hipSuccess) return fail(W4A16_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+    return ok();
+}
+
 int w4a16_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t G, int32_t *path, int32_t *splits,
                     int64_t *grid) {
     int rc = validate_sizes(M, K, N, G);

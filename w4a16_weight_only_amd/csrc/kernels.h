@@ -86,6 +86,14 @@ size_t mfma_rn_extra_floats(const GemmPlan &plan);
 // (mt, waves, kwaves) configuration.
 int mfma_max_splits(int mt, int waves, int kwaves);
 hipError_t launch_repack(const int32_t *src, int32_t *dst, int64_t K, int64_t N, hipStream_t stream);
+
+// Split-K scratch of the allocation-free GEMM entry point (noalloc.hip): a
+// fixed device array per GPU, counters and slots first, fp32 partials after.
+constexpr size_t kNoAllocCounterBytes = (size_t)4 << 20;
+constexpr size_t kNoAllocPartialBytes = (size_t)12 << 20;
+// Device addresses of this GPU's array (taken once per device, the counter
+// region cleared by a kernel on `stream` the first time).
+hipError_t noalloc_scratch(hipStream_t stream, uint32_t **counters, float **partials);
 // fp16 [N, Gn] -> [Gn, N] (checkpoint group scales to the kernel layout).
 hipError_t launch_repack_scales(const uint16_t *src, uint16_t *dst, int64_t Gn, int64_t N, hipStream_t stream);
 
