@@ -137,7 +137,9 @@ TUNED_FORMS = ["gemv_mma=0", "gemv_mma=0,gemv_fold=0", "gemv_mma=0,gemv_fold=1",
                "gemv_max_m=0", "mfma_cfg=3", "mfma_cfg=2,mfma_splits=3",
                "mfma_cfg=1", "mfma_cfg=2", "mfma_cfg=3,mfma_splits=3", "mfma_cfg=3,mfma_splits=8",
                "mfma_mgroup=1", "mfma_mgroup=2",
-               "mfma_cfg=3,mfma_mgroup=3", "mfma_cfg=1,mfma_mgroup=4,mfma_splits=2"]
+               "mfma_cfg=3,mfma_mgroup=3", "mfma_cfg=1,mfma_mgroup=4,mfma_splits=2",
+               "mfma_shared_m=0", "mfma_shared_m=0,mfma_cfg=2", "mfma_shared_m=9", "mfma_shared_m=9,mfma_wm=4",
+               "mfma_shared_m=9,mfma_splits=2", "mfma_wm=2,mfma_mgroup=2", "mfma_wm=4,mfma_mgroup=1"]
 
 
 @pytest.mark.parametrize("spec", TUNED_FORMS)
@@ -161,6 +163,29 @@ def test_gemm_tuned_forms_match_oracle(spec):
             check_close(got, want, "%s M=%d" % (spec, M))
     finally:
         w4.w4a16_set_tuning(None)
+
+
+SHARED_CASES = [(64, 4096, 1000, 32, True), (129, 4096, 1000, 64, False), (256, 4096, 1032, 128, True),
+                (100, 3072, 520, 256, True), (256, 12800, 512, 128, True), (33, 2048, 4104, 128, False)]
+SHARED_FORMS = ["", "mfma_wm=2", "mfma_wm=4", "mfma_splits=1", "mfma_splits=3", "mfma_splits=8",
+                "mfma_wm=4,mfma_splits=7,mfma_mgroup=1", "mfma_wm=2,mfma_splits=5,mfma_mgroup=3"]
+
+
+@pytest.mark.parametrize("M,K,N,G,asym", SHARED_CASES)
+def test_gemm_shared_kernel_matches_oracle(M, K, N, G, asym):
+    """The MFMA kernel whose row waves share each step's dequantised weights
+    through LDS, in both row-wave shapes, at every group size it takes, with
+    ragged rows and column tiles, K-waves of unequal group counts and forced
+    K-split counts (one to eight, uneven)."""
+    p = synth.problem(M, K, N, G, asym, seed=900 + M + K + N)
+    want = oracle_gemm_columns(p["a"], p["b_packed"], p["scales"], p["qzeros"], G, 8)
+    for spec in SHARED_FORMS:
+        full = "mfma_shared_m=1," + spec if spec else "mfma_shared_m=1"
+        path, splits, grid = tuned(full, lambda: w4.w4a16_gemm_plan(M, K, N, G))
+        note("shared %s M=%d K=%d N=%d G=%d path=%d splits=%d grid=%d" % (full, M, K, N, G, path, splits, grid))
+        assert path == 2
+        got = tuned(full, lambda: run_gemm(p))
+        check_close(got, want, "shared %s M=%d" % (full, M))
 
 
 @pytest.mark.parametrize("M", [1, 4, 8, 16, 32, 256])
@@ -230,7 +255,7 @@ def same_fp16(got, want):
     return np.array_equal(gn, rn) and np.array_equal(g[~gn], r[~rn])
 
 
-NONFINITE_FORMS = ["", "gemv_mma_exact=0", "gemv_mma=0,gemv_fold=0", "gemv_max_m=0"]
+NONFINITE_FORMS = ["", "gemv_mma_exact=0", "gemv_mma=0,gemv_fold=0", "gemv_max_m=0", "gemv_max_m=0,mfma_shared_m=1"]
 
 
 @pytest.mark.parametrize("spec", NONFINITE_FORMS)

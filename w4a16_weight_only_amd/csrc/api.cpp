@@ -69,6 +69,9 @@ struct Tune {
     int64_t decode_fuse = 1;           // 0: decode-step glue as separate kernels
     int64_t decode_swiglu_m = 3;       // GEMV route: from this M on, SwiGLU + row-norm as a kernel of its own
     int64_t decode_rn_mfma = 0;        // 1: the MFMA GEMMs fold the row-norm (no fp16 rounding of rn(x))
+    int64_t mfma_shared_m = 64;        // from this M on, the MFMA kernel sharing dequantised weights
+                                       // through LDS (0: never)
+    int64_t mfma_wm = 0;               // force its row waves (2 or 4; 0: 4 above 64 rows, else 2)
 };
 
 // Returns false on an unknown key or a malformed entry (nothing applied).
@@ -96,6 +99,8 @@ bool parse_tune(const char *spec, Tune *out) {
         else if (k == "gemv_mma") v.gemv_mma = val;
         else if (k == "gemv_mma_words") v.gemv_mma_words = val;
         else if (k == "gemv_mma_exact") v.gemv_mma_exact = val;
+        else if (k == "mfma_shared_m") v.mfma_shared_m = val;
+        else if (k == "mfma_wm") v.mfma_wm = val;
 
         else if (k == "mfma_target_waves") v.mfma_target_waves = val;
         else if (k == "mfma_splits") v.mfma_splits = val;
@@ -147,10 +152,13 @@ int validate_sizes(int64_t M, int64_t K, int64_t N, int64_t G) {
 
 namespace w4a16 {
 
-GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma, bool allow_wide) {
+GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma, bool allow_wide, bool allow_shared,
+                   int64_t partial_cap_bytes) {
     const Tune &t = tune();
     GemmPlan p;
     const int64_t N8 = N / 8;
+    const int64_t cap = partial_cap_bytes >= 0 ? std::min<int64_t>(partial_cap_bytes, t.max_partial_bytes)
+                                               : t.max_partial_bytes;
     if (M <= std::min<int64_t>(8, t.gemv_max_m) && N % 32 == 0) {
         // 256-column tiles (one 128-byte line of every weight row per
         // workgroup); K-splits to fill one round of the 256 CUs (below).
@@ -252,14 +260,35 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma, b
             int64_t splits = t.mfma_splits > 0 ? t.mfma_splits : target / (tiles * wg_waves);
             // at least two 32-row steps per K-wave, bounded partials
             splits = std::min<int64_t>(splits, std::max<int64_t>(1, nsteps / (2 * p.kwaves)));
-            splits = std::min<int64_t>(splits, std::max<int64_t>(1, t.max_partial_bytes / std::max<int64_t>(1, M * N * 4)));
+            splits = std::min<int64_t>(splits, std::max<int64_t>(1, cap / std::max<int64_t>(1, M * N * 4)));
             splits = std::min<int64_t>(splits, mfma_max_splits(p.mt, p.waves, p.kwaves));
             splits = std::max<int64_t>(1, splits);
             p.split_len = cdiv(nsteps, splits);
             p.splits = (int)cdiv(nsteps, p.split_len);
         };
+        // The LDS-shared kernel: 32 * wm rows x 128 columns per workgroup,
+        // whole groups per K-wave, K-splits to about one workgroup per CU.
+        auto fill_shared = [&](int wm) {
+            p.wm = wm;
+            p.mt = 2;
+            p.waves = 1;
+            p.kwaves = 8 / wm;
+            p.tiles_n = cdiv(N8, 16);
+            p.tiles_m = cdiv(M, 32 * wm);
+            const int64_t spg = G / 32, ngroups = K / G;
+            const int64_t tiles = p.tiles_n * p.tiles_m;
+            int64_t splits = t.mfma_splits > 0 ? t.mfma_splits : std::max<int64_t>(1, 256 / tiles);
+            splits = std::min<int64_t>(splits, std::max<int64_t>(1, ngroups / p.kwaves));  // a group per K-wave
+            splits = std::min<int64_t>(splits, std::max<int64_t>(1, cap / std::max<int64_t>(1, M * N * 4)));
+            splits = std::max<int64_t>(1, std::min<int64_t>(splits, kSharedMaxSplits));
+            p.split_len = cdiv(ngroups, splits) * spg;
+            p.splits = (int)cdiv(K / 32, p.split_len);
+        };
+        const bool shared = allow_shared && t.mfma_shared_m > 0 && M >= t.mfma_shared_m && shared_supports(G);
         static const int kCfg[3][3] = {{1, 2, 4}, {2, 2, 4}, {2, 1, 8}};
-        if (t.mfma_cfg >= 1 && t.mfma_cfg <= 3) {
+        if (shared) {
+            fill_shared(t.mfma_wm == 2 || t.mfma_wm == 4 ? (int)t.mfma_wm : (M > 64 ? 4 : 2));
+        } else if (t.mfma_cfg >= 1 && t.mfma_cfg <= 3) {
             fill(kCfg[t.mfma_cfg - 1][0], kCfg[t.mfma_cfg - 1][1], kCfg[t.mfma_cfg - 1][2]);
         } else if (M <= 16) {
             // One 16-row tile.  Measured on MI355X at M = 9..16: the 256-column
@@ -269,6 +298,11 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma, b
             // N = 6144 within 0.1 us at M = 9 and 0.7 us better at M = 16.
             if (cdiv(N8, 32) <= 24) fill(2, 1, 8);
             else fill(1, 2, 4);
+        } else if (M <= 32) {
+            // Measured on MI355X (M = 32 K = 4096 N = 12800): the 128-column
+            // 8-K-wave shape with 2 splits 17.9 us against 19.7 for the
+            // 256-column 4-K-wave shape with 5 splits, which fills more CUs.
+            fill(2, 1, 8);
         } else {
             // 32-row wave tiles (a wave keeps each group's sums and the scaled
             // totals, 128 accumulator registers): 256 columns with 4 K-waves or
@@ -305,7 +339,7 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma, b
         const int64_t krows = p.split_len * 32;
         const int64_t cols = 16 * 8 * (int64_t)p.waves;
         const double wcol = (double)krows * (double)cols * 0.5 + (double)(krows / G) * (double)cols * 2.5;
-        const double arow = (double)(16 * p.mt) * (double)krows * 2.0;
+        const double arow = (double)(p.wm ? 32 * p.wm : 16 * p.mt) * (double)krows * 2.0;
         const int64_t resident = std::max<int64_t>(1, std::min<int64_t>(32, cdiv(p.tiles_n * p.tiles_m * p.splits, 8)));
         int64_t gbest = 1;
         double cbest = -1;

@@ -292,6 +292,15 @@ __device__ __forceinline__ void slot_reset(uint64_t *slot) {
     __hip_atomic_store(slot, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Compile-time loop: f(integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima).
 __device__ __forceinline__ void wait_vm_zero() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ __forceinline__ uint32_t arrive_agent(uint32_t *counter) {

@@ -80,14 +80,6 @@ __device__ __forceinline__ void interleave() {
     }
 }
 
-// Compile-time loop: f(integral_constant<int, I>) for I in [B, E).
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F &&f) {
-    if constexpr (B < E) {
-        f(std::integral_constant<int, B>{});
-        static_for<B + 1, E>(f);
-    }
-}
 template <int A, int B>
 struct Gcd : Gcd<B, A % B> {};
 template <int A>
@@ -584,6 +576,7 @@ int mfma_max_splits(int mt, int waves, int kwaves) {
 
 hipError_t launch_mfma_rn(const GemmArgs &g, const GemmPlan &p, bool rn, const uint16_t *a, int64_t lda,
                           hipStream_t stream) {
+    if (p.wm != 0) return hipErrorInvalidValue;  // a plan of the LDS-shared kernel
     // (MT, NWN, NWK) combinations the planner emits.
     if (p.mt == 1 && p.waves == 2 && p.kwaves == 4) return launch_cfg<1, 2, 4>(g, p, rn, a, lda, stream);
     if (p.mt == 2 && p.waves == 2 && p.kwaves == 4) return launch_cfg<2, 2, 4>(g, p, rn, a, lda, stream);
@@ -592,6 +585,7 @@ hipError_t launch_mfma_rn(const GemmArgs &g, const GemmPlan &p, bool rn, const u
 }
 
 hipError_t launch_mfma(const GemmArgs &g, const GemmPlan &p, hipStream_t stream) {
+    if (p.wm != 0) return launch_mfma_shared(g, p, stream);
     return launch_mfma_rn(g, p, false, g.a, g.K, stream);
 }
 

@@ -27,6 +27,9 @@ struct GemmPlan {
     int waves = 4;
     int mt = 1;
     int kwaves = 1;           // MFMA: waves dividing a workgroup's K range (LDS-reduced)
+    int wm = 0;               // MFMA: row waves sharing each step's dequantised weights through
+                              // LDS (2 or 4; mt = 2, waves = 1, kwaves = 8 / wm); 0: the
+                              // register-direct kernel
     bool mma = false;         // GEMV with the k-reduction on the matrix cores (split_len in
                               // kMmaChunkRows-row chunks); false: the dot2 GEMV
     bool fold = false;        // GEMV, symmetric zero point: remove bias and zero per chunk, not per pair
@@ -60,8 +63,11 @@ struct GemmArgs {
 
 // allow_mma = false keeps a GEMV plan on the dot2 kernel; allow_wide = false
 // keeps the matrix-core GEMV on 256-column tiles (its SwiGLU variant has no
-// 512-column form).
-GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma = true, bool allow_wide = true);
+// 512-column form); allow_shared = false keeps an MFMA plan on the
+// register-direct kernel (the one with the folded row-norm).  MFMA K-splits
+// stop where their fp32 partials would pass partial_cap_bytes (>= 0).
+GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma = true, bool allow_wide = true,
+                   bool allow_shared = true, int64_t partial_cap_bytes = -1);
 
 hipError_t launch_gemv(const GemmArgs &args, const GemmPlan &plan, hipStream_t stream);
 // GEMV with the decode step's glue folded in: act 1: out = (src . W) * inv_row,
@@ -74,7 +80,15 @@ hipError_t launch_gemv(const GemmArgs &args, const GemmPlan &plan, hipStream_t s
 // Needs plan.waves == 8.
 hipError_t launch_gemv_act(const GemmArgs &args, const GemmPlan &plan, int act, const uint16_t *src,
                            int64_t ld, hipStream_t stream);
+// Runs the LDS-shared kernel (gemm_shared.hip) when plan.wm is set.
 hipError_t launch_mfma(const GemmArgs &args, const GemmPlan &plan, hipStream_t stream);
+// MFMA GEMM whose row waves share each step's dequantised weights through LDS
+// (plan.wm = 2 or 4 row waves of 32 rows, 8 / wm K-waves, 128-column tiles).
+// G must be 32, 64, 128 or 256, split_len whole groups, at most
+// kSharedMaxSplits K-splits.
+constexpr int kSharedMaxSplits = 8;
+inline bool shared_supports(int64_t G) { return G == 32 || G == 64 || G == 128 || G == 256; }
+hipError_t launch_mfma_shared(const GemmArgs &args, const GemmPlan &plan, hipStream_t stream);
 // MFMA GEMM on A = `a` with row stride lda (>= K); with rn, the decode step's
 // row-norm folded in: out = (a . W) * inv_row, inv_row = 1/sqrt(mean(a_row^2)
 // + 1e-6) over the row's K values, applied to the products (the partials
