@@ -166,9 +166,12 @@ def test_gemm_tuned_forms_match_oracle(spec):
 
 
 SHARED_CASES = [(64, 4096, 1000, 32, True), (129, 4096, 1000, 64, False), (256, 4096, 1032, 128, True),
-                (100, 3072, 520, 256, True), (256, 12800, 512, 128, True), (33, 2048, 4104, 128, False)]
+                (100, 3072, 520, 256, True), (256, 12800, 512, 128, True), (33, 2048, 4104, 128, False),
+                (96, 12800, 264, 32, True)]  # 400 groups: at least 4 splits (128 staged groups per split)
 SHARED_FORMS = ["", "mfma_wm=2", "mfma_wm=4", "mfma_splits=1", "mfma_splits=3", "mfma_splits=8",
-                "mfma_wm=4,mfma_splits=7,mfma_mgroup=1", "mfma_wm=2,mfma_splits=5,mfma_mgroup=3"]
+                "mfma_wm=4,mfma_splits=7,mfma_mgroup=1", "mfma_wm=2,mfma_splits=5,mfma_mgroup=3",
+                "mfma_shared_kw=1", "mfma_shared_kw=1,mfma_wm=2", "mfma_shared_kw=1,mfma_splits=3",
+                "mfma_shared_kw=1,mfma_wm=2,mfma_splits=8,mfma_mgroup=2"]
 
 
 @pytest.mark.parametrize("M,K,N,G,asym", SHARED_CASES)

@@ -69,9 +69,13 @@ struct Tune {
     int64_t decode_fuse = 1;           // 0: decode-step glue as separate kernels
     int64_t decode_swiglu_m = 3;       // GEMV route: from this M on, SwiGLU + row-norm as a kernel of its own
     int64_t decode_rn_mfma = 0;        // 1: the MFMA GEMMs fold the row-norm (no fp16 rounding of rn(x))
-    int64_t mfma_shared_m = 64;        // from this M on, the MFMA kernel sharing dequantised weights
-                                       // through LDS (0: never)
+    int64_t mfma_shared_m = 129;       // from this M on, the MFMA kernel sharing dequantised weights
+                                       // through LDS (0: never); measured on MI355X the
+                                       // register-direct kernel is faster up to M = 128 (M = 64
+                                       // K = 4096 N = 12800: 23.5 against 26.6 us; M = 128: 37.9
+                                       // against 39.8) and the two agree at M = 256 (62.5 us)
     int64_t mfma_wm = 0;               // force its row waves (2 or 4; 0: 4 above 64 rows, else 2)
+    int64_t mfma_shared_kw = 0;        // its K-waves: 1 (one wave per SIMD, deeper load ring), else 8 / wm
 };
 
 // Returns false on an unknown key or a malformed entry (nothing applied).
@@ -101,6 +105,7 @@ bool parse_tune(const char *spec, Tune *out) {
         else if (k == "gemv_mma_exact") v.gemv_mma_exact = val;
         else if (k == "mfma_shared_m") v.mfma_shared_m = val;
         else if (k == "mfma_wm") v.mfma_wm = val;
+        else if (k == "mfma_shared_kw") v.mfma_shared_kw = val;
 
         else if (k == "mfma_target_waves") v.mfma_target_waves = val;
         else if (k == "mfma_splits") v.mfma_splits = val;
@@ -272,19 +277,26 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma, b
             p.wm = wm;
             p.mt = 2;
             p.waves = 1;
-            p.kwaves = 8 / wm;
+            p.kwaves = t.mfma_shared_kw == 1 ? 1 : 8 / wm;
             p.tiles_n = cdiv(N8, 16);
             p.tiles_m = cdiv(M, 32 * wm);
             const int64_t spg = G / 32, ngroups = K / G;
             const int64_t tiles = p.tiles_n * p.tiles_m;
-            int64_t splits = t.mfma_splits > 0 ? t.mfma_splits : std::max<int64_t>(1, 256 / tiles);
+            // workgroups one round of the chip holds: one per CU, or with one
+            // K-wave (a wave per SIMD) 4 / wm per CU
+            const int64_t round = p.kwaves == 1 ? 256 * (4 / wm) : 256;
+            int64_t splits = t.mfma_splits > 0 ? t.mfma_splits : std::max<int64_t>(1, round / tiles);
             splits = std::min<int64_t>(splits, std::max<int64_t>(1, ngroups / p.kwaves));  // a group per K-wave
             splits = std::min<int64_t>(splits, std::max<int64_t>(1, cap / std::max<int64_t>(1, M * N * 4)));
+            // every K-wave's groups fit its LDS scale slots
+            splits = std::max<int64_t>(splits, cdiv(ngroups, kSharedGroupSlots));
             splits = std::max<int64_t>(1, std::min<int64_t>(splits, kSharedMaxSplits));
             p.split_len = cdiv(ngroups, splits) * spg;
             p.splits = (int)cdiv(K / 32, p.split_len);
         };
-        const bool shared = allow_shared && t.mfma_shared_m > 0 && M >= t.mfma_shared_m && shared_supports(G);
+        // (the shared kernel stages at most kSharedGroupSlots groups per split)
+        const bool shared = allow_shared && t.mfma_shared_m > 0 && M >= t.mfma_shared_m && shared_supports(G) &&
+                            cdiv(K / G, kSharedMaxSplits) <= kSharedGroupSlots;
         static const int kCfg[3][3] = {{1, 2, 4}, {2, 2, 4}, {2, 1, 8}};
         if (shared) {
             fill_shared(t.mfma_wm == 2 || t.mfma_wm == 4 ? (int)t.mfma_wm : (M > 64 ? 4 : 2));

@@ -33,14 +33,21 @@
 namespace w4a16 {
 namespace {
 
-// LDS bytes of the fragment buffers and of the K-wave reduction (the two
-// share memory).
-template <int WM>
+// LDS bytes: fragment buffers, each K-wave's group scales and packed zeros
+// (staged once per workgroup), and the K-wave reduction after the loop (which
+// reuses the same memory).
+template <int WM, int WK>
 struct SharedCfg {
-    static constexpr int kWK = 8 / WM;
-    static constexpr int kFragBytes = 2 * kWK * 8 * 4 * 256;         // [buf][kw][op][j][lane] u32
-    static constexpr int kRedBytes = (kWK - 1) * WM * 32 * 128 * 4;  // K-waves 1.. totals
-    static constexpr int kLds = kFragBytes > kRedBytes ? kFragBytes : kRedBytes;
+    static constexpr int kThreads = 64 * WM * WK;
+    static constexpr int kFragBytes = 2 * WK * 8 * 4 * 256;            // [buf][kw][op][j][lane] u32
+    static constexpr int kGM = kSharedGroupSlots / WK;                 // group slots per K-wave
+    static constexpr int kScaleBytes = kSharedGroupSlots * 256;        // [kw][group][128 columns] fp16
+    static constexpr int kZeroBytes = kSharedGroupSlots * 64;          // [kw][group][16 words] u32
+    static constexpr int kLoopBytes = kFragBytes + kScaleBytes + kZeroBytes;
+    static constexpr int kRedBytes = (WK - 1) * WM * 32 * 128 * 4;     // K-waves 1.. totals
+    static constexpr int kLds = kLoopBytes > kRedBytes ? kLoopBytes : kRedBytes;
+    // ring of steps in flight in registers: deeper with one wave per SIMD
+    static constexpr int kRing = WK == 1 ? 8 : 4;
 };
 
 // Workgroup barrier for waves that keep global loads in flight: waits for
@@ -48,22 +55,25 @@ struct SharedCfg {
 // prefetched global loads), then s_barrier.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int WM, int SPG, bool ASYM>
-__global__ __launch_bounds__(512) void mfma_shared_kernel(
+template <int WM, int WK, int SPG, bool ASYM>
+__global__ __launch_bounds__(64 * WM * WK) void mfma_shared_kernel(
     const uint16_t *__restrict__ a, const uint32_t *__restrict__ b, const uint16_t *__restrict__ scales,
     const uint32_t *__restrict__ qzeros, int M, int K, int N, int G, uint32_t zp, int tiles_n, int tiles_m,
     int m_group, int split_len, int splits, uint16_t *__restrict__ out, float *__restrict__ partials,
     uint32_t *__restrict__ counters) {
-    using C = SharedCfg<WM>;
-    constexpr int WK = C::kWK;
-    constexpr int R = 4;                  // ring of steps in registers (loads three steps ahead)
-    constexpr int U = SPG > 4 ? SPG : 4;  // steps per loop iteration (ring indices stay static)
+    using C = SharedCfg<WM, WK>;
+    constexpr int NT = C::kThreads;
+    constexpr int R = C::kRing;           // loads R - 1 steps ahead
+    constexpr int U = SPG > R ? SPG : R;  // steps per loop iteration (ring indices stay static)
     constexpr int JPW = 4 / WM;           // row pairs (B registers per operand) each row wave converts
+    constexpr int GM = C::kGM;
     static_assert(WM == 2 || WM == 4, "two or four row waves");
     static_assert(U % R == 0 && U % 2 == 0 && U % SPG == 0, "static ring slots per iteration");
 
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::kLds];
     uint32_t *const frag = reinterpret_cast<uint32_t *>(smem);  // [2][WK][8][4][64]
+    uint16_t *const sl = reinterpret_cast<uint16_t *>(smem + C::kFragBytes);                   // [WK][GM][128]
+    uint32_t *const zl = reinterpret_cast<uint32_t *>(smem + C::kFragBytes + C::kScaleBytes);  // [WK][GM][16]
 
     // Logical workgroup (XCD-contiguous runs; grid is a multiple of 8), split,
     // then bands of m_group row tiles per column tile, as in gemm_mfma.hip.
@@ -114,8 +124,6 @@ __global__ __launch_bounds__(512) void mfma_shared_kernel(
     const __amdgpu_buffer_rsrc_t ars = buffer_rsrc(a, (uint32_t)((uint64_t)M * K * 2));
     const __amdgpu_buffer_rsrc_t srs = buffer_rsrc(scales, (uint32_t)((uint64_t)(K / G) * N * 2));
     const __amdgpu_buffer_rsrc_t zrs = buffer_rsrc(qzeros, ASYM ? (uint32_t)((uint64_t)(K / G) * row_bytes) : 0u);
-    const uint32_t s_voff = (uint32_t)wordc * 16u;
-    const uint32_t z_voff = (uint32_t)wordc * 4u;
     // A rows past M read row M - 1, packed words past the tile's last word read
     // on into the next row or (past the end) zeros: their results are never
     // stored
@@ -151,13 +159,20 @@ __global__ __launch_bounds__(512) void mfma_shared_kernel(
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) araw[slot][mt] = buffer_load_x4(ars, a_voff2[mt], (uint32_t)stc(t) * 64u);
     };
-    u32x4 sv[R];     // scales of the lane's 8 columns, per ring slot
-    uint32_t zw[R];  // packed zeros of its word (ASYM), per ring slot
-    auto issue_sz = [&](int t, int slot) __attribute__((always_inline)) {
-        const uint32_t g = (uint32_t)(stc(t) / SPG);
-        sv[slot] = buffer_load_x4(srs, s_voff, g * (uint32_t)N * 2u);
-        if constexpr (ASYM) zw[slot] = buffer_load_x1(zrs, z_voff, g * row_bytes);
-    };
+    // Group scales and packed zeros of this K-wave's run, staged in LDS once
+    // (the K-wave's row waves share the loads): lane l of a wave takes the
+    // scale pair of columns 2 l, 2 l + 1 of the tile, lanes 0..15 the zero word.
+    {
+        const int ng = n_my / SPG, g0 = st0 / SPG;
+        for (int gi = wm; gi < ng; gi += WM) {
+            const uint32_t g = (uint32_t)(g0 + gi);
+            const uint32_t sw = buffer_load_x1(srs, (uint32_t)(tile_n * 128 + 2 * lane) * 2u, g * (uint32_t)N * 2u);
+            *reinterpret_cast<uint32_t *>(sl + (kw * GM + gi) * 128 + 2 * lane) = sw;
+            if constexpr (ASYM) {
+                if (lane < 16) zl[(kw * GM + gi) * 16 + lane] = buffer_load_x1(zrs, (uint32_t)(tile_n * 16 + lane) * 4u, g * row_bytes);
+            }
+        }
+    }
     // A operand of row tile mt: lane (j16, kq) takes row j16, k 8 kq .. from
     // lane 4 j16 + kq.
     const int a_src = (4 * j16 + kq) * 4;
@@ -185,13 +200,15 @@ __global__ __launch_bounds__(512) void mfma_shared_kernel(
     // ---- this wave's share of a step's dequantisation ----
     // Register j of every B operand o: (q - z) of rows 2j, 2j+1 of the lane's
     // slice at nibble o.
-    auto convert = [&](int slot, int buf) __attribute__((always_inline)) {
+    // t: the loop step converted (its group's zeros come from LDS)
+    auto convert = [&](int t, int slot, int buf) __attribute__((always_inline)) {
         f16x2 zc[8];
         if constexpr (ASYM) {
-            zc[0] = zero_pair_from_word<0>(zw[slot], nk); zc[1] = zero_pair_from_word<1>(zw[slot], nk);
-            zc[2] = zero_pair_from_word<2>(zw[slot], nk); zc[3] = zero_pair_from_word<3>(zw[slot], nk);
-            zc[4] = zero_pair_from_word<4>(zw[slot], nk); zc[5] = zero_pair_from_word<5>(zw[slot], nk);
-            zc[6] = zero_pair_from_word<6>(zw[slot], nk); zc[7] = zero_pair_from_word<7>(zw[slot], nk);
+            const uint32_t zw = zl[(kw * GM + min(t / SPG, GM - 1)) * 16 + j16];
+            zc[0] = zero_pair_from_word<0>(zw, nk); zc[1] = zero_pair_from_word<1>(zw, nk);
+            zc[2] = zero_pair_from_word<2>(zw, nk); zc[3] = zero_pair_from_word<3>(zw, nk);
+            zc[4] = zero_pair_from_word<4>(zw, nk); zc[5] = zero_pair_from_word<5>(zw, nk);
+            zc[6] = zero_pair_from_word<6>(zw, nk); zc[7] = zero_pair_from_word<7>(zw, nk);
         } else {
             zc[0] = zero_pair_const<0>(zp); zc[1] = zero_pair_const<1>(zp);
             zc[2] = zero_pair_const<2>(zp); zc[3] = zero_pair_const<3>(zp);
@@ -234,17 +251,16 @@ __global__ __launch_bounds__(512) void mfma_shared_kernel(
     // ---- prologue: steps 0 .. R-2 issued (in the loop's order, so that the
     // waits the compiler derives for the first iteration hold for all), step
     // 0 converted ----
+    __syncthreads();  // scales and zeros are in LDS
     static_for<0, R - 1>([&](auto tc) __attribute__((always_inline)) {
         constexpr int t = decltype(tc)::value;
         issue_b(t, t);
         asm volatile("" ::: "memory");
         issue_a(t, t);
         asm volatile("" ::: "memory");
-        issue_sz(t, t);
-        asm volatile("" ::: "memory");
     });
     permute_a(0, 0);
-    convert(0, 0);
+    convert(0, 0, 0);
     lds_barrier();  // step 0's operands are in the fragment buffer
 
     // ---- main loop: U steps per iteration, ring slots static; at least one
@@ -259,8 +275,6 @@ __global__ __launch_bounds__(512) void mfma_shared_kernel(
             issue_b(t + R - 1, (u + R - 1) % R);
             __builtin_amdgcn_sched_barrier(0);
             issue_a(t + R - 1, (u + R - 1) % R);
-            __builtin_amdgcn_sched_barrier(0);
-            issue_sz(t + R - 1, (u + R - 1) % R);
             __builtin_amdgcn_sched_barrier(0);
             // this step's operands (written before the last barrier)
             f16x8 bop[8];
@@ -285,10 +299,10 @@ __global__ __launch_bounds__(512) void mfma_shared_kernel(
             // the next step's activations and share of the conversion (into
             // the other fragment buffer)
             permute_a((u + 1) % R, (u + 1) & 1);
-            convert((u + 1) % R, (u + 1) & 1);
+            convert(t + 1, (u + 1) % R, (u + 1) & 1);
             if constexpr (u % SPG == SPG - 1) {
                 if (valid) {
-                    const u32x4 scl = sv[u % R];
+                    const u32x4 scl = *reinterpret_cast<const u32x4 *>(sl + (kw * GM + min(t / SPG, GM - 1)) * 128 + 8 * j16);
 #pragma unroll
                     for (int o = 0; o < 8; ++o) {
                         const float so = f16_bits_to_f32((scl[o >> 1] >> (16 * (o & 1))) & 0xffffu);
@@ -306,7 +320,7 @@ __global__ __launch_bounds__(512) void mfma_shared_kernel(
 
     // ---- K-wave reduction: K-waves 1.. write their totals, K-wave 0 sums in
     // order and stores (fp16, or fp32 partials with K-splits) ----
-    lds_barrier();  // fragment buffers are free
+    lds_barrier();  // fragment buffers, scales and zeros are free
     float *red = reinterpret_cast<float *>(smem);  // [(kw-1)][wm][slot 0..7][2 halves][64 lanes] f32x4
     auto red_at = [&](int k, int q, int h) __attribute__((always_inline)) {
         return reinterpret_cast<f32x4 *>(red) + ((((k - 1) * WM + wm) * 8 + q) * 2 + h) * 64 + lane;
@@ -320,14 +334,16 @@ __global__ __launch_bounds__(512) void mfma_shared_kernel(
         const int mt = q >> 2, v = q & 3;
         return f32x4{tot[mt][4][v], tot[mt][5][v], tot[mt][6][v], tot[mt][7][v]};
     };
-    if (kw > 0) {
+    if constexpr (WK > 1) {
+        if (kw > 0) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            *red_at(kw, q, 0) = slot_lo(q);
-            *red_at(kw, q, 1) = slot_hi(q);
+            for (int q = 0; q < 8; ++q) {
+                *red_at(kw, q, 0) = slot_lo(q);
+                *red_at(kw, q, 1) = slot_hi(q);
+            }
         }
+        lds_barrier();
     }
-    lds_barrier();
     const int tile = tile_m * tiles_n + tile_n;
     const uint32_t plane = (uint32_t)M * (uint32_t)N * 4u;
     const __amdgpu_buffer_rsrc_t prs = buffer_rsrc(partials, splits > 1 ? (uint32_t)splits * plane : 0u);
@@ -370,7 +386,7 @@ __global__ __launch_bounds__(512) void mfma_shared_kernel(
     // split order; per chunk of units every split's load is issued before the
     // first add.
     constexpr int kRows = 32 * WM, kRowUnits = 128 / 4;  // f32x4 units per tile row
-    constexpr int kUnits = kRows * kRowUnits / 512, kChunk = 4;
+    constexpr int kUnits = kRows * kRowUnits / NT, kChunk = kUnits < 4 ? kUnits : 4;
     static_assert(kUnits % kChunk == 0, "whole chunks");
     const int row0 = tile_m * kRows, col0 = tile_n * 128;
     typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
@@ -379,7 +395,7 @@ __global__ __launch_bounds__(512) void mfma_shared_kernel(
         f32x4 v[kChunk][kSharedMaxSplits];
 #pragma unroll
         for (int u = 0; u < kChunk; ++u) {
-            const int idx = threadIdx.x + (u0 + u) * 512;
+            const int idx = threadIdx.x + (u0 + u) * NT;
             const int row = row0 + idx / kRowUnits;
             const int col = col0 + 4 * (idx % kRowUnits);
             const bool ok = row < M && col < N;
@@ -391,7 +407,7 @@ __global__ __launch_bounds__(512) void mfma_shared_kernel(
         }
 #pragma unroll
         for (int u = 0; u < kChunk; ++u) {
-            const int idx = threadIdx.x + (u0 + u) * 512;
+            const int idx = threadIdx.x + (u0 + u) * NT;
             const int row = row0 + idx / kRowUnits;
             const int col = col0 + 4 * (idx % kRowUnits);
             if (row >= M || col >= N) continue;
@@ -408,28 +424,29 @@ __global__ __launch_bounds__(512) void mfma_shared_kernel(
     if (threadIdx.x == 0) reset_counter_agent(&counters[tile]);
 }
 
-template <int WM, int SPG>
+template <int WM, int WK, int SPG>
 hipError_t launch_shared_spg(const GemmArgs &g, const GemmPlan &p, hipStream_t stream) {
+    constexpr int NT = SharedCfg<WM, WK>::kThreads;
     if (g.qzeros)
-        hipLaunchKernelGGL((mfma_shared_kernel<WM, SPG, true>), dim3((unsigned)p.grid), dim3(512), 0, stream, g.a,
+        hipLaunchKernelGGL((mfma_shared_kernel<WM, WK, SPG, true>), dim3((unsigned)p.grid), dim3(NT), 0, stream, g.a,
                            reinterpret_cast<const uint32_t *>(g.b), g.scales, reinterpret_cast<const uint32_t *>(g.qzeros),
                            (int)g.M, (int)g.K, (int)g.N, (int)g.G, (uint32_t)g.zp, (int)p.tiles_n, (int)p.tiles_m,
                            p.m_group, (int)p.split_len, p.splits, g.out, g.partials, g.counters);
     else
-        hipLaunchKernelGGL((mfma_shared_kernel<WM, SPG, false>), dim3((unsigned)p.grid), dim3(512), 0, stream, g.a,
+        hipLaunchKernelGGL((mfma_shared_kernel<WM, WK, SPG, false>), dim3((unsigned)p.grid), dim3(NT), 0, stream, g.a,
                            reinterpret_cast<const uint32_t *>(g.b), g.scales, reinterpret_cast<const uint32_t *>(g.qzeros),
                            (int)g.M, (int)g.K, (int)g.N, (int)g.G, (uint32_t)g.zp, (int)p.tiles_n, (int)p.tiles_m,
                            p.m_group, (int)p.split_len, p.splits, g.out, g.partials, g.counters);
     return hipGetLastError();
 }
 
-template <int WM>
+template <int WM, int WK>
 hipError_t launch_shared_wm(const GemmArgs &g, const GemmPlan &p, hipStream_t stream) {
     switch (g.G / 32) {
-        case 1: return launch_shared_spg<WM, 1>(g, p, stream);
-        case 2: return launch_shared_spg<WM, 2>(g, p, stream);
-        case 4: return launch_shared_spg<WM, 4>(g, p, stream);
-        case 8: return launch_shared_spg<WM, 8>(g, p, stream);
+        case 1: return launch_shared_spg<WM, WK, 1>(g, p, stream);
+        case 2: return launch_shared_spg<WM, WK, 2>(g, p, stream);
+        case 4: return launch_shared_spg<WM, WK, 4>(g, p, stream);
+        case 8: return launch_shared_spg<WM, WK, 8>(g, p, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -437,12 +454,19 @@ hipError_t launch_shared_wm(const GemmArgs &g, const GemmPlan &p, hipStream_t st
 }  // namespace
 
 
+inline int64_t cdiv_groups(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
 hipError_t launch_mfma_shared(const GemmArgs &g, const GemmPlan &p, hipStream_t stream) {
     if (p.splits > 1 && (!g.partials || !g.counters)) return hipErrorInvalidValue;
     if (!shared_supports(g.G) || p.split_len % (g.G / 32) != 0 || p.splits > kSharedMaxSplits)
         return hipErrorInvalidValue;
-    if (p.wm == 4) return launch_shared_wm<4>(g, p, stream);
-    if (p.wm == 2) return launch_shared_wm<2>(g, p, stream);
+    // every K-wave's run of groups fits its LDS scale slots
+    const int64_t spg = g.G / 32, groups = p.split_len / spg;
+    if (p.kwaves < 1 || cdiv_groups(groups, p.kwaves) > kSharedGroupSlots / p.kwaves) return hipErrorInvalidValue;
+    if (p.wm == 4 && p.kwaves == 2) return launch_shared_wm<4, 2>(g, p, stream);
+    if (p.wm == 2 && p.kwaves == 4) return launch_shared_wm<2, 4>(g, p, stream);
+    if (p.wm == 4 && p.kwaves == 1) return launch_shared_wm<4, 1>(g, p, stream);
+    if (p.wm == 2 && p.kwaves == 1) return launch_shared_wm<2, 1>(g, p, stream);
     return hipErrorInvalidValue;
 }
 

@@ -83,10 +83,12 @@ hipError_t launch_gemv_act(const GemmArgs &args, const GemmPlan &plan, int act, 
 // Runs the LDS-shared kernel (gemm_shared.hip) when plan.wm is set.
 hipError_t launch_mfma(const GemmArgs &args, const GemmPlan &plan, hipStream_t stream);
 // MFMA GEMM whose row waves share each step's dequantised weights through LDS
-// (plan.wm = 2 or 4 row waves of 32 rows, 8 / wm K-waves, 128-column tiles).
-// G must be 32, 64, 128 or 256, split_len whole groups, at most
-// kSharedMaxSplits K-splits.
+// (plan.wm = 2 or 4 row waves of 32 rows, plan.kwaves = 8 / wm K-waves or 1,
+// 128-column tiles).  G must be 32, 64, 128 or 256, split_len whole groups,
+// at most kSharedGroupSlots / kwaves groups per K-wave (each K-wave's group
+// scales and zeros are staged in LDS) and kSharedMaxSplits K-splits.
 constexpr int kSharedMaxSplits = 8;
+constexpr int kSharedGroupSlots = 128;
 inline bool shared_supports(int64_t G) { return G == 32 || G == 64 || G == 128 || G == 256; }
 hipError_t launch_mfma_shared(const GemmArgs &args, const GemmPlan &plan, hipStream_t stream);
 // MFMA GEMM on A = `a` with row stride lda (>= K); with rn, the decode step's
