@@ -116,9 +116,12 @@ int w4a16_repack_scales(const uint16_t *src_ng, uint16_t *dst_gn, int64_t Gn, in
  * tuning key gemv_mma_exact=0 and a symmetric zero point, on biased weights
  * 1024 + q or 64 + q with the zero term removed per 32-row chunk by the same
  * MFMA chain); the tuning key gemv_mma=0 selects the same GEMV with
- * v_dot2_f32_f16 on the vector ALUs.  M >= 9 runs an MFMA
- * GEMM that dequantises the weights in registers to exact (q - z) fp16
- * operands and applies each group's scale to the fp32 sums of that group.
+ * v_dot2_f32_f16 on the vector ALUs.  M >= 9 runs an MFMA GEMM on exact
+ * (q - z) fp16 operands that applies each group's scale to the fp32 sums of
+ * that group: up to M = 128 each wave dequantises its own operands in
+ * registers; from M = 129 (tuning key mfma_shared_m) the waves that cover
+ * different rows share each K-step's dequantised weights through LDS, each
+ * weight converted once per workgroup.
  * Accumulation is fp32 throughout.  K-splits across workgroups meet in
  * fixed point (GEMV) or in split order (MFMA GEMM), so the result is
  * deterministic for a given shape and plan.
@@ -298,7 +301,10 @@ int w4a16_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t G, int32_t *path,
  * row-norm runs as a kernel of its own instead of inside the down GEMV),
  * decode_rn_mfma (1: the MFMA GEMMs of M >= 9 fold the row-norm, applying the
  * row scale to the products, instead of reading the row-norm kernel's fp16
- * output).  Every
+ * output), mfma_shared_m (the M from which the LDS-shared MFMA GEMM runs,
+ * default 129; 0: never), mfma_wm (its row waves per workgroup, 2 or 4; 0:
+ * 4 above 64 rows), mfma_shared_kw (1: one K-wave per workgroup, one wave
+ * per SIMD with a deeper load ring).  Every
  * choice computes the same product; they differ in speed and in fp32
  * rounding.  Unknown keys or malformed values: W4A16_ERR_INVALID_ARG and the
  * current settings stay.  Affects calls planned after it returns; not

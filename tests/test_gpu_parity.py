@@ -50,7 +50,9 @@ def check_close(got, want, what="", tol=TOL):
     bound = tol * np.maximum(1.0, np.abs(r))
     worst = np.unravel_index(np.argmax(err / bound), err.shape) if err.size else None
     ulp = np.abs(got.view(np.uint16).astype(np.int64) - want.view(np.uint16).astype(np.int64))
-    note("%s max|err|=%.3g max ulp=%d" % (what, err.max() if err.size else 0, ulp.max() if ulp.size else 0))
+    note("%s max|err|=%.3g max err/bound=%.3g max ulp=%d" % (what, err.max() if err.size else 0,
+                                                            (err / bound).max() if err.size else 0,
+                                                            ulp.max() if ulp.size else 0))
     assert np.all(err <= bound), "%s: worst at %s got %r want %r" % (what, worst, g[worst], r[worst])
 
 
