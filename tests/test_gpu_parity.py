@@ -141,7 +141,8 @@ TUNED_FORMS = ["gemv_mma=0", "gemv_mma=0,gemv_fold=0", "gemv_mma=0,gemv_fold=1",
                "mfma_mgroup=1", "mfma_mgroup=2",
                "mfma_cfg=3,mfma_mgroup=3", "mfma_cfg=1,mfma_mgroup=4,mfma_splits=2",
                "mfma_shared_m=0", "mfma_shared_m=0,mfma_cfg=2", "mfma_shared_m=9", "mfma_shared_m=9,mfma_wm=4",
-               "mfma_shared_m=9,mfma_splits=2", "mfma_wm=2,mfma_mgroup=2", "mfma_wm=4,mfma_mgroup=1"]
+               "mfma_shared_m=9,mfma_splits=2", "mfma_wm=2,mfma_mgroup=2", "mfma_wm=4,mfma_mgroup=1",
+               "mfma_tile_m=9", "mfma_tile_m=9,mfma_splits=3"]
 
 
 @pytest.mark.parametrize("spec", TUNED_FORMS)
@@ -173,15 +174,18 @@ SHARED_CASES = [(64, 4096, 1000, 32, True), (129, 4096, 1000, 64, False), (256, 
 SHARED_FORMS = ["", "mfma_wm=2", "mfma_wm=4", "mfma_splits=1", "mfma_splits=3", "mfma_splits=8",
                 "mfma_wm=4,mfma_splits=7,mfma_mgroup=1", "mfma_wm=2,mfma_splits=5,mfma_mgroup=3",
                 "mfma_shared_kw=1", "mfma_shared_kw=1,mfma_wm=2", "mfma_shared_kw=1,mfma_splits=3",
-                "mfma_shared_kw=1,mfma_wm=2,mfma_splits=8,mfma_mgroup=2"]
+                "mfma_shared_kw=1,mfma_wm=2,mfma_splits=8,mfma_mgroup=2",
+                "mfma_tile_m=1", "mfma_tile_m=1,mfma_splits=1", "mfma_tile_m=1,mfma_splits=3",
+                "mfma_tile_m=1,mfma_splits=8,mfma_mgroup=2"]
 
 
 @pytest.mark.parametrize("M,K,N,G,asym", SHARED_CASES)
 def test_gemm_shared_kernel_matches_oracle(M, K, N, G, asym):
-    """The MFMA kernel whose row waves share each step's dequantised weights
-    through LDS, in both row-wave shapes, at every group size it takes, with
-    ragged rows and column tiles, K-waves of unequal group counts and forced
-    K-split counts (one to eight, uneven)."""
+    """The MFMA kernels that share dequantised weights through LDS: the
+    row-wave kernel in both row-wave shapes and its single-K-wave form, and the
+    128 x 256 kernel that also shares the activations, at every group size they
+    take, with ragged rows and column tiles, K-waves of unequal group counts
+    and forced K-split counts (one to eight, uneven)."""
     p = synth.problem(M, K, N, G, asym, seed=900 + M + K + N)
     want = oracle_gemm_columns(p["a"], p["b_packed"], p["scales"], p["qzeros"], G, 8)
     for spec in SHARED_FORMS:
@@ -191,6 +195,28 @@ def test_gemm_shared_kernel_matches_oracle(M, K, N, G, asym):
         assert path == 2
         got = tuned(full, lambda: run_gemm(p))
         check_close(got, want, "shared %s M=%d" % (full, M))
+
+
+@pytest.mark.parametrize("spec", ["mfma_shared_m=0,mfma_splits=2", "mfma_shared_m=1,mfma_splits=2",
+                                  "mfma_shared_m=1,mfma_wm=2,mfma_splits=4", "mfma_tile_m=1,mfma_splits=2",
+                                  "mfma_tile_m=1,mfma_splits=8"])
+def test_gemm_split_partials_repeated(spec):
+    """The MFMA kernels' fp32 split partials, ten calls in a row on one
+    problem: every call matches the oracle and the first bit for bit.  (A
+    partial's wide store once let the next value written into its data
+    registers reach memory instead, in some calls only: one split's column c
+    summed with its column c + 4.)"""
+    M, K, N, G = 128, 1024, 512, 128
+    p = synth.problem(M, K, N, G, True, seed=515)
+    want = oracle.gemm(p["a"], p["b_packed"], p["scales"], p["qzeros"], G, 8)
+    a, b, s, z = dev(p["a"]), dev(p["b_packed"]), dev(p["scales"]), dev(p["qzeros"])
+    path, splits, grid = tuned(spec, lambda: w4.w4a16_gemm_plan(M, K, N, G))
+    note("partials %s path=%d splits=%d grid=%d" % (spec, path, splits, grid))
+    assert splits > 1
+    outs = tuned(spec, lambda: [host(w4.w4a16_gemm(a, b, s, z, G, 8)) for _ in range(10)])
+    for i, o in enumerate(outs):
+        check_close(o, want, "%s call %d" % (spec, i))
+        assert np.array_equal(o.view(np.uint16), outs[0].view(np.uint16)), "call %d differs" % i
 
 
 @pytest.mark.parametrize("M", [1, 4, 8, 16, 32, 256])
@@ -260,7 +286,8 @@ def same_fp16(got, want):
     return np.array_equal(gn, rn) and np.array_equal(g[~gn], r[~rn])
 
 
-NONFINITE_FORMS = ["", "gemv_mma_exact=0", "gemv_mma=0,gemv_fold=0", "gemv_max_m=0", "gemv_max_m=0,mfma_shared_m=1"]
+NONFINITE_FORMS = ["", "gemv_mma_exact=0", "gemv_mma=0,gemv_fold=0", "gemv_max_m=0", "gemv_max_m=0,mfma_shared_m=1",
+                   "gemv_max_m=0,mfma_tile_m=1"]
 
 
 @pytest.mark.parametrize("spec", NONFINITE_FORMS)

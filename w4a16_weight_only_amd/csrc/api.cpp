@@ -76,6 +76,8 @@ struct Tune {
                                        // against 39.8) and the two agree at M = 256 (62.5 us)
     int64_t mfma_wm = 0;               // force its row waves (2 or 4; 0: 4 above 64 rows, else 2)
     int64_t mfma_shared_kw = 0;        // its K-waves: 1 (one wave per SIMD, deeper load ring), else 8 / wm
+    int64_t mfma_tile_m = 0;           // from this M on, the 128 x 256 kernel sharing activations and
+                                       // weights through LDS (0: never)
 };
 
 // Returns false on an unknown key or a malformed entry (nothing applied).
@@ -106,6 +108,7 @@ bool parse_tune(const char *spec, Tune *out) {
         else if (k == "mfma_shared_m") v.mfma_shared_m = val;
         else if (k == "mfma_wm") v.mfma_wm = val;
         else if (k == "mfma_shared_kw") v.mfma_shared_kw = val;
+        else if (k == "mfma_tile_m") v.mfma_tile_m = val;
 
         else if (k == "mfma_target_waves") v.mfma_target_waves = val;
         else if (k == "mfma_splits") v.mfma_splits = val;
@@ -297,8 +300,32 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma, b
         // (the shared kernel stages at most kSharedGroupSlots groups per split)
         const bool shared = allow_shared && t.mfma_shared_m > 0 && M >= t.mfma_shared_m && shared_supports(G) &&
                             cdiv(K / G, kSharedMaxSplits) <= kSharedGroupSlots;
+        const bool wide = allow_shared && t.mfma_tile_m > 0 && M >= t.mfma_tile_m && shared_supports(G) &&
+                          cdiv(K / G, kSharedMaxSplits) <= kTileGroupSlots;
+        // The 128 x 256 kernel: one K stream per workgroup, K-splits to about
+        // one workgroup per CU, at most kTileGroupSlots groups per split.
+        auto fill_tile = [&]() {
+            p.wide = true;
+            p.wm = 0;
+            p.mt = 2;
+            p.waves = 2;
+            p.kwaves = 1;
+            p.tiles_n = cdiv(N8, 32);
+            p.tiles_m = cdiv(M, 128);
+            const int64_t spg = G / 32, ngroups = K / G;
+            const int64_t tiles = p.tiles_n * p.tiles_m;
+            int64_t splits = t.mfma_splits > 0 ? t.mfma_splits : std::max<int64_t>(1, 256 / tiles);
+            splits = std::min<int64_t>(splits, ngroups);
+            splits = std::min<int64_t>(splits, std::max<int64_t>(1, cap / std::max<int64_t>(1, M * N * 4)));
+            splits = std::max<int64_t>(splits, cdiv(ngroups, kTileGroupSlots));
+            splits = std::max<int64_t>(1, std::min<int64_t>(splits, kSharedMaxSplits));
+            p.split_len = cdiv(ngroups, splits) * spg;
+            p.splits = (int)cdiv(K / 32, p.split_len);
+        };
         static const int kCfg[3][3] = {{1, 2, 4}, {2, 2, 4}, {2, 1, 8}};
-        if (shared) {
+        if (wide) {
+            fill_tile();
+        } else if (shared) {
             fill_shared(t.mfma_wm == 2 || t.mfma_wm == 4 ? (int)t.mfma_wm : (M > 64 ? 4 : 2));
         } else if (t.mfma_cfg >= 1 && t.mfma_cfg <= 3) {
             fill(kCfg[t.mfma_cfg - 1][0], kCfg[t.mfma_cfg - 1][1], kCfg[t.mfma_cfg - 1][2]);
@@ -351,7 +378,7 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma, b
         const int64_t krows = p.split_len * 32;
         const int64_t cols = 16 * 8 * (int64_t)p.waves;
         const double wcol = (double)krows * (double)cols * 0.5 + (double)(krows / G) * (double)cols * 2.5;
-        const double arow = (double)(p.wm ? 32 * p.wm : 16 * p.mt) * (double)krows * 2.0;
+        const double arow = (double)(p.wide ? 128 : p.wm ? 32 * p.wm : 16 * p.mt) * (double)krows * 2.0;
         const int64_t resident = std::max<int64_t>(1, std::min<int64_t>(32, cdiv(p.tiles_n * p.tiles_m * p.splits, 8)));
         int64_t gbest = 1;
         double cbest = -1;

@@ -36,6 +36,7 @@
 // them in split order (deterministic), writes fp16 and resets the counter.
 #include "device.h"
 #include "kernels.h"
+#include "store.h"
 
 #include <type_traits>
 
@@ -406,8 +407,8 @@ __global__ __launch_bounds__(64 * NWN * NWK) void mfma_kernel(
             *reinterpret_cast<f16x8_t *>(out + (size_t)row * N + word * 8) = o;
         } else {
             const uint32_t off = ((uint32_t)row * (uint32_t)N + (uint32_t)word * 8u) * 4u;
-            buffer_store_f32x4_sc1(lo, prs, off, (uint32_t)split * plane);
-            buffer_store_f32x4_sc1(hi, prs, off + 16u, (uint32_t)split * plane);
+            store_partial_x4(lo, prs, off, (uint32_t)split * plane);
+            store_partial_x4(hi, prs, off + 16u, (uint32_t)split * plane);
         }
     };
     auto slot_lo = [&](int mt, int v) __attribute__((always_inline)) {
@@ -576,7 +577,7 @@ int mfma_max_splits(int mt, int waves, int kwaves) {
 
 hipError_t launch_mfma_rn(const GemmArgs &g, const GemmPlan &p, bool rn, const uint16_t *a, int64_t lda,
                           hipStream_t stream) {
-    if (p.wm != 0) return hipErrorInvalidValue;  // a plan of the LDS-shared kernel
+    if (p.wm != 0 || p.wide) return hipErrorInvalidValue;  // a plan of an LDS-sharing kernel
     // (MT, NWN, NWK) combinations the planner emits.
     if (p.mt == 1 && p.waves == 2 && p.kwaves == 4) return launch_cfg<1, 2, 4>(g, p, rn, a, lda, stream);
     if (p.mt == 2 && p.waves == 2 && p.kwaves == 4) return launch_cfg<2, 2, 4>(g, p, rn, a, lda, stream);
@@ -585,6 +586,7 @@ hipError_t launch_mfma_rn(const GemmArgs &g, const GemmPlan &p, bool rn, const u
 }
 
 hipError_t launch_mfma(const GemmArgs &g, const GemmPlan &p, hipStream_t stream) {
+    if (p.wide) return launch_mfma_tile(g, p, stream);
     if (p.wm != 0) return launch_mfma_shared(g, p, stream);
     return launch_mfma_rn(g, p, false, g.a, g.K, stream);
 }

@@ -29,6 +29,7 @@
 // last arriving workgroup sums them), as in gemm_mfma.hip.
 #include "device.h"
 #include "kernels.h"
+#include "store.h"
 
 namespace w4a16 {
 namespace {
@@ -162,14 +163,26 @@ __global__ __launch_bounds__(64 * WM * WK) void mfma_shared_kernel(
     // Group scales and packed zeros of this K-wave's run, staged in LDS once
     // (the K-wave's row waves share the loads): lane l of a wave takes the
     // scale pair of columns 2 l, 2 l + 1 of the tile, lanes 0..15 the zero word.
+    // (every load issued before the first store: one round trip)
     {
         const int ng = n_my / SPG, g0 = st0 / SPG;
-        for (int gi = wm; gi < ng; gi += WM) {
-            const uint32_t g = (uint32_t)(g0 + gi);
-            const uint32_t sw = buffer_load_x1(srs, (uint32_t)(tile_n * 128 + 2 * lane) * 2u, g * (uint32_t)N * 2u);
-            *reinterpret_cast<uint32_t *>(sl + (kw * GM + gi) * 128 + 2 * lane) = sw;
-            if constexpr (ASYM) {
-                if (lane < 16) zl[(kw * GM + gi) * 16 + lane] = buffer_load_x1(zrs, (uint32_t)(tile_n * 16 + lane) * 4u, g * row_bytes);
+        constexpr int kPer = GM / WM;
+        uint32_t sw[kPer], zw0[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int gi = wm + WM * i;
+            const uint32_t g = (uint32_t)(g0 + min(gi, max(ng - 1, 0)));
+            sw[i] = buffer_load_x1(srs, (uint32_t)(tile_n * 128 + 2 * lane) * 2u, g * (uint32_t)N * 2u);
+            if constexpr (ASYM) zw0[i] = buffer_load_x1(zrs, (uint32_t)(tile_n * 16 + (lane & 15)) * 4u, g * row_bytes);
+        }
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int gi = wm + WM * i;
+            if (gi < ng) {
+                *reinterpret_cast<uint32_t *>(sl + (kw * GM + gi) * 128 + 2 * lane) = sw[i];
+                if constexpr (ASYM) {
+                    if (lane < 16) zl[(kw * GM + gi) * 16 + lane] = zw0[i];
+                }
             }
         }
     }
@@ -366,8 +379,8 @@ __global__ __launch_bounds__(64 * WM * WK) void mfma_shared_kernel(
                     *reinterpret_cast<f16x8_t *>(out + (size_t)row * N + word * 8) = o;
                 } else {
                     const uint32_t off = ((uint32_t)row * (uint32_t)N + (uint32_t)word * 8u) * 4u;
-                    buffer_store_f32x4_sc1(lo, prs, off, (uint32_t)split * plane);
-                    buffer_store_f32x4_sc1(hi, prs, off + 16u, (uint32_t)split * plane);
+                    store_partial_x4(lo, prs, off, (uint32_t)split * plane);
+                    store_partial_x4(hi, prs, off + 16u, (uint32_t)split * plane);
                 }
             }
         }

@@ -27,6 +27,8 @@ struct GemmPlan {
     int waves = 4;
     int mt = 1;
     int kwaves = 1;           // MFMA: waves dividing a workgroup's K range (LDS-reduced)
+    bool wide = false;        // MFMA: the 128 x 256 kernel sharing activations and weights
+                              // through LDS (gemm_tile.hip)
     int wm = 0;               // MFMA: row waves sharing each step's dequantised weights through
                               // LDS (2 or 4; mt = 2, waves = 1, kwaves = 8 / wm); 0: the
                               // register-direct kernel
@@ -91,6 +93,12 @@ constexpr int kSharedMaxSplits = 8;
 constexpr int kSharedGroupSlots = 128;
 inline bool shared_supports(int64_t G) { return G == 32 || G == 64 || G == 128 || G == 256; }
 hipError_t launch_mfma_shared(const GemmArgs &args, const GemmPlan &plan, hipStream_t stream);
+// MFMA GEMM on 128-row x 256-column workgroup tiles whose activations and
+// dequantised weights are both shared through LDS (gemm_tile.hip; plan.wide).
+// G must be 32, 64, 128 or 256, split_len whole groups, at most
+// kTileGroupSlots groups per split and kSharedMaxSplits K-splits.
+constexpr int kTileGroupSlots = 64;
+hipError_t launch_mfma_tile(const GemmArgs &args, const GemmPlan &plan, hipStream_t stream);
 // MFMA GEMM on A = `a` with row stride lda (>= K); with rn, the decode step's
 // row-norm folded in: out = (a . W) * inv_row, inv_row = 1/sqrt(mean(a_row^2)
 // + 1e-6) over the row's K values, applied to the products (the partials
