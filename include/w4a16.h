@@ -304,7 +304,9 @@ int w4a16_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t G, int32_t *path,
  * output), mfma_shared_m (the M from which the LDS-shared MFMA GEMM runs,
  * default 129; 0: never), mfma_wm (its row waves per workgroup, 2 or 4; 0:
  * 4 above 64 rows), mfma_shared_kw (1: one K-wave per workgroup, one wave
- * per SIMD with a deeper load ring).  Every
+ * per SIMD with a deeper load ring), mfma_tile_m (the M from which a
+ * 128-row x 256-column workgroup tile runs that also stages the activations
+ * in LDS; default 0: never; groups of at most 64 per K-split).  Every
  * choice computes the same product; they differ in speed and in fp32
  * rounding.  Unknown keys or malformed values: W4A16_ERR_INVALID_ARG and the
  * current settings stay.  Affects calls planned after it returns; not
