@@ -447,8 +447,8 @@ def main():
                          % ",".join(EXTRA_ROWS))
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the W4A16 linear "
-              "shards column- or row-wise with one all-reduce; see the design notes). Run with --gpus 1.",
+        print("bench.py measures one GPU: the library has no multi-GPU path (the W4A16 linear "
+              "would shard column- or row-wise with one all-reduce). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
