@@ -118,10 +118,12 @@ int w4a16_repack_scales(const uint16_t *src_ng, uint16_t *dst_gn, int64_t Gn, in
  * MFMA chain); the tuning key gemv_mma=0 selects the same GEMV with
  * v_dot2_f32_f16 on the vector ALUs.  M >= 9 runs an MFMA GEMM on exact
  * (q - z) fp16 operands that applies each group's scale to the fp32 sums of
- * that group: up to M = 128 each wave dequantises its own operands in
- * registers; from M = 129 (tuning key mfma_shared_m) the waves that cover
- * different rows share each K-step's dequantised weights through LDS, each
- * weight converted once per workgroup.
+ * that group: below M = 192 each wave dequantises its own operands in
+ * registers for 32 rows; from M = 192 (tuning key mfma_tall_m) a workgroup
+ * owns 128 rows x 128 columns, each wave converts the weights of one
+ * 32-column strip once for all 128 rows, and the activations are staged in
+ * LDS once per workgroup.  (A third form, tuning key mfma_shared_m, shares
+ * each K-step's dequantised weights between row waves through LDS.)
  * Accumulation is fp32 throughout.  K-splits across workgroups meet in
  * fixed point (GEMV) or in split order (MFMA GEMM), so the result is
  * deterministic for a given shape and plan.
@@ -301,8 +303,11 @@ int w4a16_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t G, int32_t *path,
  * row-norm runs as a kernel of its own instead of inside the down GEMV),
  * decode_rn_mfma (1: the MFMA GEMMs of M >= 9 fold the row-norm, applying the
  * row scale to the products, instead of reading the row-norm kernel's fp16
- * output), mfma_shared_m (the M from which the LDS-shared MFMA GEMM runs,
- * default 129; 0: never), mfma_wm (its row waves per workgroup, 2 or 4; 0:
+ * output), mfma_tall_m (the M from which the 128 x 128 MFMA GEMM whose waves
+ * each convert a 32-column strip runs, default 192; 0: never; at most 8
+ * K-splits), mfma_shared_m (the M from which the MFMA GEMM sharing
+ * dequantised weights between row waves through LDS runs, default 0:
+ * never), mfma_wm (its row waves per workgroup, 2 or 4; 0:
  * 4 above 64 rows), mfma_shared_kw (1: one K-wave per workgroup, one wave
  * per SIMD with a deeper load ring), mfma_tile_m (the M from which a
  * 128-row x 256-column workgroup tile runs that also stages the activations

@@ -142,7 +142,7 @@ TUNED_FORMS = ["gemv_mma=0", "gemv_mma=0,gemv_fold=0", "gemv_mma=0,gemv_fold=1",
                "mfma_cfg=3,mfma_mgroup=3", "mfma_cfg=1,mfma_mgroup=4,mfma_splits=2",
                "mfma_shared_m=0", "mfma_shared_m=0,mfma_cfg=2", "mfma_shared_m=9", "mfma_shared_m=9,mfma_wm=4",
                "mfma_shared_m=9,mfma_splits=2", "mfma_wm=2,mfma_mgroup=2", "mfma_wm=4,mfma_mgroup=1",
-               "mfma_tile_m=9", "mfma_tile_m=9,mfma_splits=3"]
+               "mfma_tile_m=9", "mfma_tile_m=9,mfma_splits=3", "mfma_tall_m=9", "mfma_tall_m=9,mfma_splits=5"]
 
 
 @pytest.mark.parametrize("spec", TUNED_FORMS)
@@ -197,7 +197,32 @@ def test_gemm_shared_kernel_matches_oracle(M, K, N, G, asym):
         check_close(got, want, "shared %s M=%d" % (full, M))
 
 
+TALL_CASES = [(129, 4096, 1024, 64, False), (256, 4096, 1056, 128, True), (256, 12800, 512, 128, True),
+              (200, 3072, 544, 256, True), (130, 1024, 320, 32, False), (384, 1056, 288, 96, True),
+              (96, 12800, 256, 32, True), (17, 544, 64, 32, False)]
+TALL_FORMS = ["", "mfma_splits=1", "mfma_splits=2", "mfma_splits=3", "mfma_splits=8"]
+
+
+@pytest.mark.parametrize("M,K,N,G,asym", TALL_CASES)
+def test_gemm_tall_kernel_matches_oracle(M, K, N, G, asym):
+    """The MFMA kernel whose waves convert a 32-column strip of weights for
+    all 128 rows of the workgroup tile (activations staged in LDS): ragged row
+    tiles (rows past M), ragged column tiles (words past N), group sizes from
+    32 to 256 and one (96) that does not divide the two-step LDS stages, odd
+    step counts per split, and K-split counts from one to eight."""
+    p = synth.problem(M, K, N, G, asym, seed=700 + M + K + N)
+    want = oracle_gemm_columns(p["a"], p["b_packed"], p["scales"], p["qzeros"], G, 8)
+    for spec in TALL_FORMS:
+        full = "mfma_tall_m=1," + spec if spec else "mfma_tall_m=1"
+        path, splits, grid = tuned(full, lambda: w4.w4a16_gemm_plan(M, K, N, G))
+        note("tall %s M=%d K=%d N=%d G=%d path=%d splits=%d grid=%d" % (full, M, K, N, G, path, splits, grid))
+        assert path == 2
+        got = tuned(full, lambda: run_gemm(p))
+        check_close(got, want, "tall %s M=%d" % (full, M))
+
+
 @pytest.mark.parametrize("spec", ["mfma_shared_m=0,mfma_splits=2", "mfma_shared_m=1,mfma_splits=2",
+                                  "mfma_tall_m=1,mfma_splits=2", "mfma_tall_m=1,mfma_splits=8",
                                   "mfma_shared_m=1,mfma_wm=2,mfma_splits=4", "mfma_tile_m=1,mfma_splits=2",
                                   "mfma_tile_m=1,mfma_splits=8"])
 def test_gemm_split_partials_repeated(spec):

@@ -47,7 +47,8 @@ def inputs(M, K, N, G, asym, seed):
 PAIRS = [((1, 4096, 12800, 128, False), (1, 1024, 2048, 128, False)),
          ((32, 4096, 12800, 128, True), (20, 2048, 4096, 128, True)),
          ((8, 4096, 6144, 128, True), (3, 512, 1024, 64, False)),
-         ((64, 4096, 4096, 128, False), (2, 2048, 1024, 128, True))]
+         ((64, 4096, 4096, 128, False), (2, 2048, 1024, 128, True)),
+         ((256, 2048, 1024, 128, True), (200, 1024, 512, 64, False))]  # the 128 x 128 strip kernel
 
 
 @pytest.mark.parametrize("first,second", PAIRS)

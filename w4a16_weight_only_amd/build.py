@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libw4a16.so")
-SOURCES = ["api.cpp", "gemv.hip", "gemm_mfma.hip", "gemm_shared.hip", "gemm_tile.hip", "repack.hip", "glue.hip", "noalloc.hip"]
+SOURCES = ["api.cpp", "gemv.hip", "gemm_mfma.hip", "gemm_shared.hip", "gemm_tile.hip", "gemm_tall.hip", "repack.hip", "glue.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -69,15 +69,22 @@ struct Tune {
     int64_t decode_fuse = 1;           // 0: decode-step glue as separate kernels
     int64_t decode_swiglu_m = 3;       // GEMV route: from this M on, SwiGLU + row-norm as a kernel of its own
     int64_t decode_rn_mfma = 0;        // 1: the MFMA GEMMs fold the row-norm (no fp16 rounding of rn(x))
-    int64_t mfma_shared_m = 129;       // from this M on, the MFMA kernel sharing dequantised weights
-                                       // through LDS (0: never); measured on MI355X the
-                                       // register-direct kernel is faster up to M = 128 (M = 64
-                                       // K = 4096 N = 12800: 23.5 against 26.6 us; M = 128: 37.9
-                                       // against 39.8) and the two agree at M = 256 (62.5 us)
+    int64_t mfma_shared_m = 0;         // from this M on, the MFMA kernel sharing dequantised weights
+                                       // through LDS (0: never); measured on MI355X it loses to the
+                                       // register-direct kernel up to M = 160 (M = 160 K = 12800
+                                       // N = 4096: 62.1 against 47.1 us) and to the 128 x 128
+                                       // strip kernel from M = 192 on, so it is a tuning form
     int64_t mfma_wm = 0;               // force its row waves (2 or 4; 0: 4 above 64 rows, else 2)
     int64_t mfma_shared_kw = 0;        // its K-waves: 1 (one wave per SIMD, deeper load ring), else 8 / wm
     int64_t mfma_tile_m = 0;           // from this M on, the 128 x 256 kernel sharing activations and
                                        // weights through LDS (0: never)
+    int64_t mfma_tall_m = 192;         // from this M on, the 128 x 128 kernel whose waves each convert
+                                       // a 32-column strip for all 128 rows (0: never); measured on
+                                       // MI355X (K = 12800 N = 4096 / K = 4096 N = 12800, best other
+                                       // kernel in brackets): M = 160 57.5 (47.1) / 59.6 (40.0) us,
+                                       // M = 192 57.0 (58.6) / 58.5 (59.0), M = 256 60.0 (62.2) /
+                                       // 61.2 (62.8), M = 512 90.4 (108.5) / 89.7 (118.0), M = 1024
+                                       // 150.5 (175.9) / 172.8 (226.4)
 };
 
 // Returns false on an unknown key or a malformed entry (nothing applied).
@@ -109,6 +116,7 @@ bool parse_tune(const char *spec, Tune *out) {
         else if (k == "mfma_wm") v.mfma_wm = val;
         else if (k == "mfma_shared_kw") v.mfma_shared_kw = val;
         else if (k == "mfma_tile_m") v.mfma_tile_m = val;
+        else if (k == "mfma_tall_m") v.mfma_tall_m = val;
 
         else if (k == "mfma_target_waves") v.mfma_target_waves = val;
         else if (k == "mfma_splits") v.mfma_splits = val;
@@ -322,8 +330,31 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma, b
             p.split_len = cdiv(ngroups, splits) * spg;
             p.splits = (int)cdiv(K / 32, p.split_len);
         };
+        // The 128 x 128 kernel with 32-column wave strips: K-splits to about
+        // two workgroups per CU (it holds two: 235 registers per lane, 41 KB
+        // of LDS per workgroup), at least two 32-row steps per split.
+        const bool tall = allow_shared && t.mfma_tall_m > 0 && M >= t.mfma_tall_m && N % 32 == 0;
+        auto fill_tall = [&]() {
+            p.tall = true;
+            p.wm = 0;
+            p.mt = 8;
+            p.waves = 4;
+            p.kwaves = 1;
+            p.tiles_n = cdiv(N8, 16);
+            p.tiles_m = cdiv(M, 128);
+            const int64_t nsteps = K / 32;
+            const int64_t tiles = p.tiles_n * p.tiles_m;
+            int64_t splits = t.mfma_splits > 0 ? t.mfma_splits : std::max<int64_t>(1, 512 / tiles);
+            splits = std::min<int64_t>(splits, std::max<int64_t>(1, nsteps / 2));
+            splits = std::min<int64_t>(splits, std::max<int64_t>(1, cap / std::max<int64_t>(1, M * N * 4)));
+            splits = std::max<int64_t>(1, std::min<int64_t>(splits, kTallMaxSplits));
+            p.split_len = cdiv(nsteps, splits);
+            p.splits = (int)cdiv(nsteps, p.split_len);
+        };
         static const int kCfg[3][3] = {{1, 2, 4}, {2, 2, 4}, {2, 1, 8}};
-        if (wide) {
+        if (tall) {
+            fill_tall();
+        } else if (wide) {
             fill_tile();
         } else if (shared) {
             fill_shared(t.mfma_wm == 2 || t.mfma_wm == 4 ? (int)t.mfma_wm : (M > 64 ? 4 : 2));
@@ -376,9 +407,9 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma, b
         // tiles of activations through that XCD's L2.  Pick the g with the
         // fewest such bytes (the smallest g on ties).
         const int64_t krows = p.split_len * 32;
-        const int64_t cols = 16 * 8 * (int64_t)p.waves;
+        const int64_t cols = p.tall ? 128 : 16 * 8 * (int64_t)p.waves;
         const double wcol = (double)krows * (double)cols * 0.5 + (double)(krows / G) * (double)cols * 2.5;
-        const double arow = (double)(p.wide ? 128 : p.wm ? 32 * p.wm : 16 * p.mt) * (double)krows * 2.0;
+        const double arow = (double)(p.wide || p.tall ? 128 : p.wm ? 32 * p.wm : 16 * p.mt) * (double)krows * 2.0;
         const int64_t resident = std::max<int64_t>(1, std::min<int64_t>(32, cdiv(p.tiles_n * p.tiles_m * p.splits, 8)));
         int64_t gbest = 1;
         double cbest = -1;
@@ -391,7 +422,7 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma, b
             }
         }
         if (t.mfma_mgroup > 0) gbest = std::min<int64_t>(t.mfma_mgroup, p.tiles_m);
-        p.m_group = (int)gbest;
+        p.m_group = p.tall ? 1 : (int)gbest;  // the 128 x 128 kernel walks row tiles first
     }
     p.grid = p.tiles_n * p.tiles_m * p.splits;
     p.grid = cdiv(p.grid, 8) * 8;  // XCD-aware index mapping needs a multiple of 8

@@ -577,7 +577,7 @@ int mfma_max_splits(int mt, int waves, int kwaves) {
 
 hipError_t launch_mfma_rn(const GemmArgs &g, const GemmPlan &p, bool rn, const uint16_t *a, int64_t lda,
                           hipStream_t stream) {
-    if (p.wm != 0 || p.wide) return hipErrorInvalidValue;  // a plan of an LDS-sharing kernel
+    if (p.wm != 0 || p.wide || p.tall) return hipErrorInvalidValue;  // a plan of an LDS-sharing kernel
     // (MT, NWN, NWK) combinations the planner emits.
     if (p.mt == 1 && p.waves == 2 && p.kwaves == 4) return launch_cfg<1, 2, 4>(g, p, rn, a, lda, stream);
     if (p.mt == 2 && p.waves == 2 && p.kwaves == 4) return launch_cfg<2, 2, 4>(g, p, rn, a, lda, stream);
@@ -586,6 +586,7 @@ hipError_t launch_mfma_rn(const GemmArgs &g, const GemmPlan &p, bool rn, const u
 }
 
 hipError_t launch_mfma(const GemmArgs &g, const GemmPlan &p, hipStream_t stream) {
+    if (p.tall) return launch_mfma_tall(g, p, stream);
     if (p.wide) return launch_mfma_tile(g, p, stream);
     if (p.wm != 0) return launch_mfma_shared(g, p, stream);
     return launch_mfma_rn(g, p, false, g.a, g.K, stream);

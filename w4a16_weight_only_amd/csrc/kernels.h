@@ -29,6 +29,8 @@ struct GemmPlan {
     int kwaves = 1;           // MFMA: waves dividing a workgroup's K range (LDS-reduced)
     bool wide = false;        // MFMA: the 128 x 256 kernel sharing activations and weights
                               // through LDS (gemm_tile.hip)
+    bool tall = false;        // MFMA: the 128 x 128 kernel whose waves each own a 32-column strip
+                              // of all 128 rows, activations staged in LDS (gemm_tall.hip)
     int wm = 0;               // MFMA: row waves sharing each step's dequantised weights through
                               // LDS (2 or 4; mt = 2, waves = 1, kwaves = 8 / wm); 0: the
                               // register-direct kernel
@@ -99,6 +101,12 @@ hipError_t launch_mfma_shared(const GemmArgs &args, const GemmPlan &plan, hipStr
 // kTileGroupSlots groups per split and kSharedMaxSplits K-splits.
 constexpr int kTileGroupSlots = 64;
 hipError_t launch_mfma_tile(const GemmArgs &args, const GemmPlan &plan, hipStream_t stream);
+// MFMA GEMM on 128 x 128 workgroup tiles, each wave dequantising one
+// 32-column strip for all 128 rows, the activations staged in LDS per
+// workgroup (gemm_tall.hip; plan.tall).  N and G multiples of 32, at most
+// kTallMaxSplits K-splits.
+constexpr int kTallMaxSplits = 8;
+hipError_t launch_mfma_tall(const GemmArgs &args, const GemmPlan &plan, hipStream_t stream);
 // MFMA GEMM on A = `a` with row stride lda (>= K); with rn, the decode step's
 // row-norm folded in: out = (a . W) * inv_row, inv_row = 1/sqrt(mean(a_row^2)
 // + 1e-6) over the row's K values, applied to the products (the partials
