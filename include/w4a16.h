@@ -118,8 +118,8 @@ int w4a16_repack_scales(const uint16_t *src_ng, uint16_t *dst_gn, int64_t Gn, in
  * MFMA chain); the tuning key gemv_mma=0 selects the same GEMV with
  * v_dot2_f32_f16 on the vector ALUs.  M >= 9 runs an MFMA GEMM on exact
  * (q - z) fp16 operands that applies each group's scale to the fp32 sums of
- * that group: below M = 192 each wave dequantises its own operands in
- * registers for 32 rows; from M = 192 (tuning key mfma_tall_m) a workgroup
+ * that group: below M = 161 each wave dequantises its own operands in
+ * registers for 32 rows; from M = 161 (tuning key mfma_tall_m) a workgroup
  * owns 128 rows x 128 columns, each wave converts the weights of one
  * 32-column strip once for all 128 rows, and the activations are staged in
  * LDS once per workgroup.  (A third form, tuning key mfma_shared_m, shares
@@ -304,8 +304,9 @@ int w4a16_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t G, int32_t *path,
  * decode_rn_mfma (1: the MFMA GEMMs of M >= 9 fold the row-norm, applying the
  * row scale to the products, instead of reading the row-norm kernel's fp16
  * output), mfma_tall_m (the M from which the 128 x 128 MFMA GEMM whose waves
- * each convert a 32-column strip runs, default 192; 0: never; at most 8
- * K-splits), mfma_shared_m (the M from which the MFMA GEMM sharing
+ * each convert a 32-column strip runs, default 161; 0: never; at most 8
+ * K-splits), mfma_tall_kg (its K-groups of four waves per workgroup, 1 or 2;
+ * default 0: two where the grid still fits one round of the chip), mfma_shared_m (the M from which the MFMA GEMM sharing
  * dequantised weights between row waves through LDS runs, default 0:
  * never), mfma_wm (its row waves per workgroup, 2 or 4; 0:
  * 4 above 64 rows), mfma_shared_kw (1: one K-wave per workgroup, one wave

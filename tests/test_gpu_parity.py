@@ -200,7 +200,8 @@ def test_gemm_shared_kernel_matches_oracle(M, K, N, G, asym):
 TALL_CASES = [(129, 4096, 1024, 64, False), (256, 4096, 1056, 128, True), (256, 12800, 512, 128, True),
               (200, 3072, 544, 256, True), (130, 1024, 320, 32, False), (384, 1056, 288, 96, True),
               (96, 12800, 256, 32, True), (17, 544, 64, 32, False)]
-TALL_FORMS = ["", "mfma_splits=1", "mfma_splits=2", "mfma_splits=3", "mfma_splits=8"]
+TALL_FORMS = ["", "mfma_splits=1", "mfma_splits=2", "mfma_splits=3", "mfma_splits=8", "mfma_tall_kg=2",
+              "mfma_tall_kg=2,mfma_splits=1", "mfma_tall_kg=2,mfma_splits=3", "mfma_tall_kg=2,mfma_splits=8"]
 
 
 @pytest.mark.parametrize("M,K,N,G,asym", TALL_CASES)
@@ -209,7 +210,9 @@ def test_gemm_tall_kernel_matches_oracle(M, K, N, G, asym):
     all 128 rows of the workgroup tile (activations staged in LDS): ragged row
     tiles (rows past M), ragged column tiles (words past N), group sizes from
     32 to 256 and one (96) that does not divide the two-step LDS stages, odd
-    step counts per split, and K-split counts from one to eight."""
+    step counts per split, and K-split counts from one to eight; with one and
+    with two K-groups of waves per workgroup (the second group's share of a
+    split shorter than the first's, or empty)."""
     p = synth.problem(M, K, N, G, asym, seed=700 + M + K + N)
     want = oracle_gemm_columns(p["a"], p["b_packed"], p["scales"], p["qzeros"], G, 8)
     for spec in TALL_FORMS:
@@ -223,6 +226,7 @@ def test_gemm_tall_kernel_matches_oracle(M, K, N, G, asym):
 
 @pytest.mark.parametrize("spec", ["mfma_shared_m=0,mfma_splits=2", "mfma_shared_m=1,mfma_splits=2",
                                   "mfma_tall_m=1,mfma_splits=2", "mfma_tall_m=1,mfma_splits=8",
+                                  "mfma_tall_m=1,mfma_tall_kg=2,mfma_splits=4",
                                   "mfma_shared_m=1,mfma_wm=2,mfma_splits=4", "mfma_tile_m=1,mfma_splits=2",
                                   "mfma_tile_m=1,mfma_splits=8"])
 def test_gemm_split_partials_repeated(spec):

@@ -78,13 +78,16 @@ struct Tune {
     int64_t mfma_shared_kw = 0;        // its K-waves: 1 (one wave per SIMD, deeper load ring), else 8 / wm
     int64_t mfma_tile_m = 0;           // from this M on, the 128 x 256 kernel sharing activations and
                                        // weights through LDS (0: never)
-    int64_t mfma_tall_m = 192;         // from this M on, the 128 x 128 kernel whose waves each convert
+    int64_t mfma_tall_m = 161;         // from this M on, the 128 x 128 kernel whose waves each convert
                                        // a 32-column strip for all 128 rows (0: never); measured on
-                                       // MI355X (K = 12800 N = 4096 / K = 4096 N = 12800, best other
-                                       // kernel in brackets): M = 160 57.5 (47.1) / 59.6 (40.0) us,
-                                       // M = 192 57.0 (58.6) / 58.5 (59.0), M = 256 60.0 (62.2) /
-                                       // 61.2 (62.8), M = 512 90.4 (108.5) / 89.7 (118.0), M = 1024
-                                       // 150.5 (175.9) / 172.8 (226.4)
+                                       // MI355X (K = 12800 N = 4096 / K = 4096 N = 12800, the
+                                       // register-direct kernel in brackets): M = 160 52.3 (46.5) /
+                                       // 55.3 (38.1) us, M = 176 50.8 (55.8) / 52.8 (57.0), M = 256
+                                       // 54.1 (59.0) / 53.3 (69.9), M = 512 89.3 (107.7) / 97.3
+                                       // (133.5), M = 1024 154.7 (204.8) / 179.0 (239.6); the
+                                       // register-direct kernel's next row tile starts at M = 161
+    int64_t mfma_tall_kg = 0;          // its K-groups of four waves per workgroup (1 or 2; 0: by the
+                                       // grid, see plan_gemm)
 };
 
 // Returns false on an unknown key or a malformed entry (nothing applied).
@@ -117,6 +120,7 @@ bool parse_tune(const char *spec, Tune *out) {
         else if (k == "mfma_shared_kw") v.mfma_shared_kw = val;
         else if (k == "mfma_tile_m") v.mfma_tile_m = val;
         else if (k == "mfma_tall_m") v.mfma_tall_m = val;
+        else if (k == "mfma_tall_kg") v.mfma_tall_kg = val;
 
         else if (k == "mfma_target_waves") v.mfma_target_waves = val;
         else if (k == "mfma_splits") v.mfma_splits = val;
@@ -334,22 +338,46 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma, b
         // two workgroups per CU (it holds two: 235 registers per lane, 41 KB
         // of LDS per workgroup), at least two 32-row steps per split.
         const bool tall = allow_shared && t.mfma_tall_m > 0 && M >= t.mfma_tall_m && N % 32 == 0;
-        auto fill_tall = [&]() {
+        auto fill_tall_kg = [&](int kg) {
             p.tall = true;
             p.wm = 0;
             p.mt = 8;
             p.waves = 4;
-            p.kwaves = 1;
+            p.kwaves = kg;  // K-groups of four waves
             p.tiles_n = cdiv(N8, 16);
             p.tiles_m = cdiv(M, 128);
             const int64_t nsteps = K / 32;
             const int64_t tiles = p.tiles_n * p.tiles_m;
-            int64_t splits = t.mfma_splits > 0 ? t.mfma_splits : std::max<int64_t>(1, 512 / tiles);
-            splits = std::min<int64_t>(splits, std::max<int64_t>(1, nsteps / 2));
+            const int64_t round = kg == 2 ? 256 : 512;  // workgroups one round of the chip holds
+            int64_t splits = t.mfma_splits > 0 ? t.mfma_splits : std::max<int64_t>(1, round / tiles);
+            splits = std::min<int64_t>(splits, std::max<int64_t>(1, nsteps / (2 * kg)));
             splits = std::min<int64_t>(splits, std::max<int64_t>(1, cap / std::max<int64_t>(1, M * N * 4)));
             splits = std::max<int64_t>(1, std::min<int64_t>(splits, kTallMaxSplits));
             p.split_len = cdiv(nsteps, splits);
             p.splits = (int)cdiv(nsteps, p.split_len);
+        };
+        // Two K-groups (one 8-wave workgroup per CU) halve the split partials
+        // of one-group workgroups (two per CU).  Measured on MI355X they win
+        // where their grid fits one round of the chip and keeps about as many
+        // CUs busy: M = 256 K = 12800 N = 4096 54.1 against 60.9 us, M = 256
+        // K = 4096 N = 12800 53.3 against 61.2, M = 1024 K = 12800 N = 4096
+        // 154.7 against 170.4; and lose past one round (M = 512 K = 4096
+        // N = 12800 103.8 against 97.3) or with fewer CUs busy (M = 384
+        // K = 12800 N = 4096, 192 against 480 of 512 slots: 83.8 against 77.8).
+        auto fill_tall = [&]() {
+            if (t.mfma_tall_kg == 1 || t.mfma_tall_kg == 2) {
+                fill_tall_kg((int)t.mfma_tall_kg);
+                return;
+            }
+            auto eff = [&](int64_t slots) {
+                const int64_t grid = p.tiles_n * p.tiles_m * p.splits;
+                return (double)grid / (double)(cdiv(grid, slots) * slots);
+            };
+            fill_tall_kg(1);
+            const double e1 = eff(512);
+            fill_tall_kg(2);
+            const bool one_round = p.tiles_n * p.tiles_m * p.splits <= 256;
+            if (!one_round || eff(256) < e1 - 0.05) fill_tall_kg(1);
         };
         static const int kCfg[3][3] = {{1, 2, 4}, {2, 2, 4}, {2, 1, 8}};
         if (tall) {

@@ -63,20 +63,24 @@ constexpr int kAChunks = kRows * kKS * 4 / kThreads;  // 16-byte A pieces per th
 constexpr int kBRowWords = kWords + 1;                // padded LDS row of packed words
 constexpr int kBStageWords = 32 * kKS * kBRowWords;
 constexpr int kMaxSplits = 8;
-constexpr int kUnits = kRows * (kWords * 8 / 4) / kThreads;  // f32x4 units per thread, last arrival
+constexpr int kTileUnits = kRows * (kWords * 8 / 4);  // f32x4 units of a tile (last arrival)
 constexpr int kChunk = 4;
 static_assert(kAChunks * kThreads == kRows * kKS * 4, "whole A pieces per thread");
 static_assert(32 * kKS * kWords / 4 == kThreads, "one 16-byte B piece per thread per stage");
-static_assert(kUnits % kChunk == 0, "whole chunks");
+static_assert(kTileUnits % (2 * kThreads * kChunk) == 0, "whole chunks");
 
-template <bool ASYM>
-__global__ __launch_bounds__(kThreads, 2) void tall_kernel(
+// KG K-groups of four waves per workgroup: each group takes its own part of
+// the workgroup's K range with its own LDS stage buffers, and the groups'
+// totals meet in LDS (group 0 + group 1) before the split hand-off, so two
+// groups halve the fp32 partials of a given number of workgroups per CU.
+template <bool ASYM, int KG>
+__global__ __launch_bounds__(kThreads * KG, 2) void tall_kernel(
     const uint16_t *__restrict__ a, const uint32_t *__restrict__ b, const uint16_t *__restrict__ scales,
     const uint32_t *__restrict__ qzeros, int M, int K, int N, int G, uint32_t zp, int tiles_n, int tiles_m,
     int split_len, int splits, uint16_t *__restrict__ out, float *__restrict__ partials,
     uint32_t *__restrict__ counters) {
-    __shared__ __attribute__((aligned(16))) uint8_t s_a[2][kAStage];
-    __shared__ uint32_t s_b[2][kBStageWords];
+    __shared__ __attribute__((aligned(16))) uint8_t s_a[KG][2][kAStage];
+    __shared__ uint32_t s_b[KG][2][kBStageWords];
 
     // Logical workgroup: XCD-contiguous runs (grid a multiple of 8); within a
     // split, the row tiles of one column tile are consecutive (same weights).
@@ -87,7 +91,9 @@ __global__ __launch_bounds__(kThreads, 2) void tall_kernel(
     const int tile_n = rem / tiles_m;
     const int tile_m = rem - tile_n * tiles_m;
 
-    const int tid = threadIdx.x;
+    const int tid_all = threadIdx.x;
+    const int kg = __builtin_amdgcn_readfirstlane(tid_all >> 8);  // K-group
+    const int tid = tid_all & (kThreads - 1);                    // thread within the group
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j16 = lane & 15;
@@ -100,9 +106,14 @@ __global__ __launch_bounds__(kThreads, 2) void tall_kernel(
     const int wordc = col_ok ? word : N8 - 1;
     const int m0 = tile_m * kRows;
     const int nsteps = K / 32;
-    const int s_begin = split * split_len;
-    const int s_end = min(s_begin + split_len, nsteps);
-    const int nstages = (s_end - s_begin + kKS - 1) / kKS;
+    // The split's steps, then this K-group's share of them (whole stages; every
+    // group runs the same number of stages, a group past the split's end none
+    // of their steps).
+    const int sp_begin = split * split_len;
+    const int sp_end = min(sp_begin + split_len, nsteps);
+    const int nstages = ((sp_end - sp_begin + kKS - 1) / kKS + KG - 1) / KG;
+    const int s_begin = min(sp_begin + kg * nstages * kKS, sp_end);
+    const int s_end = min(s_begin + nstages * kKS, sp_end);
     const NibbleConsts nk = nibble_consts();
     // v_perm selector: byte bsel of the first word into byte 0, of the second
     // into byte 2 (bytes 1 and 3 zero)
@@ -159,11 +170,11 @@ __global__ __launch_bounds__(kThreads, 2) void tall_kernel(
     };
     auto stage_store = [&](int buf, const u32x4 (&ast)[kAChunks], const u32x4 &bst) __attribute__((always_inline)) {
 #pragma unroll
-        for (int p = 0; p < kAChunks; ++p) *reinterpret_cast<u32x4 *>(&s_a[buf][a_lds[p]]) = ast[p];
-        s_b[buf][b_lds + 0] = bst.x;
-        s_b[buf][b_lds + 1] = bst.y;
-        s_b[buf][b_lds + 2] = bst.z;
-        s_b[buf][b_lds + 3] = bst.w;
+        for (int p = 0; p < kAChunks; ++p) *reinterpret_cast<u32x4 *>(&s_a[kg][buf][a_lds[p]]) = ast[p];
+        s_b[kg][buf][b_lds + 0] = bst.x;
+        s_b[kg][buf][b_lds + 1] = bst.y;
+        s_b[kg][buf][b_lds + 2] = bst.z;
+        s_b[kg][buf][b_lds + 3] = bst.w;
     };
     // Group scale pair (this lane's two columns) and zero word of group g.
     auto load_sz = [&](int g, uint32_t &sc, uint32_t &zw) __attribute__((always_inline)) {
@@ -237,7 +248,7 @@ __global__ __launch_bounds__(kThreads, 2) void tall_kernel(
             }
         }
         stage_load(i + 2, a_st[P], b_st[P]);
-        const uint8_t *abase = s_a[P];
+        const uint8_t *abase = s_a[kg][P];
 #pragma unroll
         for (int ks = 0; ks < kKS; ++ks) {
             const int st = st0 + ks;
@@ -245,7 +256,7 @@ __global__ __launch_bounds__(kThreads, 2) void tall_kernel(
             // this lane's 8 packed words: rows 8 kq .. 8 kq + 7 of the step
             uint32_t w[8];
 #pragma unroll
-            for (int r = 0; r < 8; ++r) w[r] = s_b[P][b_rd + (32 * ks + r) * kBRowWords];
+            for (int r = 0; r < 8; ++r) w[r] = s_b[kg][P][b_rd + (32 * ks + r) * kBRowWords];
             f16x2 zc0, zc1;
             if constexpr (ASYM) {
                 const uint32_t pz = __builtin_amdgcn_perm(zw[ks], zw[ks], sel);
@@ -315,7 +326,31 @@ __global__ __launch_bounds__(kThreads, 2) void tall_kernel(
         if (i < nstages) body(i, I0{});
     }
 
-    // Epilogue: lane (j16, kq) holds rows m0 + 16 r + 4 kq + v, columns
+    if constexpr (KG == 2) {
+        // Group 1's totals to LDS (the stage buffers are free: every stage ended
+        // with a barrier), added to group 0's in that order.
+        static_assert(sizeof(s_a) >= sizeof(float) * kRowTiles * 2 * 4 * kThreads, "totals fit the stage buffers");
+        float *red = reinterpret_cast<float *>(&s_a[0][0][0]);
+        if (kg == 1) {
+#pragma unroll
+            for (int r = 0; r < kRowTiles; ++r)
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) red[((r * 2 + c) * 4 + v) * kThreads + tid] = tot[r][c][v];
+        }
+        __syncthreads();
+        if (kg == 0) {
+#pragma unroll
+            for (int r = 0; r < kRowTiles; ++r)
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) tot[r][c][v] += red[((r * 2 + c) * 4 + v) * kThreads + tid];
+        }
+    }
+
+    // Epilogue (group 0): lane (j16, kq) holds rows m0 + 16 r + 4 kq + v, columns
     // 8 word + 2 bsel + {0, 1}.
     const int col = word * 8 + 2 * bsel;
     const uint32_t plane = (uint32_t)M * (uint32_t)N * 4u;
@@ -325,7 +360,7 @@ __global__ __launch_bounds__(kThreads, 2) void tall_kernel(
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int row = m0 + 16 * r + 4 * kq + v;
-            if (row >= M || !col_ok) continue;
+            if (kg != 0 || row >= M || !col_ok) continue;
             if (splits == 1) {
                 const uint32_t o = (uint32_t)f32_to_f16_bits(tot[r][0][v]) |
                                    ((uint32_t)f32_to_f16_bits(tot[r][1][v]) << 16);
@@ -342,7 +377,7 @@ __global__ __launch_bounds__(kThreads, 2) void tall_kernel(
     __syncthreads();
     __shared__ uint32_t last;
     const int tile = tile_m * tiles_n + tile_n;
-    if (tid == 0) last = (arrive_agent(&counters[tile]) == (uint32_t)(splits - 1)) ? 1u : 0u;
+    if (tid_all == 0) last = (arrive_agent(&counters[tile]) == (uint32_t)(splits - 1)) ? 1u : 0u;
     __syncthreads();
     if (!last) return;
 
@@ -352,12 +387,14 @@ __global__ __launch_bounds__(kThreads, 2) void tall_kernel(
     constexpr int kRowUnits = kWords * 8 / 4;
     const int col0 = tile_n * kWords * 8;
     typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+    constexpr int kT = kThreads * KG;
+    constexpr int kUnits = kTileUnits / kT;  // f32x4 units per thread
 #pragma unroll
     for (int u0 = 0; u0 < kUnits; u0 += kChunk) {
         f32x4 v[kChunk][kMaxSplits];
 #pragma unroll
         for (int u = 0; u < kChunk; ++u) {
-            const int idx = tid + (u0 + u) * kThreads;
+            const int idx = tid_all + (u0 + u) * kT;
             const int row = m0 + idx / kRowUnits;
             const int c4 = col0 + 4 * (idx % kRowUnits);
             const bool ok = row < M && c4 < N;
@@ -369,7 +406,7 @@ __global__ __launch_bounds__(kThreads, 2) void tall_kernel(
         }
 #pragma unroll
         for (int u = 0; u < kChunk; ++u) {
-            const int idx = tid + (u0 + u) * kThreads;
+            const int idx = tid_all + (u0 + u) * kT;
             const int row = m0 + idx / kRowUnits;
             const int c4 = col0 + 4 * (idx % kRowUnits);
             if (row >= M || c4 >= N) continue;
@@ -382,7 +419,7 @@ __global__ __launch_bounds__(kThreads, 2) void tall_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
     }
-    if (tid == 0) reset_counter_agent(&counters[tile]);
+    if (tid_all == 0) reset_counter_agent(&counters[tile]);
 }
 
 }  // namespace
@@ -391,17 +428,21 @@ hipError_t launch_mfma_tall(const GemmArgs &g, const GemmPlan &p, hipStream_t st
     if (p.splits > kMaxSplits || p.splits < 1) return hipErrorInvalidValue;
     if (p.splits > 1 && (!g.partials || !g.counters)) return hipErrorInvalidValue;
     if (g.N % 32 != 0 || g.G % 32 != 0) return hipErrorInvalidValue;
-    if (g.qzeros)
-        hipLaunchKernelGGL(tall_kernel<true>, dim3((unsigned)p.grid), dim3(kThreads), 0, stream, g.a,
+    if (p.kwaves != 1 && p.kwaves != 2) return hipErrorInvalidValue;
+    auto go = [&](auto kern, int kgroups) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)p.grid), dim3(kThreads * kgroups), 0, stream, g.a,
                            reinterpret_cast<const uint32_t *>(g.b), g.scales,
                            reinterpret_cast<const uint32_t *>(g.qzeros), (int)g.M, (int)g.K, (int)g.N, (int)g.G,
                            (uint32_t)g.zp, (int)p.tiles_n, (int)p.tiles_m, (int)p.split_len, p.splits, g.out,
                            g.partials, g.counters);
-    else
-        hipLaunchKernelGGL(tall_kernel<false>, dim3((unsigned)p.grid), dim3(kThreads), 0, stream, g.a,
-                           reinterpret_cast<const uint32_t *>(g.b), g.scales, nullptr, (int)g.M, (int)g.K,
-                           (int)g.N, (int)g.G, (uint32_t)g.zp, (int)p.tiles_n, (int)p.tiles_m, (int)p.split_len,
-                           p.splits, g.out, g.partials, g.counters);
+    };
+    if (p.kwaves == 2) {
+        if (g.qzeros) go(tall_kernel<true, 2>, 2);
+        else go(tall_kernel<false, 2>, 2);
+    } else {
+        if (g.qzeros) go(tall_kernel<true, 1>, 1);
+        else go(tall_kernel<false, 1>, 1);
+    }
     return hipGetLastError();
 }
 
