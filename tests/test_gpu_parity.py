@@ -199,7 +199,8 @@ def test_gemm_shared_kernel_matches_oracle(M, K, N, G, asym):
 
 TALL_CASES = [(129, 4096, 1024, 64, False), (256, 4096, 1056, 128, True), (256, 12800, 512, 128, True),
               (200, 3072, 544, 256, True), (130, 1024, 320, 32, False), (384, 1056, 288, 96, True),
-              (96, 12800, 256, 32, True), (17, 544, 64, 32, False)]
+              (96, 12800, 256, 32, True), (17, 544, 64, 32, False),
+              (160, 2048, 512, 2048, False)]  # G = K: one group per row
 TALL_FORMS = ["", "mfma_splits=1", "mfma_splits=2", "mfma_splits=3", "mfma_splits=8", "mfma_tall_kg=2",
               "mfma_tall_kg=2,mfma_splits=1", "mfma_tall_kg=2,mfma_splits=3", "mfma_tall_kg=2,mfma_splits=8"]
 
@@ -316,7 +317,8 @@ def same_fp16(got, want):
 
 
 NONFINITE_FORMS = ["", "gemv_mma_exact=0", "gemv_mma=0,gemv_fold=0", "gemv_max_m=0", "gemv_max_m=0,mfma_shared_m=1",
-                   "gemv_max_m=0,mfma_tile_m=1"]
+                   "gemv_max_m=0,mfma_tile_m=1", "gemv_max_m=0,mfma_tall_m=1",
+                   "gemv_max_m=0,mfma_tall_m=1,mfma_tall_kg=2"]
 
 
 @pytest.mark.parametrize("spec", NONFINITE_FORMS)
@@ -355,7 +357,9 @@ def test_gemm_nonfinite_and_overflow(M, K, N, spec):
     assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
 
 
-@pytest.mark.parametrize("spec", ["gemv_splits=2", "gemv_splits=2,gemv_mma=0,gemv_fold=0", "gemv_max_m=0"])
+@pytest.mark.parametrize("spec", ["gemv_splits=2", "gemv_splits=2,gemv_mma=0,gemv_fold=0", "gemv_max_m=0",
+                                  "gemv_max_m=0,mfma_tall_m=1,mfma_splits=2",
+                                  "gemv_max_m=0,mfma_tall_m=1,mfma_tall_kg=2,mfma_splits=2"])
 def test_gemm_split_cancellation(spec):
     """Two K-splits whose partials cancel, on the forms whose products are
     exact ((q - z) weights).  Within the fixed-point range of the GEMVs'
