@@ -150,6 +150,14 @@ def test_gemm_plan_paths(lib):
     assert w4.w4a16_gemm_plan(9, 4096, 12800, 128)[0] == 2
     assert w4.w4a16_gemm_plan(32, 4096, 12800, 128)[0] == 2
     assert w4.w4a16_gemm_plan(256, 12800, 4096, 128)[0] == 2
+    # prefill sizes take the 128 x 128 strip kernel: two K-groups where their grid fits one
+    # round of the chip (256 workgroups), else one group at two workgroups per CU (512)
+    assert w4.w4a16_gemm_plan(256, 12800, 4096, 128) == (2, 4, 256)
+    assert w4.w4a16_gemm_plan(256, 4096, 12800, 128) == (2, 1, 200)
+    assert w4.w4a16_gemm_plan(384, 12800, 4096, 128) == (2, 5, 480)
+    assert w4.w4a16_gemm_plan(512, 4096, 12800, 128) == (2, 1, 400)
+    # below M = 161 the register-direct kernel (32-row wave tiles, 8 K-waves)
+    assert w4.w4a16_gemm_plan(160, 12800, 4096, 128) == (2, 3, 240)
     # N % 32 != 0 at small M goes to the MFMA kernel (word-granular loads)
     assert w4.w4a16_gemm_plan(1, 256, 264, 64)[0] == 2
     for shape in [(1, 4096, 12800, 128), (32, 4096, 12800, 128), (256, 12800, 4096, 128),
