@@ -14,9 +14,10 @@
 // workgroup here owns 128 rows x 128 columns and a K range; each of its four
 // waves owns all 128 rows of a 32-column strip (8 row tiles x 2 column tiles
 // of 16x16).  So a weight is converted by one wave, once, and feeds 8 MFMAs
-// (about 1.25 vector instructions per MFMA), and the activations, which every
+// (20 conversion instructions per 16 MFMAs), and the activations, which every
 // wave needs, are staged in LDS once per workgroup and read as whole MFMA
-// fragments (one ds_read_b128 per row tile and K-step).
+// fragments (one ds_read_b128 per row tile and K-step).  Two K-groups of four
+// waves can share a workgroup (below), halving the split partials.
 //
 // B operand mapping.  A 16x16x32 MFMA takes, in lane (j, kq) = (lane % 16,
 // lane / 16), eight consecutive k of column j of B.  A packed word holds 8
@@ -33,11 +34,10 @@
 // into one of two LDS buffers: the global reads are whole 128-byte lines (two
 // rows per quarter wave), requested two stages ahead into one of two register
 // sets, and written to LDS at the end of the stage before their own, followed
-// by the stage's single barrier.  A fragments
-// sit in LDS in MFMA lane order with the slot index XOR-swizzled by the
-// fragment's k-octet and step (lane L of block (row tile, step) at slot
-// L ^ (2 (L / 16) + step)), so neither the fragment reads nor the line-wise
-// writes meet bank conflicts.  Weight rows are 17 words apart in LDS, so the
+// by the stage's single barrier.  A fragments sit in LDS in MFMA lane order
+// with the slot index XOR-swizzled by the fragment's k-octet and step (lane L
+// of block (row tile, step) at slot L ^ (2 (L / 16) + step)), so neither the
+// fragment reads nor the line-wise writes meet bank conflicts.  Weight rows are 17 words apart in LDS, so the
 // four k-octets of a wave's reads fall in different banks.
 //
 // Reduction.  With K split across workgroups each split writes its fp32 tile
@@ -62,7 +62,6 @@ constexpr int kAStage = kRowTiles * kKS * kABlock;
 constexpr int kAChunks = kRows * kKS * 4 / kThreads;  // 16-byte A pieces per thread per stage
 constexpr int kBRowWords = kWords + 1;                // padded LDS row of packed words
 constexpr int kBStageWords = 32 * kKS * kBRowWords;
-constexpr int kMaxSplits = 8;
 constexpr int kTileUnits = kRows * (kWords * 8 / 4);  // f32x4 units of a tile (last arrival)
 constexpr int kChunk = 4;
 static_assert(kAChunks * kThreads == kRows * kKS * 4, "whole A pieces per thread");
@@ -391,7 +390,7 @@ __global__ __launch_bounds__(kThreads * KG, 2) void tall_kernel(
     constexpr int kUnits = kTileUnits / kT;  // f32x4 units per thread
 #pragma unroll
     for (int u0 = 0; u0 < kUnits; u0 += kChunk) {
-        f32x4 v[kChunk][kMaxSplits];
+        f32x4 v[kChunk][kTallMaxSplits];
 #pragma unroll
         for (int u = 0; u < kChunk; ++u) {
             const int idx = tid_all + (u0 + u) * kT;
@@ -400,7 +399,7 @@ __global__ __launch_bounds__(kThreads * KG, 2) void tall_kernel(
             const bool ok = row < M && c4 < N;
             const uint32_t off = ok ? ((uint32_t)row * (uint32_t)N + (uint32_t)c4) * 4u : 0u;
 #pragma unroll
-            for (int sp = 0; sp < kMaxSplits; ++sp)
+            for (int sp = 0; sp < kTallMaxSplits; ++sp)
                 v[u][sp] = (ok && sp < splits) ? buffer_load_f32x4_sc1(prs, off, (uint32_t)sp * plane)
                                                : f32x4{0.f, 0.f, 0.f, 0.f};
         }
@@ -412,7 +411,7 @@ __global__ __launch_bounds__(kThreads * KG, 2) void tall_kernel(
             if (row >= M || c4 >= N) continue;
             f32x4 s = v[u][0];
 #pragma unroll
-            for (int sp = 1; sp < kMaxSplits; ++sp) s += v[u][sp];
+            for (int sp = 1; sp < kTallMaxSplits; ++sp) s += v[u][sp];
             const u16x4 o = {f32_to_f16_bits(s.x), f32_to_f16_bits(s.y), f32_to_f16_bits(s.z),
                              f32_to_f16_bits(s.w)};
             *reinterpret_cast<u16x4 *>(out + (size_t)row * N + c4) = o;
@@ -425,7 +424,7 @@ __global__ __launch_bounds__(kThreads * KG, 2) void tall_kernel(
 }  // namespace
 
 hipError_t launch_mfma_tall(const GemmArgs &g, const GemmPlan &p, hipStream_t stream) {
-    if (p.splits > kMaxSplits || p.splits < 1) return hipErrorInvalidValue;
+    if (p.splits > kTallMaxSplits || p.splits < 1) return hipErrorInvalidValue;
     if (p.splits > 1 && (!g.partials || !g.counters)) return hipErrorInvalidValue;
     if (g.N % 32 != 0 || g.G % 32 != 0) return hipErrorInvalidValue;
     if (p.kwaves != 1 && p.kwaves != 2) return hipErrorInvalidValue;
