@@ -37,8 +37,9 @@
 // by the stage's single barrier.  A fragments sit in LDS in MFMA lane order
 // with the slot index XOR-swizzled by the fragment's k-octet and step (lane L
 // of block (row tile, step) at slot L ^ (2 (L / 16) + step)), so neither the
-// fragment reads nor the line-wise writes meet bank conflicts.  Weight rows are 17 words apart in LDS, so the
-// four k-octets of a wave's reads fall in different banks.
+// fragment reads nor the line-wise writes meet bank conflicts.  Weight rows
+// are 17 words apart in LDS, so the four k-octets of a wave's reads fall in
+// different banks.
 //
 // Reduction.  With K split across workgroups each split writes its fp32 tile
 // with device-coherent stores and bumps the tile's arrival counter; the last
