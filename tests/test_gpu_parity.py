@@ -200,7 +200,8 @@ def test_gemm_shared_kernel_matches_oracle(M, K, N, G, asym):
 TALL_CASES = [(129, 4096, 1024, 64, False), (256, 4096, 1056, 128, True), (256, 12800, 512, 128, True),
               (200, 3072, 544, 256, True), (130, 1024, 320, 32, False), (384, 1056, 288, 96, True),
               (96, 12800, 256, 32, True), (17, 544, 64, 32, False),
-              (160, 2048, 512, 2048, False)]  # G = K: one group per row
+              (160, 2048, 512, 2048, False),  # G = K: one group per row
+              (513, 1024, 256, 64, False), (1024, 1024, 512, 128, True)]  # many row tiles, a last tile of one row
 TALL_FORMS = ["", "mfma_splits=1", "mfma_splits=2", "mfma_splits=3", "mfma_splits=8", "mfma_tall_kg=2",
               "mfma_tall_kg=2,mfma_splits=1", "mfma_tall_kg=2,mfma_splits=3", "mfma_tall_kg=2,mfma_splits=8"]
 
