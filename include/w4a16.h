@@ -306,7 +306,8 @@ int w4a16_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t G, int32_t *path,
  * output), mfma_tall_m (the M from which the 128 x 128 MFMA GEMM whose waves
  * each convert a 32-column strip runs, default 161; 0: never; at most 8
  * K-splits), mfma_tall_kg (its K-groups of four waves per workgroup, 1 or 2;
- * default 0: two where the grid still fits one round of the chip), mfma_shared_m (the M from which the MFMA GEMM sharing
+ * default 0: two where the grid still fits one round of the chip),
+ * mfma_tall_rt (its MFMA row tiles per workgroup tile, 2, 4 or 8; default 0: 8), mfma_shared_m (the M from which the MFMA GEMM sharing
  * dequantised weights between row waves through LDS runs, default 0:
  * never), mfma_wm (its row waves per workgroup, 2 or 4; 0:
  * 4 above 64 rows), mfma_shared_kw (1: one K-wave per workgroup, one wave

@@ -203,7 +203,9 @@ TALL_CASES = [(129, 4096, 1024, 64, False), (256, 4096, 1056, 128, True), (256, 
               (160, 2048, 512, 2048, False),  # G = K: one group per row
               (513, 1024, 256, 64, False), (1024, 1024, 512, 128, True)]  # many row tiles, a last tile of one row
 TALL_FORMS = ["", "mfma_splits=1", "mfma_splits=2", "mfma_splits=3", "mfma_splits=8", "mfma_tall_kg=2",
-              "mfma_tall_kg=2,mfma_splits=1", "mfma_tall_kg=2,mfma_splits=3", "mfma_tall_kg=2,mfma_splits=8"]
+              "mfma_tall_kg=2,mfma_splits=1", "mfma_tall_kg=2,mfma_splits=3", "mfma_tall_kg=2,mfma_splits=8",
+              "mfma_tall_rt=2", "mfma_tall_rt=2,mfma_tall_kg=2,mfma_splits=3", "mfma_tall_rt=4,mfma_splits=5",
+              "mfma_tall_rt=4,mfma_tall_kg=2"]
 
 
 @pytest.mark.parametrize("M,K,N,G,asym", TALL_CASES)

@@ -86,6 +86,7 @@ struct Tune {
                                        // 54.1 (59.0) / 53.3 (69.9), M = 512 89.3 (107.7) / 97.3
                                        // (133.5), M = 1024 154.7 (204.8) / 179.0 (239.6); the
                                        // register-direct kernel's next row tile starts at M = 161
+    int64_t mfma_tall_rt = 0;          // its MFMA row tiles per workgroup tile (2, 4 or 8; 0: 8)
     int64_t mfma_tall_kg = 0;          // its K-groups of four waves per workgroup (1 or 2; 0: by the
                                        // grid, see plan_gemm)
 };
@@ -121,6 +122,7 @@ bool parse_tune(const char *spec, Tune *out) {
         else if (k == "mfma_tile_m") v.mfma_tile_m = val;
         else if (k == "mfma_tall_m") v.mfma_tall_m = val;
         else if (k == "mfma_tall_kg") v.mfma_tall_kg = val;
+        else if (k == "mfma_tall_rt") v.mfma_tall_rt = val;
 
         else if (k == "mfma_target_waves") v.mfma_target_waves = val;
         else if (k == "mfma_splits") v.mfma_splits = val;
@@ -341,11 +343,11 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma, b
         auto fill_tall_kg = [&](int kg) {
             p.tall = true;
             p.wm = 0;
-            p.mt = 8;
+            p.mt = t.mfma_tall_rt == 2 || t.mfma_tall_rt == 4 ? (int)t.mfma_tall_rt : 8;  // row tiles
             p.waves = 4;
             p.kwaves = kg;  // K-groups of four waves
             p.tiles_n = cdiv(N8, 16);
-            p.tiles_m = cdiv(M, 128);
+            p.tiles_m = cdiv(M, 16 * p.mt);
             const int64_t nsteps = K / 32;
             const int64_t tiles = p.tiles_n * p.tiles_m;
             const int64_t round = kg == 2 ? 256 : 512;  // workgroups one round of the chip holds
@@ -437,7 +439,7 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G, bool allow_mma, b
         const int64_t krows = p.split_len * 32;
         const int64_t cols = p.tall ? 128 : 16 * 8 * (int64_t)p.waves;
         const double wcol = (double)krows * (double)cols * 0.5 + (double)(krows / G) * (double)cols * 2.5;
-        const double arow = (double)(p.wide || p.tall ? 128 : p.wm ? 32 * p.wm : 16 * p.mt) * (double)krows * 2.0;
+        const double arow = (double)(p.wide ? 128 : p.wm ? 32 * p.wm : 16 * p.mt) * (double)krows * 2.0;
         const int64_t resident = std::max<int64_t>(1, std::min<int64_t>(32, cdiv(p.tiles_n * p.tiles_m * p.splits, 8)));
         int64_t gbest = 1;
         double cbest = -1;

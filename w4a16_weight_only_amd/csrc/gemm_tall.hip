@@ -54,31 +54,37 @@ namespace w4a16 {
 namespace {
 
 constexpr int kThreads = 256;          // four waves
-constexpr int kRows = 128;             // workgroup tile rows: 8 MFMA row tiles per wave
-constexpr int kRowTiles = kRows / 16;
 constexpr int kWords = 16;             // workgroup tile: 16 packed words = 128 columns
 constexpr int kKS = 2;                 // 32-row K-steps per LDS stage
 constexpr int kABlock = 1024;          // one A fragment block: 16 rows x 32 k of fp16
-constexpr int kAStage = kRowTiles * kKS * kABlock;
-constexpr int kAChunks = kRows * kKS * 4 / kThreads;  // 16-byte A pieces per thread per stage
 constexpr int kBRowWords = kWords + 1;                // padded LDS row of packed words
 constexpr int kBStageWords = 32 * kKS * kBRowWords;
-constexpr int kTileUnits = kRows * (kWords * 8 / 4);  // f32x4 units of a tile (last arrival)
-constexpr int kChunk = 4;
-static_assert(kAChunks * kThreads == kRows * kKS * 4, "whole A pieces per thread");
 static_assert(32 * kKS * kWords / 4 == kThreads, "one 16-byte B piece per thread per stage");
-static_assert(kTileUnits % (2 * kThreads * kChunk) == 0, "whole chunks");
+
+// Sizes of a workgroup tile of RT MFMA row tiles (16 RT rows; RT = 8 for the
+// prefill sizes, fewer for small M).
+template <int RT>
+struct TallRows {
+    static constexpr int kRowTiles = RT;
+    static constexpr int kRows = 16 * RT;
+    static constexpr int kAStage = RT * kKS * kABlock;
+    static constexpr int kAChunks = kRows * kKS * 4 / kThreads;  // 16-byte A pieces per thread per stage
+    static constexpr int kTileUnits = kRows * (kWords * 8 / 4);  // f32x4 units of a tile (last arrival)
+    static_assert(kAChunks >= 1 && kAChunks * kThreads == kRows * kKS * 4, "whole A pieces per thread");
+};
 
 // KG K-groups of four waves per workgroup: each group takes its own part of
 // the workgroup's K range with its own LDS stage buffers, and the groups'
 // totals meet in LDS (group 0 + group 1) before the split hand-off, so two
 // groups halve the fp32 partials of a given number of workgroups per CU.
-template <bool ASYM, int KG>
+template <bool ASYM, int KG, int RT>
 __global__ __launch_bounds__(kThreads * KG, 2) void tall_kernel(
     const uint16_t *__restrict__ a, const uint32_t *__restrict__ b, const uint16_t *__restrict__ scales,
     const uint32_t *__restrict__ qzeros, int M, int K, int N, int G, uint32_t zp, int tiles_n, int tiles_m,
     int split_len, int splits, uint16_t *__restrict__ out, float *__restrict__ partials,
     uint32_t *__restrict__ counters) {
+    using R = TallRows<RT>;
+    constexpr int kRows = R::kRows, kRowTiles = R::kRowTiles, kAStage = R::kAStage, kAChunks = R::kAChunks;
     __shared__ __attribute__((aligned(16))) uint8_t s_a[KG][2][kAStage];
     __shared__ uint32_t s_b[KG][2][kBStageWords];
 
@@ -388,7 +394,9 @@ __global__ __launch_bounds__(kThreads * KG, 2) void tall_kernel(
     const int col0 = tile_n * kWords * 8;
     typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
     constexpr int kT = kThreads * KG;
-    constexpr int kUnits = kTileUnits / kT;  // f32x4 units per thread
+    constexpr int kUnits = R::kTileUnits / kT;  // f32x4 units per thread
+    constexpr int kChunk = kUnits < 4 ? kUnits : 4;
+    static_assert(kUnits * kT == R::kTileUnits && kUnits % kChunk == 0, "whole chunks");
 #pragma unroll
     for (int u0 = 0; u0 < kUnits; u0 += kChunk) {
         f32x4 v[kChunk][kTallMaxSplits];
@@ -436,13 +444,20 @@ hipError_t launch_mfma_tall(const GemmArgs &g, const GemmPlan &p, hipStream_t st
                            (uint32_t)g.zp, (int)p.tiles_n, (int)p.tiles_m, (int)p.split_len, p.splits, g.out,
                            g.partials, g.counters);
     };
-    if (p.kwaves == 2) {
-        if (g.qzeros) go(tall_kernel<true, 2>, 2);
-        else go(tall_kernel<false, 2>, 2);
-    } else {
-        if (g.qzeros) go(tall_kernel<true, 1>, 1);
-        else go(tall_kernel<false, 1>, 1);
-    }
+    auto by_rt = [&](auto rt) {
+        constexpr int RT = decltype(rt)::value;
+        if (p.kwaves == 2) {
+            if (g.qzeros) go(tall_kernel<true, 2, RT>, 2);
+            else go(tall_kernel<false, 2, RT>, 2);
+        } else {
+            if (g.qzeros) go(tall_kernel<true, 1, RT>, 1);
+            else go(tall_kernel<false, 1, RT>, 1);
+        }
+    };
+    if (p.mt == 8) by_rt(std::integral_constant<int, 8>{});
+    else if (p.mt == 4) by_rt(std::integral_constant<int, 4>{});
+    else if (p.mt == 2) by_rt(std::integral_constant<int, 2>{});
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
